@@ -1,0 +1,383 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the
+oracle itself (closed forms, invariants, textbook routines, exact arithmetic
+on tiny inputs).  Each pin is a function taking an ``oracle.Oracle`` and
+raising AssertionError on failure, so the same pins run against the real
+oracle (test_oracle_pins.py) and against copies with planted mistakes
+(test_oracle_mutants.py), which every pin set must reject.
+
+What is being pinned: RMSNorm over the innermost dimension with an optional
+weight and eps default 1e-6 (Hugging Face cuda-kernels skill page, section
+"Kernel-Specific Guidelines", RMSNorm), read as
+y = x / sqrt(mean(x^2) + eps) * w; and rms_norm_rope (LTX-2 ltx-kernels
+README, introduction) read as that RMSNorm followed by rotate-half RoPE per
+head over the 1D [batch, seq, heads, head_dim] layout (skill page, RoPE).
+"""
+from __future__ import annotations
+
+import cmath
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import datagen
+
+EPS32 = float(np.float32(1e-6))  # the binary32 epsilon both sides actually use
+
+
+def _bf16(vals) -> np.ndarray:
+    """Exact bf16 bit patterns for values that are exactly representable."""
+    f = np.asarray(vals, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _val(bits) -> np.ndarray:
+    return datagen.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _rand_bf16(rng, shape, scale=1.0):
+    return datagen.to_bf16_bits(rng.standard_normal(shape) * scale)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm pins
+# --------------------------------------------------------------------------
+
+def pin_eps_inside_root(o):
+    """Constant row c = 2^-10, no weight, eps = 1e-6 (binary32).  mean(x^2) is
+    c^2 = 2^-20, so y = c / sqrt(2^-20 + eps32) = 0.698672999...  (eps added
+    outside the root would give 0.998977, a sum instead of a mean 0.123988)."""
+    x = _bf16(np.full((2, 64), 2.0 ** -10))
+    y = o.rmsnorm(x, None, 1e-6)
+    # 2^-10 / sqrt(2^-20 + 9.999999974752427e-07), evaluated at 40 digits
+    # with Python's decimal module
+    expected = 0.69867299943694822
+    assert np.allclose(y, expected, rtol=1e-13, atol=0), (y[0, 0], expected)
+
+
+def pin_constant_row_gives_weight(o):
+    """Constant row c with |c| >= 0.1: eps shifts rstd by < 5e-5 relative,
+    below half a bf16 ulp, so the bf16 output is exactly sign(c) * w."""
+    rng = np.random.default_rng(11)
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 96))
+    for c in (0.125, -0.5, 3.0, -96.0, 0.1015625):
+        x = _bf16(np.full((3, 96), c, dtype=np.float32))
+        _, ref16 = o.round(o.rmsnorm(x, w, 1e-6))
+        want = w if c > 0 else (w ^ np.uint16(0x8000))
+        assert np.array_equal(ref16, np.broadcast_to(want, ref16.shape)), c
+
+
+def pin_constant_row_small_value(o):
+    """Constant row c = 0.01 (bf16 0.010009765625), unit weight: y =
+    c / sqrt(c^2 + eps32), a closed form that depends on eps at 0.5 %."""
+    c = float(np.float32(datagen.bf16_bits_to_f32(datagen.to_bf16_bits(np.array([0.01])))[0]))
+    assert c == 0.010009765625
+    x = _bf16(np.full((1, 32), c))
+    y = o.rmsnorm(x, None, 1e-6)
+    # c^2 = 1.00195407867431640625e-04 (exact), + eps32 = 1.0119540786490688e-04,
+    # sqrt = 1.0059592827987964e-02, so y = 0.99504679723722674 (40 digits)
+    assert np.allclose(y, 0.99504679723722674, rtol=1e-14, atol=0)
+
+
+def pin_zero_row(o):
+    """A zero row normalises to exact zeros (rstd = 1/sqrt(eps) is finite),
+    and zero elements in a nonzero row give zero outputs."""
+    rng = np.random.default_rng(3)
+    x = _rand_bf16(rng, (4, 40))
+    x[1] = 0
+    x[2, ::3] = 0
+    y = o.rmsnorm(x, datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 40)), 1e-6)
+    assert np.all(y[1] == 0.0)
+    assert np.all(y[2, ::3] == 0.0)
+    assert np.all(np.isfinite(y))
+
+
+def pin_scale_invariance(o):
+    """With eps = 0, x -> 2^k x leaves the output bit-identical (powers of two
+    scale exactly; the norm divides them out)."""
+    rng = np.random.default_rng(5)
+    x = _rand_bf16(rng, (5, 72))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 72))
+    base = o.rmsnorm(x, w, 0.0)
+    for k in (-8, -3, 1, 4, 8):
+        xs = datagen.to_bf16_bits(_val(x) * 2.0 ** k)
+        assert np.array_equal(o.rmsnorm(xs, w, 0.0), base), k
+
+
+def pin_sign_symmetry(o):
+    """y(-x) = -y(x) exactly."""
+    rng = np.random.default_rng(7)
+    x = _rand_bf16(rng, (3, 50))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 50))
+    assert np.array_equal(o.rmsnorm(x ^ np.uint16(0x8000), w, 1e-6), -o.rmsnorm(x, w, 1e-6))
+
+
+def pin_textbook_norm(o):
+    """Unit weight, eps = 0: y = sqrt(H) * x / ||x||_2 with the Euclidean
+    norm from numpy.linalg.norm."""
+    rng = np.random.default_rng(9)
+    for hidden in (1, 7, 64, 3072):
+        x = _rand_bf16(rng, (3, hidden))
+        xv = _val(x)
+        want = math.sqrt(hidden) * xv / np.linalg.norm(xv, axis=1, keepdims=True)
+        assert np.allclose(o.rmsnorm(x, None, 0.0), want, rtol=1e-13, atol=0), hidden
+
+
+def pin_none_weight_is_ones(o):
+    """An absent weight behaves exactly as a weight of ones (skill page,
+    section "Diffusers Critical Pitfalls", item 1)."""
+    rng = np.random.default_rng(13)
+    x = _rand_bf16(rng, (4, 24))
+    ones = _bf16(np.ones(24))
+    assert np.array_equal(o.rmsnorm(x, None, 1e-6), o.rmsnorm(x, ones, 1e-6))
+
+
+def pin_rows_independent(o):
+    """Each row depends only on itself: any subset of rows gives the same
+    values as the full call."""
+    rng = np.random.default_rng(17)
+    x = _rand_bf16(rng, (9, 32))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 32))
+    full = o.rmsnorm(x, w, 1e-6)
+    for sel in ([4], [0, 8], [2, 3, 5]):
+        assert np.array_equal(o.rmsnorm(x[sel], w, 1e-6), full[sel])
+
+
+def pin_permutation(o):
+    """Permuting the elements of x and w together permutes y (up to the
+    rounding of the sum in a different order)."""
+    rng = np.random.default_rng(19)
+    x = _rand_bf16(rng, (3, 48))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 48))
+    perm = rng.permutation(48)
+    a = o.rmsnorm(x, w, 1e-6)[:, perm]
+    b = o.rmsnorm(x[:, perm], w[perm], 1e-6)
+    assert np.allclose(a, b, rtol=1e-14, atol=0)
+
+
+def _exact_rms_row(xv, wv, eps):
+    """Exact sum of squares with fractions, root and products at 60 digits."""
+    getcontext().prec = 60
+    ss = sum(Fraction(v) * Fraction(v) for v in xv)
+    ms = ss / len(xv) + Fraction(eps)
+    ms_dec = Decimal(ms.numerator) / Decimal(ms.denominator)
+    rstd = 1 / ms_dec.sqrt()
+    return [Decimal(v) * rstd * Decimal(wj) for v, wj in zip(xv, wv)]
+
+
+def pin_brute_force_exact(o):
+    """Tiny rows, random and adversarial (mixed magnitudes, magnitudes so
+    small that eps dominates, a single nonzero) against exact rational /
+    60-digit arithmetic: the double result within (H + 8) * 2^-53 relative
+    (H rounded additions plus a few rounded operations), and the binary32
+    reference within one binary32 ulp of the exact value."""
+    rng = np.random.default_rng(23)
+    rows = []
+    for hidden in (1, 2, 8, 16, 64):
+        rows.append(_rand_bf16(rng, (hidden,)))
+        rows.append(_rand_bf16(rng, (hidden,), scale=1e-5))
+        mixed = rng.standard_normal(hidden) * np.where(rng.random(hidden) < 0.2, 300.0, 1e-3)
+        rows.append(datagen.to_bf16_bits(mixed))
+        single = np.zeros(hidden)
+        single[hidden // 2] = -2.5
+        rows.append(datagen.to_bf16_bits(single))
+    for x in rows:
+        hidden = x.size
+        w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, hidden))
+        xv, wv = _val(x), _val(w)
+        exact = _exact_rms_row(xv, wv, EPS32)
+        y = o.rmsnorm(x[None, :], w, 1e-6)[0]
+        ref32, _ = o.round(y)
+        for j in range(hidden):
+            e = exact[j]
+            if e == 0:
+                assert y[j] == 0.0
+                continue
+            tol = Decimal((hidden + 8) * 2.0 ** -53)
+            assert abs(Decimal(y[j]) - e) <= abs(e) * tol, (hidden, j, y[j], e)
+            f = np.float32(float(e))
+            ulp = np.spacing(np.float32(abs(f)))
+            assert abs(float(ref32[j]) - float(e)) <= float(ulp), (hidden, j)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm + RoPE pins
+# --------------------------------------------------------------------------
+
+def _tables(positions, head_dim, theta=10000.0):
+    return datagen.rope_tables(0, head_dim, theta, positions=np.asarray(positions))
+
+
+def pin_rope_position_zero_is_rmsnorm(o):
+    """cos = 1, sin = 0 rotates by nothing: RMSNorm+RoPE at position 0 is the
+    plain RMSNorm, exactly."""
+    rng = np.random.default_rng(29)
+    heads, d = 4, 16
+    x = _rand_bf16(rng, (3, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables([0], d)
+    assert np.all(c == 1.0) and np.all(s == 0.0)
+    y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6)
+    assert np.array_equal(y, o.rmsnorm(x, w, 1e-6))
+
+
+def pin_rope_complex_rotation(o):
+    """Each rotate-half pair (i, i + d/2) is the complex number a + ib turned
+    by the unit phasor c + is (Python complex multiplication); checked against
+    RMSNorm from the same oracle for the un-rotated values."""
+    rng = np.random.default_rng(31)
+    heads, d, seq = 3, 8, 5
+    x = _rand_bf16(rng, (seq, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables(np.arange(seq), d)
+    y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6)
+    z = o.rmsnorm(x, w, 1e-6)
+    for r in range(seq):
+        for h in range(heads):
+            for i in range(d // 2):
+                a, b = z[r, h * d + i], z[r, h * d + i + d // 2]
+                rot = complex(a, b) * complex(float(c[r, i]), float(s[r, i]))
+                assert cmath.isclose(complex(y[r, h * d + i], y[r, h * d + i + d // 2]), rot,
+                                     rel_tol=1e-14, abs_tol=1e-300), (r, h, i)
+
+
+def pin_rope_pair_norm(o):
+    """The rotation preserves each pair's norm: o1^2 + o2^2 = (a^2 + b^2)(c^2 + s^2)."""
+    rng = np.random.default_rng(37)
+    heads, d = 2, 32
+    x = _rand_bf16(rng, (6, heads * d))
+    c, s = _tables(np.arange(6) * 37, d)
+    y = o.rmsnorm_rope(x, None, c, s, heads, d, 1e-6)
+    z = o.rmsnorm(x, None, 1e-6)
+    hd = d // 2
+    for h in range(heads):
+        a, b = z[:, h * d:h * d + hd], z[:, h * d + hd:(h + 1) * d]
+        o1, o2 = y[:, h * d:h * d + hd], y[:, h * d + hd:(h + 1) * d]
+        cc, ss = c.astype(np.float64), s.astype(np.float64)
+        assert np.allclose(o1 ** 2 + o2 ** 2, (a ** 2 + b ** 2) * (cc ** 2 + ss ** 2), rtol=1e-13, atol=1e-300)
+
+
+def pin_rope_constant_row(o):
+    """Constant positive x and unit weight normalise to exactly 1 (in double,
+    up to eps); the output is then cos - sin in the first half of each head and
+    cos + sin in the second half."""
+    heads, d = 2, 16
+    x = _bf16(np.full((3, heads * d), 0.75))
+    c, s = _tables([1, 2, 9], d)
+    y = o.rmsnorm_rope(x, None, c, s, heads, d, 0.0)
+    cc, ss = c.astype(np.float64), s.astype(np.float64)
+    for h in range(heads):
+        assert np.allclose(y[:, h * d:h * d + d // 2], cc - ss, rtol=1e-15, atol=1e-15)
+        assert np.allclose(y[:, h * d + d // 2:(h + 1) * d], cc + ss, rtol=1e-15, atol=1e-15)
+
+
+def pin_rope_row_position(o):
+    """Row r uses table row r mod seq_len: each row alone, given a one-row
+    table holding just that position, gives the same result."""
+    rng = np.random.default_rng(41)
+    heads, d, seq = 2, 8, 3
+    x = _rand_bf16(rng, (8, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables([5, 11, 17], d)
+    y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6)
+    for r in range(8):
+        p = [0, 1, 2][r % seq]
+        yr = o.rmsnorm_rope(x[r:r + 1], w, c[p:p + 1], s[p:p + 1], heads, d, 1e-6)
+        assert np.array_equal(yr[0], y[r]), r
+
+
+def pin_rope_mag(o):
+    """The magnitude sum returned with the rotation is |a c| + |b s| (first
+    half) and |b c| + |a s| (second half): it bounds the rotated value and
+    equals its magnitude when the two products do not cancel."""
+    rng = np.random.default_rng(43)
+    heads, d = 2, 8
+    x = _rand_bf16(rng, (4, heads * d))
+    c, s = _tables([1, 2, 3, 4], d)
+    y, mag = o.rmsnorm_rope(x, None, c, s, heads, d, 1e-6, with_mag=True)
+    z = o.rmsnorm(x, None, 1e-6)
+    assert np.all(np.abs(y) <= mag * (1 + 1e-15))
+    hd = d // 2
+    for h in range(heads):
+        a, b = z[:, h * d:h * d + hd], z[:, h * d + hd:(h + 1) * d]
+        cc, ss = c.astype(np.float64), s.astype(np.float64)
+        assert np.allclose(mag[:, h * d:h * d + hd], np.abs(a * cc) + np.abs(b * ss), rtol=1e-15)
+        assert np.allclose(mag[:, h * d + hd:(h + 1) * d], np.abs(b * cc) + np.abs(a * ss), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Rounding pins
+# --------------------------------------------------------------------------
+
+def _bf16_nearest_reference(f32: np.ndarray) -> np.ndarray:
+    """Independent RNE: take the two bf16 neighbours bracketing the value
+    (truncation and the next one away from zero), compare distances in
+    double, break ties toward the even mantissa."""
+    u = f32.view(np.uint32)
+    lo = (u >> 16).astype(np.uint32)
+    hi = lo + 1
+    v = f32.astype(np.float64)
+    vlo = ((lo << 16).astype(np.uint32)).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        vhi = ((hi << 16).astype(np.uint32)).view(np.float32).astype(np.float64)
+        dlo, dhi = np.abs(v - vlo), np.abs(vhi - v)
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1))
+    # the neighbour past the largest finite bf16 is infinity: the value
+    # rounds there only if it is at or beyond the midpoint 0x7f7f8000
+    top = (u & 0x7FFFFFFF) >= 0x7F7F8000
+    edge = ((lo & 0x7FFF) == 0x7F7F)
+    pick_hi = np.where(edge, top, pick_hi)
+    return np.where(pick_hi, hi, lo).astype(np.uint16)
+
+
+def pin_bf16_rounding(o):
+    """All 2^16 upper halves (every sign, exponent and kept mantissa) times
+    the dropped-bit patterns that decide rounding (0, 1, just below half,
+    half, just above half, all ones, and random ones), for finite values,
+    against the neighbour-distance formulation; NaN stays NaN and quiet;
+    +-Inf stays +-Inf."""
+    rng = np.random.default_rng(47)
+    uppers = np.arange(1 << 16, dtype=np.uint32)
+    lows = np.concatenate([np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32),
+                           rng.integers(0, 1 << 16, 6, dtype=np.uint32)])
+    bits = ((uppers[:, None] << 16) | lows[None, :]).reshape(-1).astype(np.uint32)
+    f = bits.view(np.float32)
+    got = o.bf16_from_f32(f)
+    finite = np.isfinite(f)
+    want = _bf16_nearest_reference(f[finite])
+    assert np.array_equal(got[finite], want)
+    nan = np.isnan(f)
+    g = got[nan]
+    assert np.all((g & 0x7F80) == 0x7F80) and np.all((g & 0x0040) != 0)
+    assert np.array_equal(np.signbit(f[nan]), (g & 0x8000) != 0)
+    inf = np.isinf(f)
+    assert np.array_equal(got[inf], (bits[inf] >> 16).astype(np.uint16))
+
+
+def pin_round_twice(o):
+    """oracle_round: binary32 of the double, then its bf16 (hand-worked cases
+    across a tie, a carry into the exponent, and a negative value)."""
+    y = np.array([1.0 + 2 ** -8,              # tie -> even 1.0
+                  1.0 + 3 * 2 ** -8,          # tie -> even 1 + 2^-6
+                  1.0 + 2 ** -8 + 2 ** -20,   # just above the tie -> up
+                  1.0 + 2 ** -8 + 2 ** -30,   # binary32 drops 2^-30: a tie again
+                  2.0 - 2 ** -9,              # 0.75 ulp dropped: carry to 2.0
+                  -1.5 - 2 ** -8 - 2 ** -20,  # above half, negative: -(1.5 + 2^-7)
+                  -1.5 - 2 ** -9 - 2 ** -20,  # below half: -1.5
+                  0.0])
+    ref32, ref16 = o.round(y)
+    assert np.array_equal(ref32, y.astype(np.float32))
+    assert list(ref16) == [0x3F80, 0x3F82, 0x3F81, 0x3F80, 0x4000, 0xBFC1, 0xBFC0, 0x0000]
+
+
+PINS = [
+    pin_eps_inside_root, pin_constant_row_gives_weight, pin_constant_row_small_value,
+    pin_zero_row, pin_scale_invariance, pin_sign_symmetry, pin_textbook_norm,
+    pin_none_weight_is_ones, pin_rows_independent, pin_permutation, pin_brute_force_exact,
+    pin_rope_position_zero_is_rmsnorm, pin_rope_complex_rotation, pin_rope_pair_norm,
+    pin_rope_constant_row, pin_rope_row_position, pin_rope_mag,
+    pin_bf16_rounding, pin_round_twice,
+]

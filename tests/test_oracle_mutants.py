@@ -1,0 +1,72 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies ``oracle/oracle.c``, plants one mistake by replacing a piece
+of its text (a dropped term, a wrong sign or index, a transposed operand, a
+wrong rounding rule), builds the copy with gcc into a temporary directory, and
+asserts that at least one pin rejects it.  The real oracle is never modified.
+Mutants are chosen so that none reads or writes outside its buffers.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "eps_outside_root": ("sqrt(mean_sq + (double)eps)", "(sqrt(mean_sq) + (double)eps)"),
+    "no_root": ("1.0 / sqrt(mean_sq + (double)eps)", "1.0 / (mean_sq + (double)eps)"),
+    "sum_not_mean": ("sum_sq / (double)hidden", "sum_sq"),
+    "mean_over_hidden_minus_one": ("sum_sq / (double)hidden", "sum_sq / (double)(hidden > 1 ? hidden - 1 : 1)"),
+    "eps_dropped": ("mean_sq + (double)eps", "mean_sq"),
+    "square_dropped": ("sum_sq += v * v;", "sum_sq += fabs(v);"),
+    "weight_dropped": ("z[j] = bf16_value(x[j]) * rstd * wj;", "z[j] = bf16_value(x[j]) * rstd;"),
+    "weight_reversed": ("bf16_value(w[j])", "bf16_value(w[hidden - 1 - j])"),
+    "weight_none_zero": ("w ? bf16_value(w[j]) : 1.0", "w ? bf16_value(w[j]) : 0.5"),
+    "rope_sign_first": ("head[i] = a * c - b * s;", "head[i] = a * c + b * s;"),
+    "rope_sign_second": ("head[i + half] = b * c + a * s;", "head[i + half] = b * c - a * s;"),
+    "rope_cos_sin_swapped": ("double c = (double)cp[i];", "double c = (double)sp[i];"),
+    "rope_halves_swapped": ("double a = head[i];        /* first half  */\n                double b = head[i + half]; /* second half */",
+                            "double b = head[i];        /* first half  */\n                double a = head[i + half]; /* second half */"),
+    "rope_pair_mirrored": ("double b = head[i + half]; /* second half */",
+                           "double b = head[head_dim - 1 - i]; /* second half */"),
+    "rope_position_div": ("const int64_t p = r % seq_len;", "const int64_t p = (r / seq_len) % seq_len;"),
+    "rope_position_zero": ("const int64_t p = r % seq_len;", "const int64_t p = 0;"),
+    "rope_rounded_input": ("double a = head[i];        /* first half  */",
+                           "double a = (double)(float)head[i]; /* first half  */"),
+    "mag_signed": ("m[i] = fabs(a * c) + fabs(b * s);", "m[i] = fabs(a * c - b * s);"),
+    "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
+    "bf16_truncate": ("kept += 1u;", "kept += 0u;"),
+    "bf16_ties_odd": ("(kept & 1u))", "!(kept & 1u))"),
+    "bf16_nan_not_quiet": ("return (uint16_t)((u >> 16) | 0x0040u);", "return (uint16_t)(u >> 16);"),
+    "round_skips_f32": ("float f = (float)y[i];", "float f = (float)(y[i] * (1.0 + 0x1p-20));"),
+}
+
+
+def _first_failing_pin(o):
+    for pin in PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            return pin.__name__
+        except (ValueError, FloatingPointError, OverflowError, ZeroDivisionError, ArithmeticError):
+            return pin.__name__
+    return None
+
+
+def test_real_oracle_passes_every_pin():
+    assert _first_failing_pin(oracle.Oracle()) is None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation site for {name} not found in oracle.c"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+    caught = _first_failing_pin(oracle.Oracle(lib))
+    assert caught is not None, f"no pin rejects the planted mistake {name}"
