@@ -1,0 +1,288 @@
+"""Benchmark: effective HBM bandwidth of RMSNorm bf16 at [4 x 4096 x 3072] on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one launch of the RMSNorm path (load, square-accumulate, reduce,
+scale, round, store) over the whole [4 x 4096 x 3072] bf16 batch.  Inputs are
+seeded synthetic tensors (x ~ N(0,1), weight ~ U(0.5,1.5)), resident in HBM
+before timing starts.  Consecutive steps cycle through enough copies of the
+input and output buffers (>= 1 GiB in total) that the 256 MB memory-side
+Infinity Cache cannot serve a step from the previous one.  Timing uses HIP
+events recorded on the stream the kernels are launched on.
+
+value = algorithmic bytes per step (read x + write y + read weight once,
+201,332,736 B) / seconds per step, in GB/s (10^9 B/s); it is compared with
+MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
+the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
+cos/sin tables) under "rope", and the CPU oracle timed on this host under
+"cpu_baseline".  Prints one JSON line.
+
+--probe rms|rope|copy runs a few launches only, for rocprofv3 counter passes.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, RMSNorm bf16"
+# H100 figure for the same shape and byte convention: 201,332,736 B in 0.157 ms
+# (Hugging Face cuda-kernels skill page, "RMSNorm Micro-benchmarks"); context only.
+H100_GBPS_4x4096x3072 = 201_332_736 / 0.157e-3 / 1e9
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "ltxnorm.hip"),
+                  os.path.join(ROOT, "include", "ltxnorm.h")]
+
+
+def gbps(nbytes: float, seconds: float) -> float:
+    return nbytes / seconds / 1e9
+
+
+def pct_of_peak(gb_s: float, peak_gbps: float) -> float:
+    return 100.0 * gb_s / peak_gbps
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cur = source_hash()
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("#") or not line.strip():
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload:
+            if kv.get("src_sha") != cur:
+                return None
+            return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
+def to_device(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+class Workload:
+    """Rotating device buffers for one config, and the launch of one step."""
+
+    def __init__(self, cfg: datagen.Config, dev, stream, max_sets=None):
+        import torch
+        import rmsnorm_video_dit_amd as ltx
+        self.cfg, self.ltx, self.stream = cfg, ltx, stream
+        inp = datagen.make_inputs(cfg)
+        self.host = inp
+        per_set = 2 * cfg.rows * cfg.hidden * 2
+        n = max(2, -(-ROTATE_BYTES // per_set))
+        if max_sets:
+            n = min(n, max_sets)
+        self.nsets = n
+        x0 = to_device(inp["x"], dev)
+        self.x = [x0] + [x0.clone() for _ in range(n - 1)]
+        self.y = [torch.empty_like(x0) for _ in range(n)]
+        self.w = to_device(inp["w"], dev)
+        if cfg.rope:
+            self.cos = torch.from_numpy(inp["cos"]).to(dev)
+            self.sin = torch.from_numpy(inp["sin"]).to(dev)
+        torch.cuda.synchronize()
+
+    def step(self, i: int):
+        c = self.cfg
+        k = i % self.nsets
+        if c.rope:
+            self.ltx.ltxnorm_rmsnorm_rope_fwd(self.y[k], self.x[k], self.w, self.cos, self.sin,
+                                              c.rows, c.hidden, c.heads, c.head_dim, c.seq,
+                                              c.eps, self.stream)
+        else:
+            self.ltx.ltxnorm_rmsnorm_fwd(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
+                                         self.stream)
+
+    def time_steps(self, steps: int, warmup: int):
+        """Warm up, then time exactly `steps` launches with HIP events on
+        the launch stream; returns seconds per step."""
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for i in range(steps):
+            self.step(i)
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e-3 / steps
+
+
+def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict:
+    """The CPU oracle (double arithmetic, one rounding) on this host's cores,
+    rows split into contiguous blocks across a thread pool; repeated over the
+    full batch until `budget_s` has passed."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    o = oracle.Oracle()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    x, w = inp["x"], inp["w"]
+    blocks = np.array_split(np.arange(cfg.rows), threads)
+
+    def work(b):
+        if len(b) == 0:
+            return 0
+        y = o.rmsnorm(x[b[0]:b[-1] + 1], w, cfg.eps)
+        o.round(y)
+        return len(b)
+
+    passes = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            list(ex.map(work, blocks))
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    per_pass = el / passes
+    return {"value": round(gbps(cfg.algorithmic_bytes(), per_pass), 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"full {cfg.name} batch ({cfg.rows} rows x {cfg.hidden}), {passes} passes "
+                      f"in {el:.1f} s; double arithmetic + rounding to bf16; "
+                      f"{per_pass * 1e3:.1f} ms per pass"}
+
+
+def probe(kind: str, launches: int):
+    """A handful of launches for counter collection (rocprofv3 --pmc)."""
+    import torch
+    dev = torch.device("cuda:0")
+    s = torch.cuda.Stream()
+    if kind == "copy":
+        n = datagen.CONFIGS[datagen.HEADLINE].rows * datagen.CONFIGS[datagen.HEADLINE].hidden
+        a = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+        b = torch.empty_like(a)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(launches):
+                b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                          "launches": launches}), flush=True)
+        return
+    cfg = datagen.CONFIGS[datagen.HEADLINE if kind == "rms" else datagen.ROPE]
+    wl = Workload(cfg, dev, s, max_sets=2)
+    for i in range(launches):
+        wl.step(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": kind, "workload": cfg.name, "launches": launches,
+                      "algorithmic_bytes": cfg.algorithmic_bytes()}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-rope", action="store_true", help="skip the RMSNorm+RoPE line item")
+    ap.add_argument("--probe", choices=["rms", "rope", "copy"])
+    ap.add_argument("--launches", type=int, default=10)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; rows are independent, so a multi-GPU "
+              "deployment shards rows across GPUs with no communication, and the one-GPU "
+              "figure is the per-GPU throughput. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.probe:
+        probe(args.probe, args.launches)
+        return
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible; the HIP kernels are the only path", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    name = torch.cuda.get_device_name(0)
+
+    cfg = datagen.CONFIGS[datagen.HEADLINE]
+    wl = Workload(cfg, dev, stream)
+    sec = wl.time_steps(args.steps, args.warmup)
+    value = gbps(cfg.algorithmic_bytes(), sec)
+    traffic = read_traffic("rmsnorm", cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / H100_GBPS_4x4096x3072, 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq": cfg.seq,
+                   "hidden": cfg.hidden, "io_dtype": "bf16", "eps": cfg.eps,
+                   "bytes_per_step": cfg.algorithmic_bytes(), "rotating_sets": wl.nsets,
+                   "seed": datagen.BASE_SEED, "x_fnv": datagen.fnv1a64(wl.host["x"]),
+                   "device": name},
+        "pct_of_peak": round(pct_of_peak(value, HBM_PEAK_GBPS), 2),
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / sec / 1e9, 2),
+                     "kernel": "rmsnorm_kernel<VPL=6, WPR=1, FULL>",
+                     "kernel_us": round(sec * 1e6, 3)},
+        "baseline_note": "vs_baseline divides by the H100 figure for this shape on the "
+                         "pages (0.157 ms = 1282.4 GB/s); another GPU, context only",
+    }
+    if traffic is not None:
+        line["roofline"]["traffic_bytes_per_launch"] = int(traffic)
+    host = wl.host
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_rope:
+        rc = datagen.CONFIGS[datagen.ROPE]
+        rw = Workload(rc, dev, stream)
+        rsec = rw.time_steps(args.steps, args.warmup)
+        rv = gbps(rc.algorithmic_bytes(), rsec)
+        rtraffic = read_traffic("rmsnorm_rope", rc.name)
+        line["rope"] = {"workload": rc.name, "value": round(rv, 2), "unit": "GB/s",
+                        "ms_per_step": round(rsec * 1e3, 6),
+                        "bytes_per_step": rc.algorithmic_bytes(), "rotating_sets": rw.nsets,
+                        "frac": round(rv / HBM_PEAK_GBPS, 4),
+                        "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+        del rw
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, host)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

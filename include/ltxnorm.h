@@ -1,0 +1,122 @@
+/*
+ * ltxnorm.h -- C ABI of libltxnorm.so: row-wise RMSNorm and fused RMSNorm +
+ * rotate-half RoPE over bf16 activations, as HIP kernels for gfx950 (MI355X).
+ *
+ * Operations
+ *   RMSNorm over the innermost dimension of [..., hidden] activations, with
+ *   epsilon (default 1e-6) and a weight that may be absent: Hugging Face
+ *   "cuda-kernels" skill page ("CUDA Kernels for Diffusers & Transformers"),
+ *   section "Kernel-Specific Guidelines", RMSNorm; an absent weight acts as a
+ *   weight of ones (same page, "Diffusers Critical Pitfalls", item 1).  The
+ *   page prints no formula; the library computes the standard definition
+ *       y[r, j] = x[r, j] * rsqrt( (1/H) * sum_k x[r, k]^2 + eps ) * w[j]
+ *   with the sum of squares accumulated in binary32 and one rounding to bf16
+ *   (round-to-nearest-even) at the output.
+ *
+ *   Fused RMSNorm followed by rotary position embedding: the rms_norm_rope op
+ *   listed among the fused element ops of the LTX-2 ltx-kernels README
+ *   (introduction).  The row is normalised over the full hidden size, then
+ *   each head of head_dim elements (1D layout [batch, seq, heads, head_dim],
+ *   skill page, section "Kernel-Specific Guidelines", RoPE) is rotated
+ *   rotate-half style: element i pairs with element i + head_dim/2 and
+ *       out[i]          = y[i] * c - y[i + d/2] * s
+ *       out[i + d/2]    = y[i + d/2] * c + y[i] * s
+ *   with c = cos_tab[p, i], s = sin_tab[p, i], p = row mod seq_len, applied
+ *   to the un-rounded binary32 y, then rounded once to bf16.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (HIP device memory, or memory the device
+ *     can access) unless stated otherwise.  bf16 tensors are arrays of 16-bit
+ *     IEEE bfloat16 values, row-major, contiguous, hidden innermost.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates nothing and never synchronises; work is enqueued on `stream`
+ *     (0 = the null stream) and runs asynchronously.  Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - The destination comes first, as in an out-variant op.
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call enqueues nothing.  No C++ exception crosses this boundary.
+ *   - Calls are thread-safe and reentrant.  The only state kept is a cached
+ *     per-device compute-unit count used to size launches.
+ */
+#ifndef LTXNORM_H
+#define LTXNORM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LTXNORM_ABI_VERSION 1
+
+/* Largest supported hidden size: 16 wavefronts x 64 lanes x 8 vectors of 8
+ * bf16 values per row, all held in registers. */
+#define LTXNORM_MAX_HIDDEN 65536
+
+typedef enum ltxnorm_status {
+    LTXNORM_OK = 0,
+    LTXNORM_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    LTXNORM_ERR_SHAPE = 2,       /* rows < 0, hidden <= 0, size overflow, or a RoPE
+                                    shape that does not fit (see below)             */
+    LTXNORM_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                 */
+    LTXNORM_ERR_UNSUPPORTED = 4, /* hidden % 8 != 0 or hidden > LTXNORM_MAX_HIDDEN   */
+    LTXNORM_ERR_ALIAS = 5,       /* out partially overlaps x, or overlaps an input
+                                    that is only read (weight, tables)              */
+    LTXNORM_ERR_VALUE = 6,       /* eps negative, infinite or NaN                    */
+    LTXNORM_ERR_HIP = 7          /* the HIP runtime refused the launch               */
+} ltxnorm_status;
+
+/*
+ * Row-wise RMSNorm, bf16 in / bf16 out, binary32 arithmetic.
+ *
+ *   out     bf16 [rows, hidden], written.  May equal x exactly (in place);
+ *           any other overlap with x, or overlap with weight, is ERR_ALIAS.
+ *   x       bf16 [rows, hidden], read.
+ *   weight  bf16 [hidden], read; NULL means a weight of ones (bit-identical
+ *           to passing ones).
+ *   rows    number of rows (B*S); 0 returns LTXNORM_OK and enqueues nothing
+ *           (pointers may then be NULL).
+ *   hidden  row length H; a multiple of 8, 8 <= H <= LTXNORM_MAX_HIDDEN.
+ *   eps     added to the mean of squares inside the root; finite, >= 0.
+ *           With eps = 0 an all-zero row gives NaN (0 * inf), as IEEE does.
+ *   stream  HIP stream to enqueue on.
+ * out, x and weight must be 16-byte aligned.
+ */
+ltxnorm_status ltxnorm_rmsnorm_fwd(void *out, const void *x, const void *weight,
+                                   int64_t rows, int64_t hidden, float eps,
+                                   hipStream_t stream);
+
+/*
+ * Fused RMSNorm over the full row, then rotate-half RoPE per head.
+ *
+ *   out, x, weight, rows, eps, stream   as for ltxnorm_rmsnorm_fwd.
+ *   cos_tab, sin_tab  binary32 [seq_len, head_dim/2], row-major, read; shared
+ *           by all heads; row r of x uses table row (r mod seq_len).  A caller
+ *           with other positions (a sequence shard, flattened t*h*w video
+ *           positions) passes tables holding one row per position it needs.
+ *           Both must be 16-byte aligned and must not overlap out.
+ *   hidden  must equal heads * head_dim.
+ *   heads   number of heads, >= 1.
+ *   head_dim  a multiple of 16 (each lane rotates 8-wide halves in place).
+ *   seq_len number of table rows, >= 1.
+ * Shape errors (hidden != heads*head_dim, head_dim % 16 != 0, seq_len < 1)
+ * give LTXNORM_ERR_SHAPE.
+ */
+ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *weight,
+                                        const float *cos_tab, const float *sin_tab,
+                                        int64_t rows, int64_t hidden, int32_t heads,
+                                        int32_t head_dim, int64_t seq_len, float eps,
+                                        hipStream_t stream);
+
+/* Static, never-NULL description of a status code (unknown codes included). */
+const char *ltxnorm_status_str(ltxnorm_status s);
+
+/* LTXNORM_ABI_VERSION of the built library. */
+int ltxnorm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LTXNORM_H */

@@ -1,0 +1,167 @@
+"""Python binding of libltxnorm.so: gfx950 RMSNorm and fused RMSNorm + RoPE.
+
+Argument marshalling only.  Every step of both ops runs in the HIP kernels of
+``csrc/ltxnorm.hip`` behind the C ABI declared in ``include/ltxnorm.h``; this
+module converts tensors to device pointers and the current torch stream to a
+``hipStream_t``.  There is no fallback: if the library is not built, or a
+tensor is not on the GPU, calls raise.
+
+The low-level functions keep the C names and argument order:
+
+    ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, stream)
+    ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden,
+                             heads, head_dim, seq_len, eps, stream)
+    ltxnorm_status_str(status), ltxnorm_version()
+
+Pointer arguments accept a torch tensor, an integer address or None; ``stream``
+accepts a ``torch.cuda.Stream``, an integer handle, or None for torch's
+current stream.  A non-OK status raises ``LtxnormError``.
+
+``rmsnorm(x, weight=None, eps=1e-6, out=None)`` and ``rmsnorm_rope(...)`` are
+the tensor-level forms (functional, or out-variant when ``out`` is given).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libltxnorm.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_ALIAS, ERR_VALUE, ERR_HIP = range(8)
+MAX_HIDDEN = 65536
+
+_lib = None
+
+
+class LtxnormError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ltxnorm_status_str(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libltxnorm.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(or python -m rmsnorm_video_dit_amd._build); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.ltxnorm_rmsnorm_fwd.argtypes = [p, p, p, i64, i64, f32, p]
+        L.ltxnorm_rmsnorm_fwd.restype = ctypes.c_int
+        L.ltxnorm_rmsnorm_rope_fwd.argtypes = [p, p, p, p, p, i64, i64, i32, i32, i64, f32, p]
+        L.ltxnorm_rmsnorm_rope_fwd.restype = ctypes.c_int
+        L.ltxnorm_status_str.argtypes = [ctypes.c_int]
+        L.ltxnorm_status_str.restype = ctypes.c_char_p
+        L.ltxnorm_version.argtypes = []
+        L.ltxnorm_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _addr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def ltxnorm_status_str(status: int) -> str:
+    return lib().ltxnorm_status_str(int(status)).decode()
+
+
+def ltxnorm_version() -> int:
+    return lib().ltxnorm_version()
+
+
+def ltxnorm_rmsnorm_fwd_status(out, x, weight, rows, hidden, eps, stream) -> int:
+    """Same call, returning the raw status code instead of raising."""
+    return lib().ltxnorm_rmsnorm_fwd(_addr(out), _addr(x), _addr(weight), int(rows), int(hidden),
+                                     float(eps), _stream(stream))
+
+
+def ltxnorm_rmsnorm_rope_fwd_status(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                    head_dim, seq_len, eps, stream) -> int:
+    return lib().ltxnorm_rmsnorm_rope_fwd(_addr(out), _addr(x), _addr(weight), _addr(cos_tab),
+                                          _addr(sin_tab), int(rows), int(hidden), int(heads),
+                                          int(head_dim), int(seq_len), float(eps), _stream(stream))
+
+
+def ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, stream=None) -> None:
+    st = ltxnorm_rmsnorm_fwd_status(out, x, weight, rows, hidden, eps, stream)
+    if st != OK:
+        raise LtxnormError(st, "ltxnorm_rmsnorm_fwd")
+
+
+def ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim,
+                             seq_len, eps, stream=None) -> None:
+    st = ltxnorm_rmsnorm_rope_fwd_status(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                         head_dim, seq_len, eps, stream)
+    if st != OK:
+        raise LtxnormError(st, "ltxnorm_rmsnorm_rope_fwd")
+
+
+def _check_act(x, name):
+    import torch
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no host path exists)")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rmsnorm(x, weight=None, eps: float = 1e-6, out=None):
+    """RMSNorm over the last dimension of bf16 ``x`` (weight bf16 [H] or None)."""
+    import torch
+    _check_act(x, "x")
+    if weight is not None:
+        _check_act(weight, "weight")
+    hidden = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_act(out, "out")
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    rows = x.numel() // hidden if hidden else 0
+    ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, None)
+    return out
+
+
+def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: float = 1e-6,
+                 out=None):
+    """RMSNorm over the full last dimension (heads*head_dim), then rotate-half
+    RoPE per head; row r uses table row r mod cos_tab.shape[0]."""
+    import torch
+    _check_act(x, "x")
+    if weight is not None:
+        _check_act(weight, "weight")
+    for t, n in ((cos_tab, "cos_tab"), (sin_tab, "sin_tab")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 GPU tensor")
+    if cos_tab.shape != sin_tab.shape or cos_tab.dim() != 2 or cos_tab.shape[1] != head_dim // 2:
+        raise ValueError("cos_tab and sin_tab must both be [seq_len, head_dim/2]")
+    hidden = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_act(out, "out")
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    rows = x.numel() // hidden if hidden else 0
+    ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim,
+                             cos_tab.shape[0], eps, None)
+    return out

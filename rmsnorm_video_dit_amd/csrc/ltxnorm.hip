@@ -1,0 +1,536 @@
+// ltxnorm.hip -- gfx950 (MI355X) kernels and C-ABI launcher for row-wise
+// RMSNorm and fused RMSNorm + rotate-half RoPE over bf16 activations.
+//
+// The operations (declared in include/ltxnorm.h):
+//  * RMSNorm over the innermost dimension of [..., hidden], eps default 1e-6,
+//    optional weight (Hugging Face cuda-kernels skill page, "Kernel-Specific
+//    Guidelines", RMSNorm; "Diffusers Critical Pitfalls", item 1 for the
+//    absent weight), computed as y = x * rsqrt(mean(x^2) + eps) * w.
+//  * rms_norm_rope (LTX-2 ltx-kernels README, introduction): that RMSNorm
+//    over the full row followed by rotate-half RoPE per head on the 1D
+//    [batch, seq, heads, head_dim] layout (skill page, RoPE).
+//
+// Design for gfx950
+//  * The op moves 2 bytes in and 2 bytes out per element and does ~4 flops:
+//    it is bound by HBM bandwidth, so there is no MFMA and the whole design
+//    is about moving each byte exactly once with full-width accesses.
+//  * A row is held entirely in VGPRs: HBM is read once and written once.
+//    Every access is a 16-byte bf16x8 vector; consecutive lanes touch
+//    consecutive vectors, so one load instruction covers 1 KiB contiguous.
+//  * One wavefront per row for hidden <= 4096 (up to 8 vectors per lane),
+//    otherwise 2..16 wavefronts per row whose partial sums meet in LDS.
+//  * Sum of squares: per-lane fp32 FMAs in a fixed order, then a fixed
+//    DPP butterfly inside each 16-lane row (quad_perm, row_half_mirror,
+//    row_mirror) and four readlanes; every lane ends with identical bits and
+//    the result is deterministic run to run.
+//  * rstd = 1 / sqrt(sum / H + eps) with correctly rounded binary32 divide
+//    and square root: it scales exactly under x -> 2^k x, and costs nothing
+//    next to the row's memory traffic.
+//  * The weight (and for RoPE each lane's table offsets) is loaded into
+//    registers once per wavefront; the grid is capped near the resident
+//    capacity so each wavefront walks several rows and reuses them.
+//  * RoPE pairs element i with i + head_dim/2.  With 8 elements per vector
+//    both halves of a pair are whole vectors, head_dim/16 vectors apart, so
+//    each lane loads a vector and its partner ("pair unit") and rotates in
+//    registers: no cross-lane exchange.  The two load instructions of a pair
+//    unit cover complementary halves of the same cache lines and are in
+//    flight together.  cos/sin rows (head_dim/2 floats per position) are read
+//    through L2; lanes that share a table slice issue the same address.
+//  * Output: binary32 -> bf16 round-to-nearest-even via v_cvt_pk_bf16_f32.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "ltxnorm.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kElemsPerVec = 8;       // bf16 values per 16-byte vector
+constexpr int kMaxVecPerLane = 8;     // register budget for one row slice
+constexpr int kMaxWavesPerRow = 16;   // 1024-thread workgroup
+constexpr int kBlocksPerCU = 8;       // grid cap: resident 256-thread blocks per CU
+constexpr uint32_t kOnesPair = 0x3F803F80u;  // two bf16 1.0
+
+static_assert(LTXNORM_MAX_HIDDEN == kMaxWavesPerRow * kWave * kMaxVecPerLane * kElemsPerVec,
+              "cap must match the largest register-resident row");
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// bf16 is the upper half of a binary32: widening is exact.  The element at
+// the lower address sits in the low 16 bits of each 32-bit word.
+__device__ __forceinline__ void widen8(const u32x4 v, float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+}
+
+// Round 8 binary32 values to bf16 (nearest, ties to even; NaN stays NaN).
+__device__ __forceinline__ u32x4 narrow8(const float f[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 p = {f[2 * i], f[2 * i + 1]};
+        r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+    }
+    return r;
+}
+
+// Keep a packed bf16x8 register value opaque to the optimiser, so that it
+// is widened where it is used and lives in 4 VGPRs rather than 8.  Without
+// this, loop-invariant code motion widens the weight once outside the row
+// loop, and common-subexpression elimination keeps the widened row alive
+// across the reduction; either doubles the register footprint and halves
+// occupancy.  Emits no instruction.
+__device__ __forceinline__ void keep_packed(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a fully active wavefront.  Inside each row of 16
+// lanes: xor-1 and xor-2 swaps (quad_perm), then the 8-lane and 16-lane
+// mirrors; each step adds two equal-shaped partial sums, so all lanes of a
+// row hold the same bits.  The four row sums are then combined as
+// (r0 + r1) + (r2 + r3) from scalar registers: the result is uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+template <int WPR>
+struct Layout {
+    static constexpr int kRowsPerBlock = WPR >= 4 ? 1 : 4 / WPR;
+    static constexpr int kThreads = kWave * WPR * kRowsPerBlock;
+    static constexpr int kLanesPerRow = kWave * WPR;
+};
+
+// Row total of a per-lane partial: one wavefront per row needs only the
+// wave sum; several wavefronts per row publish their sums in LDS (double
+// buffered by iteration parity, so one barrier per row suffices) and every
+// wavefront adds them in the same order.
+template <int WPR>
+__device__ __forceinline__ float row_sum(float part, int slot, int wave_in_row, int parity) {
+    float s = wave_sum(part);
+    if constexpr (WPR > 1) {
+        constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+        __shared__ float partials[2][RPB][WPR];
+        if ((threadIdx.x & (kWave - 1)) == 0) partials[parity][slot][wave_in_row] = s;
+        __syncthreads();
+        s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) s += partials[parity][slot][i];
+    }
+    return s;
+}
+
+__device__ __forceinline__ float rstd_of(float sum_sq, float hidden_f, float eps) {
+    return 1.0f / sqrtf(sum_sq / hidden_f + eps);
+}
+
+struct RmsArgs {
+    uint16_t* out;
+    const uint16_t* x;
+    const uint16_t* w;
+    int64_t rows;
+    int32_t nvec;     // hidden / 8
+    float hidden_f;
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// RMSNorm: VPL vectors per lane, WPR wavefronts per row.  FULL means every
+// lane's every slot is inside the row (no masking).
+// ---------------------------------------------------------------------------
+template <int VPL, int WPR, bool FULL>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_kernel(const RmsArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int L = Layout<WPR>::kLanesPerRow;
+    const int wave = threadIdx.x / kWave;
+    const int slot = wave / WPR;
+    const int wave_in_row = wave % WPR;
+    const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
+
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = k * L + t;
+        const bool in = FULL || v < a.nvec;
+        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v]
+                                        : u32x4{kOnesPair, kOnesPair, kOnesPair, kOnesPair};
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;  // wave-uniform; no barrier at WPR 1
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+
+        u32x4 xv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            xv[k] = in ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+        }
+
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[8];
+            widen8(xv[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+        }
+        const float rstd = rstd_of(row_sum<WPR>(part, slot, wave_in_row, parity), a.hidden_f, a.eps);
+
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            float f[8], g[8];
+            keep_packed(xv[k]);
+            widen8(xv[k], f);
+            keep_packed(wv[k]);
+            widen8(wv[k], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = (f[e] * rstd) * g[e];
+            if (in) yr[v] = narrow8(f);
+        }
+    }
+}
+
+struct RopeArgs {
+    uint16_t* out;
+    const uint16_t* x;
+    const uint16_t* w;
+    const float* cos_tab;
+    const float* sin_tab;
+    int64_t rows;
+    int64_t seq_len;
+    int32_t nvec;      // hidden / 8
+    int32_t nunits;    // hidden / 16: pair units per row
+    int32_t unit_per_head;  // head_dim / 16
+    int32_t half;      // head_dim / 2: floats per table row
+    float hidden_f;
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// RMSNorm + rotate-half RoPE: UPL pair units per lane (2 vectors each).
+// Unit u covers head h = u / (d/16), quarter q = u % (d/16): vectors
+// h*(d/8) + q (first half of the head) and that + d/16 (second half), and
+// table floats [8q, 8q + 8) of the row's position.
+// ---------------------------------------------------------------------------
+template <int UPL, int WPR, bool FULL>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_kernel(const RopeArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int L = Layout<WPR>::kLanesPerRow;
+    const int wave = threadIdx.x / kWave;
+    const int slot = wave / WPR;
+    const int wave_in_row = wave % WPR;
+    const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
+
+    int va[UPL], toff[UPL];
+    bool uin[UPL];
+    u32x4 wa[UPL], wb[UPL];
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+        const int u = k * L + t;
+        uin[k] = FULL || u < a.nunits;
+        const int h = u / a.unit_per_head;
+        const int q = u - h * a.unit_per_head;
+        va[k] = h * 2 * a.unit_per_head + q;
+        toff[k] = q * 8;
+        const u32x4 ones = {kOnesPair, kOnesPair, kOnesPair, kOnesPair};
+        const bool lw = a.w != nullptr && uin[k];
+        wa[k] = lw ? reinterpret_cast<const u32x4*>(a.w)[va[k]] : ones;
+        wb[k] = lw ? reinterpret_cast<const u32x4*>(a.w)[va[k] + a.unit_per_head] : ones;
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;
+        const int64_t pos = active ? row % a.seq_len : 0;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+        const float* crow = a.cos_tab + pos * a.half;
+        const float* srow = a.sin_tab + pos * a.half;
+
+        u32x4 xa[UPL], xb[UPL];
+#pragma unroll
+        for (int k = 0; k < UPL; ++k) {
+            const bool in = uin[k] && (WPR == 1 || active);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            xa[k] = in ? xr[va[k]] : z;
+            xb[k] = in ? xr[va[k] + a.unit_per_head] : z;
+        }
+
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < UPL; ++k) {
+            float f[8];
+            widen8(xa[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+            widen8(xb[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+        }
+        const float rstd = rstd_of(row_sum<WPR>(part, slot, wave_in_row, parity), a.hidden_f, a.eps);
+
+        // The table slices are L2-resident (every head and batch row shares
+        // them); loading them only now keeps 16 VGPRs per pair unit free
+        // while the row's own loads are in flight.
+#pragma unroll
+        for (int k = 0; k < UPL; ++k) {
+            const bool in = uin[k] && (WPR == 1 || active);
+            const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+            const f32x4* cp = reinterpret_cast<const f32x4*>(crow + toff[k]);
+            const f32x4* sp = reinterpret_cast<const f32x4*>(srow + toff[k]);
+            const f32x4 c0 = in ? cp[0] : zf, c1 = in ? cp[1] : zf;
+            const f32x4 s0 = in ? sp[0] : zf, s1 = in ? sp[1] : zf;
+            float ya[8], yb[8], g[8];
+            keep_packed(xa[k]);
+            keep_packed(xb[k]);
+            keep_packed(wa[k]);
+            keep_packed(wb[k]);
+            widen8(xa[k], ya);
+            widen8(wa[k], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ya[e] = (ya[e] * rstd) * g[e];
+            widen8(xb[k], yb);
+            widen8(wb[k], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yb[e] = (yb[e] * rstd) * g[e];
+            const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float o1[8], o2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o1[e] = ya[e] * c[e] - yb[e] * s[e];
+                o2[e] = yb[e] * c[e] + ya[e] * s[e];
+            }
+            if (in) {
+                yr[va[k]] = narrow8(o1);
+                yr[va[k] + a.unit_per_head] = narrow8(o2);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, per-hidden dispatch, launch.
+// ---------------------------------------------------------------------------
+
+struct Plan {
+    int wpr;    // wavefronts per row
+    int per;    // vectors (RMSNorm) or pair units (RoPE) per lane
+    bool full;  // no masking needed
+};
+
+// Smallest number of wavefronts per row that keeps the slice within
+// `max_per` items per lane, then the fewest items per lane for that count.
+Plan plan_for(int64_t items, int max_per) {
+    int wpr = 1;
+    while (items > (int64_t)kWave * wpr * max_per) wpr *= 2;
+    const int lanes = kWave * wpr;
+    const int per = (int)((items + lanes - 1) / lanes);
+    return Plan{wpr, per, items == (int64_t)per * lanes};
+}
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+template <typename Args>
+ltxnorm_status launch(const void* fn, int threads, int rows_per_block, int64_t rows, Args args,
+                      hipStream_t stream) {
+    const int64_t need = (rows + rows_per_block - 1) / rows_per_block;
+    const int64_t cap = (int64_t)cu_count() * kBlocksPerCU * 256 / threads;
+    const unsigned grid = (unsigned)(need < cap ? need : cap);
+    void* params[] = {&args};
+    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, stream);
+    return e == hipSuccess ? LTXNORM_OK : LTXNORM_ERR_HIP;
+}
+
+template <int WPR, int PER, bool FULL>
+ltxnorm_status launch_rms(const RmsArgs& a, hipStream_t s) {
+    return launch((const void*)&rmsnorm_kernel<PER, WPR, FULL>, Layout<WPR>::kThreads,
+                  Layout<WPR>::kRowsPerBlock, a.rows, a, s);
+}
+
+template <int WPR, int PER, bool FULL>
+ltxnorm_status launch_rope(const RopeArgs& a, hipStream_t s) {
+    return launch((const void*)&rmsnorm_rope_kernel<PER, WPR, FULL>, Layout<WPR>::kThreads,
+                  Layout<WPR>::kRowsPerBlock, a.rows, a, s);
+}
+
+template <int WPR, int PER, typename Args, typename L>
+ltxnorm_status pick_full(const Plan& p, const Args& a, hipStream_t s, L launcher) {
+    return p.full ? launcher.template go<WPR, PER, true>(a, s)
+                  : launcher.template go<WPR, PER, false>(a, s);
+}
+
+struct RmsLauncher {
+    template <int WPR, int PER, bool FULL>
+    ltxnorm_status go(const RmsArgs& a, hipStream_t s) const { return launch_rms<WPR, PER, FULL>(a, s); }
+};
+struct RopeLauncher {
+    template <int WPR, int PER, bool FULL>
+    ltxnorm_status go(const RopeArgs& a, hipStream_t s) const { return launch_rope<WPR, PER, FULL>(a, s); }
+};
+
+template <int WPR, int LO, int HI, typename Args, typename L>
+ltxnorm_status by_per(const Plan& p, const Args& a, hipStream_t s, L launcher) {
+    if constexpr (LO > HI) {
+        return LTXNORM_ERR_UNSUPPORTED;
+    } else {
+        if (p.per == LO) return pick_full<WPR, LO>(p, a, s, launcher);
+        return by_per<WPR, LO + 1, HI>(p, a, s, launcher);
+    }
+}
+
+// One wavefront per row covers 1..MAXP items per lane; with several
+// wavefronts the plan always lands in (MAXP/2, MAXP].
+template <int MAXP, typename Args, typename L>
+ltxnorm_status by_plan(const Plan& p, const Args& a, hipStream_t s, L launcher) {
+    constexpr int MID = MAXP / 2 + 1;
+    switch (p.wpr) {
+        case 1: return by_per<1, 1, MAXP>(p, a, s, launcher);
+        case 2: return by_per<2, MID, MAXP>(p, a, s, launcher);
+        case 4: return by_per<4, MID, MAXP>(p, a, s, launcher);
+        case 8: return by_per<8, MID, MAXP>(p, a, s, launcher);
+        case 16: return by_per<16, MID, MAXP>(p, a, s, launcher);
+        default: return LTXNORM_ERR_UNSUPPORTED;
+    }
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Half-open byte ranges [a, a + na) and [b, b + nb) overlap.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+// Checks shared by both entry points, in order: shape, scalar value, empty,
+// pointers, alignment, aliasing.  Returns OK with *empty set when there is
+// nothing to launch.
+ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_t rows,
+                            int64_t hidden, float eps, bool* empty) {
+    *empty = false;
+    if (rows < 0 || hidden <= 0) return LTXNORM_ERR_SHAPE;
+    if (hidden % kElemsPerVec != 0 || hidden > LTXNORM_MAX_HIDDEN) return LTXNORM_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / (hidden * 2)) return LTXNORM_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return LTXNORM_ERR_VALUE;
+    if (rows == 0) {
+        *empty = true;
+        return LTXNORM_OK;
+    }
+    if (out == nullptr || x == nullptr) return LTXNORM_ERR_NULL;
+    if (misaligned(out) || misaligned(x) || (weight && misaligned(weight))) return LTXNORM_ERR_ALIGN;
+    const int64_t nbytes = rows * hidden * 2;
+    if (out != x && overlap(out, nbytes, x, nbytes)) return LTXNORM_ERR_ALIAS;
+    if (weight && overlap(out, nbytes, weight, hidden * 2)) return LTXNORM_ERR_ALIAS;
+    return LTXNORM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ltxnorm_status ltxnorm_rmsnorm_fwd(void* out, const void* x, const void* weight, int64_t rows,
+                                   int64_t hidden, float eps, hipStream_t stream) {
+    bool empty = false;
+    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, &empty);
+    if (st != LTXNORM_OK || empty) return st;
+    const int64_t nvec = hidden / kElemsPerVec;
+    const Plan p = plan_for(nvec, kMaxVecPerLane);
+    const RmsArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
+                    static_cast<const uint16_t*>(weight), rows, (int32_t)nvec, (float)hidden, eps};
+    return by_plan<kMaxVecPerLane>(p, a, stream, RmsLauncher{});
+}
+
+ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void* out, const void* x, const void* weight,
+                                        const float* cos_tab, const float* sin_tab, int64_t rows,
+                                        int64_t hidden, int32_t heads, int32_t head_dim,
+                                        int64_t seq_len, float eps, hipStream_t stream) {
+    if (heads < 1 || head_dim < 16 || head_dim % 16 != 0 || seq_len < 1 ||
+        (int64_t)heads * head_dim != hidden)
+        return LTXNORM_ERR_SHAPE;
+    if (seq_len > INT64_MAX / (head_dim * 4)) return LTXNORM_ERR_SHAPE;
+    bool empty = false;
+    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, &empty);
+    if (st != LTXNORM_OK || empty) return st;
+    if (cos_tab == nullptr || sin_tab == nullptr) return LTXNORM_ERR_NULL;
+    if (misaligned(cos_tab) || misaligned(sin_tab)) return LTXNORM_ERR_ALIGN;
+    const int64_t nbytes = rows * hidden * 2;
+    const int64_t tbytes = seq_len * (head_dim / 2) * 4;
+    if (overlap(out, nbytes, cos_tab, tbytes) || overlap(out, nbytes, sin_tab, tbytes))
+        return LTXNORM_ERR_ALIAS;
+    const int64_t nunits = hidden / (2 * kElemsPerVec);
+    const Plan p = plan_for(nunits, kMaxVecPerLane / 2);
+    const RopeArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(weight), cos_tab, sin_tab, rows, seq_len,
+                     (int32_t)(hidden / kElemsPerVec), (int32_t)nunits, head_dim / 16,
+                     head_dim / 2, (float)hidden, eps};
+    return by_plan<kMaxVecPerLane / 2>(p, a, stream, RopeLauncher{});
+}
+
+const char* ltxnorm_status_str(ltxnorm_status s) {
+    switch (s) {
+        case LTXNORM_OK: return "ok";
+        case LTXNORM_ERR_NULL: return "a required pointer is NULL";
+        case LTXNORM_ERR_SHAPE: return "invalid shape (rows, hidden, heads, head_dim or seq_len)";
+        case LTXNORM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case LTXNORM_ERR_UNSUPPORTED: return "hidden must be a multiple of 8 and at most 65536";
+        case LTXNORM_ERR_ALIAS: return "out overlaps an input other than exactly x";
+        case LTXNORM_ERR_VALUE: return "eps must be finite and non-negative";
+        case LTXNORM_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    }
+    return "unknown ltxnorm status";
+}
+
+int ltxnorm_version(void) { return LTXNORM_ABI_VERSION; }
+
+}  // extern "C"

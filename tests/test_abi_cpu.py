@@ -1,0 +1,131 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Only calls that fail validation (or have rows == 0) are made here; those
+return before the library touches the HIP runtime, so fake addresses are
+never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rmsnorm_video_dit_amd as ltx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ltxnorm.h")
+
+A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ltxnorm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
+                                    "ltxnorm_status_str", "ltxnorm_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ltx.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", ltx.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (ltxnorm_\w+)", nm.stdout))
+    assert exported == set(declared_functions())
+
+
+def test_library_targets_gfx950_only():
+    """The offload bundle inside the library (built here) names one target."""
+    data = open(ltx.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx[0-9a-z]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_version_and_status_strings():
+    assert ltx.ltxnorm_version() == 1
+    seen = set()
+    for code in range(8):
+        s = ltx.ltxnorm_status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert ltx.ltxnorm_status_str(99) == "unknown ltxnorm status"
+    assert ltx.ltxnorm_status_str(0) == "ok"
+
+
+def rms(out=A, x=A + 64 * MB, w=None, rows=4, hidden=2048, eps=1e-6):
+    return ltx.ltxnorm_rmsnorm_fwd_status(out, x, w, rows, hidden, eps, 0)
+
+
+def rope(out=A, x=A + 64 * MB, w=None, c=A + 128 * MB, s=A + 129 * MB, rows=4, hidden=2048,
+         heads=32, head_dim=64, seq_len=16, eps=1e-6):
+    return ltx.ltxnorm_rmsnorm_rope_fwd_status(out, x, w, c, s, rows, hidden, heads, head_dim,
+                                               seq_len, eps, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), ltx.ERR_SHAPE),
+    (dict(hidden=0), ltx.ERR_SHAPE),
+    (dict(hidden=-8), ltx.ERR_SHAPE),
+    (dict(hidden=2047), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=12), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=65544), ltx.ERR_UNSUPPORTED),
+    (dict(rows=1 << 62), ltx.ERR_SHAPE),
+    (dict(eps=-1e-6), ltx.ERR_VALUE),
+    (dict(eps=float("nan")), ltx.ERR_VALUE),
+    (dict(eps=float("inf")), ltx.ERR_VALUE),
+    (dict(out=None), ltx.ERR_NULL),
+    (dict(x=None), ltx.ERR_NULL),
+    (dict(out=A + 2), ltx.ERR_ALIGN),
+    (dict(x=A + 64 * MB + 8), ltx.ERR_ALIGN),
+    (dict(w=A + 200 * MB + 4), ltx.ERR_ALIGN),
+    (dict(x=A + 4096), ltx.ERR_ALIAS),            # partial overlap, out before x
+    (dict(out=A + 64 * MB + 16), ltx.ERR_ALIAS),  # partial overlap, out after x
+    (dict(w=A + 1024), ltx.ERR_ALIAS),            # weight inside out
+])
+def test_rmsnorm_validation(kw, status):
+    assert rms(**kw) == status
+
+
+def test_rmsnorm_empty_is_ok_without_pointers():
+    assert rms(out=None, x=None, rows=0) == ltx.OK
+    assert rope(out=None, x=None, c=None, s=None, rows=0) == ltx.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=2048, heads=16), ltx.ERR_SHAPE),         # hidden != heads * head_dim
+    (dict(hidden=1280, heads=32, head_dim=40), ltx.ERR_SHAPE),  # head_dim % 16 != 0
+    (dict(hidden=256, heads=32, head_dim=8), ltx.ERR_SHAPE),
+    (dict(heads=0), ltx.ERR_SHAPE),
+    (dict(seq_len=0), ltx.ERR_SHAPE),
+    (dict(c=None), ltx.ERR_NULL),
+    (dict(s=None), ltx.ERR_NULL),
+    (dict(c=A + 128 * MB + 8), ltx.ERR_ALIGN),
+    (dict(s=A + 129 * MB + 4), ltx.ERR_ALIGN),
+    (dict(c=A + 256), ltx.ERR_ALIAS),
+    (dict(s=A - 64), ltx.ERR_ALIAS),   # table [A-64, A-64+8192) reaches into out
+    (dict(x=A + 2), ltx.ERR_ALIGN),
+    (dict(eps=-0.5), ltx.ERR_VALUE),
+])
+def test_rope_validation(kw, status):
+    assert rope(**kw) == status
+
+
+def test_python_front_end_refuses_host_tensors():
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ltx.rmsnorm(x)
+    with pytest.raises(ValueError):
+        ltx.rmsnorm_rope(x, None, torch.zeros(4, 8), torch.zeros(4, 8), 4, 16)
+
+
+def test_error_raises_with_status():
+    with pytest.raises(ltx.LtxnormError) as e:
+        ltx.ltxnorm_rmsnorm_fwd(A, A + 64 * MB, None, 4, 2047, 1e-6, 0)
+    assert e.value.status == ltx.ERR_UNSUPPORTED

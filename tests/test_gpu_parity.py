@@ -1,0 +1,318 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Every comparison uses the rule of parity.py (1 bf16 ulp of the oracle's
+binary32 result rounded to bf16; a 2^-16 * m floor for cancelling RoPE
+outputs).  Full-size workloads are compared at every element, in the same
+launch configuration the benchmark times (the library's own dispatch).
+Invariants that must hold bit-exactly on the GPU are checked bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import rmsnorm_video_dit_amd as ltx
+from parity import compare_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ORC = oracle.Oracle()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_bits(t):
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def run_rms(x, w, eps=1e-6):
+    xt = dev_bf16(x)
+    wt = None if w is None else dev_bf16(w)
+    return host_bits(ltx.rmsnorm(xt, wt, eps))
+
+
+def run_rope(x, w, c, s, heads, head_dim, eps=1e-6):
+    xt = dev_bf16(x)
+    wt = None if w is None else dev_bf16(w)
+    return host_bits(ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), heads, head_dim, eps))
+
+
+def check_rms(x, w, eps=1e-6, label=""):
+    got = run_rms(x, w, eps)
+    ref32, ref16 = ORC.round(ORC.rmsnorm(x, w, eps))
+    rep = compare_bf16(got, ref16, None, ref32)
+    print(label, rep, flush=True)
+    assert rep["pass"], (label, rep)
+    return got, rep
+
+
+def check_rope(x, w, c, s, heads, head_dim, eps=1e-6, label=""):
+    got = run_rope(x, w, c, s, heads, head_dim, eps)
+    y, mag = ORC.rmsnorm_rope(x, w, c, s, heads, head_dim, eps, with_mag=True)
+    ref32, ref16 = ORC.round(y)
+    rep = compare_bf16(got, ref16, mag, ref32)
+    print(label, rep, flush=True)
+    assert rep["pass"], (label, rep)
+    return got, rep
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(datagen.CONFIGS))
+def test_workload_full_size(name):
+    cfg = datagen.CONFIGS[name]
+    announce(f"workload {name} rows={cfg.rows} hidden={cfg.hidden} seed={datagen.BASE_SEED}")
+    inp = datagen.make_inputs(cfg)
+    if cfg.rope:
+        got, rep = check_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg.heads, cfg.head_dim,
+                              cfg.eps, label=name)
+    else:
+        got, rep = check_rms(inp["x"], inp["w"], cfg.eps, label=name)
+    assert rep["max_ulp"] <= 1.0
+    # nearly every element matches bit for bit; the rest are single rounding flips
+    assert rep["n_bit_exact"] >= 0.99 * rep["n"]
+
+
+# ---------------------------------------------------------------------------
+# Edge shapes: ragged tails, one/several wavefronts per row, the hidden cap
+# ---------------------------------------------------------------------------
+
+HIDDENS = [8, 64, 520, 1000, 2048, 3072, 4096, 4104, 6144, 8192, 12296, 16384, 32768, 65536]
+ROWS = [1, 3, 5, 1023]
+
+
+@pytest.mark.parametrize("hidden", HIDDENS)
+@pytest.mark.parametrize("rows", ROWS)
+def test_rmsnorm_edge_shapes(rows, hidden):
+    if rows * hidden > (1 << 24):
+        rows = max(1, (1 << 24) // hidden)
+    announce(f"rmsnorm rows={rows} hidden={hidden}")
+    x = datagen.make_x(rows, hidden, seed=hidden * 7 + rows, stream=1)
+    w = datagen.make_w(hidden, seed=hidden * 7 + rows, stream=2)
+    check_rms(x, w, label=f"rms {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("heads,head_dim", [(1, 16), (3, 16), (32, 64), (5, 64), (16, 128),
+                                            (24, 128), (8, 256), (64, 128), (96, 128),
+                                            (512, 128), (1, 1024)])
+@pytest.mark.parametrize("rows,seq_len", [(1, 1), (7, 3), (37, 4096), (1000, 17)])
+def test_rope_edge_shapes(heads, head_dim, rows, seq_len):
+    hidden = heads * head_dim
+    if rows * hidden > (1 << 24):
+        rows = max(1, (1 << 24) // hidden)
+    announce(f"rope rows={rows} heads={heads} head_dim={head_dim} seq_len={seq_len}")
+    x = datagen.make_x(rows, hidden, seed=hidden + rows, stream=1)
+    w = datagen.make_w(hidden, seed=hidden + rows, stream=2)
+    c, s = datagen.rope_tables(seq_len, head_dim, 10000.0)
+    check_rope(x, w, c, s, heads, head_dim, label=f"rope {rows}x{heads}x{head_dim} S={seq_len}")
+
+
+def test_rope_outlier_values_and_null_weight():
+    announce("rope outliers, weight None")
+    x = datagen.make_x(300, 2048, seed=5, stream=1, sigma=2.0, outlier_p=0.01, outlier_scale=50.0)
+    c, s = datagen.rope_tables(4096, 64, 10000.0)
+    check_rope(x, None, c, s, 32, 64, label="rope outliers")
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact invariants on the GPU
+# ---------------------------------------------------------------------------
+
+def test_deterministic_run_to_run():
+    announce("determinism 4096x3072 and rope 2048x2048")
+    x = datagen.make_x(4096, 3072, seed=1, stream=1)
+    w = datagen.make_w(3072, seed=1, stream=2)
+    a, b = run_rms(x, w), run_rms(x, w)
+    assert np.array_equal(a, b)
+    x = datagen.make_x(2048, 2048, seed=2, stream=1)
+    c, s = datagen.rope_tables(4096, 64)
+    assert np.array_equal(run_rope(x, w[:2048], c, s, 32, 64), run_rope(x, w[:2048], c, s, 32, 64))
+
+
+@pytest.mark.parametrize("hidden", [3072, 8192])
+def test_batch_invariance(hidden):
+    """A row's output does not depend on how many rows are in the call."""
+    announce(f"batch invariance hidden={hidden}")
+    x = datagen.make_x(2000, hidden, seed=3, stream=1)
+    w = datagen.make_w(hidden, seed=3, stream=2)
+    full = run_rms(x, w)
+    for lo, hi in ((0, 1), (17, 18), (5, 1000), (1999, 2000)):
+        assert np.array_equal(run_rms(x[lo:hi], w), full[lo:hi]), (lo, hi)
+
+
+@pytest.mark.parametrize("hidden", [2048, 3072, 16384])
+def test_in_place_equals_out_of_place(hidden):
+    announce(f"in-place hidden={hidden}")
+    x = datagen.make_x(513, hidden, seed=4, stream=1)
+    w = datagen.make_w(hidden, seed=4, stream=2)
+    ref = run_rms(x, w)
+    xt, wt = dev_bf16(x), dev_bf16(w)
+    ltx.rmsnorm(xt, wt, 1e-6, out=xt)
+    assert np.array_equal(host_bits(xt), ref)
+    c, s = datagen.rope_tables(100, 64)
+    heads = hidden // 64
+    ref = run_rope(x, w, c, s, heads, 64)
+    xt = dev_bf16(x)
+    ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), heads, 64, 1e-6, out=xt)
+    assert np.array_equal(host_bits(xt), ref)
+
+
+@pytest.mark.parametrize("hidden", [520, 3072, 8192])
+def test_null_weight_equals_ones(hidden):
+    announce(f"null weight hidden={hidden}")
+    x = datagen.make_x(64, hidden, seed=6, stream=1)
+    ones = np.full(hidden, 0x3F80, dtype=np.uint16)
+    assert np.array_equal(run_rms(x, None), run_rms(x, ones))
+    c, s = datagen.rope_tables(9, 64)
+    heads = hidden // 64 if hidden % 64 == 0 else None
+    if heads:
+        assert np.array_equal(run_rope(x, None, c, s, heads, 64), run_rope(x, ones, c, s, heads, 64))
+
+
+def test_rope_position_zero_is_rmsnorm():
+    announce("rope at position 0")
+    x = datagen.make_x(50, 2048, seed=8, stream=1)
+    w = datagen.make_w(2048, seed=8, stream=2)
+    c, s = datagen.rope_tables(1, 64)
+    assert np.array_equal(run_rope(x, w, c, s, 32, 64), run_rms(x, w))
+
+
+def test_sign_symmetry_and_scale_invariance():
+    """y(-x) = -y(x); with eps = 0, y(2^k x) = y(x) (correctly rounded divide
+    and square root scale exactly by powers of two)."""
+    announce("sign and scale")
+    x = datagen.make_x(256, 3072, seed=9, stream=1)
+    w = datagen.make_w(3072, seed=9, stream=2)
+    base = run_rms(x, w, 0.0)
+    assert np.array_equal(run_rms(x ^ np.uint16(0x8000), w, 0.0), base ^ np.uint16(0x8000))
+    xv = datagen.bf16_bits_to_f32(x).astype(np.float64)
+    for k in (-8, -3, 2, 8):
+        assert np.array_equal(run_rms(datagen.to_bf16_bits(xv * 2.0 ** k), w, 0.0), base), k
+
+
+def test_rope_pair_norm():
+    """The rotation keeps each pair's norm (within the outputs' bf16 rounding)."""
+    announce("rope pair norm")
+    x = datagen.make_x(64, 2048, seed=10, stream=1)
+    c, s = datagen.rope_tables(4096, 64)
+    got = datagen.bf16_bits_to_f32(run_rope(x, None, c, s, 32, 64)).astype(np.float64)
+    plain = datagen.bf16_bits_to_f32(run_rms(x, None)).astype(np.float64)
+    g = got.reshape(64, 32, 2, 32)
+    p = plain.reshape(64, 32, 2, 32)
+    n_rot = g[:, :, 0] ** 2 + g[:, :, 1] ** 2
+    n_in = p[:, :, 0] ** 2 + p[:, :, 1] ** 2
+    assert np.allclose(n_rot, n_in, rtol=2 * 2.0 ** -7, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Special values
+# ---------------------------------------------------------------------------
+
+def test_zero_rows_and_eps_zero_nan():
+    announce("zero rows")
+    x = datagen.make_x(8, 2048, seed=11, stream=1)
+    x[2] = 0
+    x[5, ::7] = 0
+    got, _ = check_rms(x, datagen.make_w(2048, seed=11, stream=2), 1e-6, label="zeros")
+    assert np.all(got[2] == 0) and np.all((got[5, ::7] & 0x7FFF) == 0)
+    # eps = 0 and an all-zero row: 0 * inf = NaN on both sides
+    got = run_rms(x, None, 0.0)
+    assert np.all(np.isnan(datagen.bf16_bits_to_f32(got[2])))
+    check_rms(x, None, 0.0, label="eps0 zero row (NaN must meet NaN)")
+
+
+def test_round_to_nearest_even_on_exact_ties():
+    """Rows of 1s and 3s with mean square exactly 4 make rstd = 0.5 exactly,
+    so y = x * 0.5 * w is exact in binary32 and the only rounding is the
+    final bf16 one; weights 1 + 3*2^-7 put 1.5 * w exactly halfway between
+    two bf16 values: the result must be the even one, bit-exactly."""
+    announce("exact ties")
+    pattern = np.array([1, 1, 1, 1, 1, 3, 3, 3], dtype=np.float64)  # sum of squares 32 = 4 * 8
+    x = datagen.to_bf16_bits(np.tile(pattern, (4, 64 // 8)))
+    w = np.full(64, 0x3F83, dtype=np.uint16)          # 1 + 3 * 2^-7
+    w[1::2] = 0x3F81                                   # 1 + 2^-7: 1.5 w = 1.5 + 1.5 ulp
+    got = run_rms(x, w, 0.0)
+    _, ref16 = ORC.round(ORC.rmsnorm(x, w, 0.0))
+    assert np.array_equal(got, ref16)
+    three = x == 0x4040
+    assert np.all(got[three & (w == 0x3F83)[None, :]] == 0x3FC4)   # tie 4.5 ulp -> even 4
+    assert np.all(got[three & (w == 0x3F81)[None, :]] == 0x3FC2)   # tie 1.5 ulp -> even 2
+
+
+# ---------------------------------------------------------------------------
+# Memory safety and the boundary on the device
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,hidden", [(1, 8), (7, 520), (33, 3072), (5, 12296)])
+def test_guard_bands_survive(rows, hidden):
+    """Sentinels before and after the output (and the input) are untouched."""
+    announce(f"guard bands rows={rows} hidden={hidden}")
+    pad = 4096
+    x = datagen.make_x(rows, hidden, seed=12, stream=1)
+    w = datagen.make_w(hidden, seed=12, stream=2)
+    n = rows * hidden
+    buf = torch.full((n + 2 * pad,), 0x7A5A, dtype=torch.int16, device=DEV)
+    out = buf[pad:pad + n].view(torch.bfloat16).view(rows, hidden)
+    xt = dev_bf16(x)
+    ltx.rmsnorm(xt, dev_bf16(w), 1e-6, out=out)
+    b = host_bits(buf.view(torch.bfloat16))
+    assert np.all(b[:pad] == 0x7A5A) and np.all(b[pad + n:] == 0x7A5A)
+    assert np.array_equal(b[pad:pad + n].reshape(rows, hidden), run_rms(x, w))
+    assert np.array_equal(host_bits(xt), x)  # input untouched
+    if hidden % 64 == 0:
+        heads = hidden // 64
+        c, s = datagen.rope_tables(5, 64)
+        buf.fill_(0x7A5A)
+        ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), heads, 64, 1e-6, out=out)
+        b = host_bits(buf.view(torch.bfloat16))
+        assert np.all(b[:pad] == 0x7A5A) and np.all(b[pad + n:] == 0x7A5A)
+
+
+def test_rejected_calls_write_nothing():
+    announce("rejected calls")
+    x = dev_bf16(datagen.make_x(4, 2048, seed=13, stream=1))
+    buf = torch.full((4 * 2048 + 8,), 0x1234, dtype=torch.int16, device=DEV)
+    mis = buf.data_ptr() + 2  # 2-byte offset: misaligned
+    st = ltx.ltxnorm_rmsnorm_fwd_status(mis, x, None, 4, 2048, 1e-6, None)
+    assert st == ltx.ERR_ALIGN
+    st = ltx.ltxnorm_rmsnorm_fwd_status(buf, x, None, 4, 2040 + 4, 1e-6, None)
+    assert st == ltx.ERR_UNSUPPORTED
+    assert np.all(host_bits(buf.view(torch.bfloat16)) == 0x1234)
+
+
+def test_empty_input():
+    announce("empty")
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV)
+    assert ltx.rmsnorm(x).shape == (0, 2048)
+    c = torch.zeros((4, 32), dtype=torch.float32, device=DEV)
+    assert ltx.rmsnorm_rope(x, None, c, c, 32, 64).shape == (0, 2048)
+
+
+def test_side_stream():
+    """Work goes on the caller's stream."""
+    announce("side stream")
+    x = datagen.make_x(1024, 3072, seed=14, stream=1)
+    w = datagen.make_w(3072, seed=14, stream=2)
+    xt, wt = dev_bf16(x), dev_bf16(w)
+    out = torch.empty_like(xt)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ltx.ltxnorm_rmsnorm_fwd(out, xt, wt, 1024, 3072, 1e-6, s)
+    s.synchronize()
+    assert np.array_equal(host_bits(out), run_rms(x, w))
