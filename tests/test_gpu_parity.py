@@ -83,7 +83,12 @@ def test_workload_full_size(name):
                               cfg.eps, label=name)
     else:
         got, rep = check_rms(inp["x"], inp["w"], cfg.eps, label=name)
-    assert rep["max_ulp"] <= 1.0
+    if cfg.rope:
+        # only outputs whose two products cancel may differ by more than an
+        # ulp of their (small) value, and only within the 2^-16 * m floor
+        assert rep["n_floor_bound"] <= 1e-5 * rep["n"]
+    else:
+        assert rep["max_ulp"] <= 1.0
     # nearly every element matches bit for bit; the rest are single rounding flips
     assert rep["n_bit_exact"] >= 0.99 * rep["n"]
 
