@@ -254,7 +254,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / sec / 1e9, 2),
-                     "kernel": "rmsnorm_kernel<VPL=6, WPR=1, FULL>",
+                     "kernel": "rmsnorm_kernel",
                      "kernel_us": round(sec * 1e6, 3)},
         "baseline_note": "vs_baseline divides by the H100 figure for this shape on the "
                          "pages (0.157 ms = 1282.4 GB/s); another GPU, context only",

@@ -35,8 +35,7 @@
  *   - The destination comes first, as in an out-variant op.
  *   - Arguments are validated on the host before any HIP call; a rejected
  *     call enqueues nothing.  No C++ exception crosses this boundary.
- *   - Calls are thread-safe and reentrant.  The only state kept is a cached
- *     per-device compute-unit count used to size launches.
+ *   - Calls are thread-safe and reentrant; the library keeps no state.
  */
 #ifndef LTXNORM_H
 #define LTXNORM_H

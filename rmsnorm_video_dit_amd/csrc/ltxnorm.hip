@@ -17,8 +17,9 @@
 //  * A row is held entirely in VGPRs: HBM is read once and written once.
 //    Every access is a 16-byte bf16x8 vector; consecutive lanes touch
 //    consecutive vectors, so one load instruction covers 1 KiB contiguous.
-//  * One wavefront per row for hidden <= 4096 (up to 8 vectors per lane),
-//    otherwise 2..16 wavefronts per row whose partial sums meet in LDS.
+//  * One wavefront per row for hidden <= 2048 (up to 4 vectors per lane),
+//    otherwise 3..16 wavefronts per row (about 2 vectors per lane) whose
+//    partial sums meet in LDS.
 //  * Sum of squares: per-lane fp32 FMAs in a fixed order, then a fixed
 //    DPP butterfly inside each 16-lane row (quad_perm, row_half_mirror,
 //    row_mirror) and four readlanes; every lane ends with identical bits and
@@ -26,9 +27,9 @@
 //  * rstd = 1 / sqrt(sum / H + eps) with correctly rounded binary32 divide
 //    and square root: it scales exactly under x -> 2^k x, and costs nothing
 //    next to the row's memory traffic.
-//  * The weight (and for RoPE each lane's table offsets) is loaded into
-//    registers once per wavefront; the grid is capped near the resident
-//    capacity so each wavefront walks several rows and reuses them.
+//  * The weight slice (and for RoPE each lane's table offsets) is loaded at
+//    the start, in flight together with the row; one workgroup per 1-4 rows.
+//  * x is loaded and y stored with the non-temporal hint (streamed once).
 //  * RoPE pairs element i with i + head_dim/2.  With 8 elements per vector
 //    both halves of a pair are whole vectors, head_dim/16 vectors apart, so
 //    each lane loads a vector and its partner ("pair unit") and rotates in
@@ -40,7 +41,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -57,7 +57,7 @@ constexpr int kWave = 64;
 constexpr int kElemsPerVec = 8;       // bf16 values per 16-byte vector
 constexpr int kMaxVecPerLane = 8;     // register budget for one row slice
 constexpr int kMaxWavesPerRow = 16;   // 1024-thread workgroup
-constexpr int kBlocksPerCU = 8;       // grid cap: resident 256-thread blocks per CU
+constexpr int64_t kMaxGrid = 1 << 30; // rows beyond grid * rows-per-block loop
 constexpr uint32_t kOnesPair = 0x3F803F80u;  // two bf16 1.0
 
 static_assert(LTXNORM_MAX_HIDDEN == kMaxWavesPerRow * kWave * kMaxVecPerLane * kElemsPerVec,
@@ -96,6 +96,13 @@ __device__ __forceinline__ u32x4 narrow8(const float f[8]) {
 // occupancy.  Emits no instruction.
 __device__ __forceinline__ void keep_packed(u32x4& v) { asm volatile("" : "+v"(v)); }
 
+// x is read once and y written once: stream both past the caches with the
+// non-temporal hint (measured ~3% more HBM throughput than plain accesses on
+// a 50/50 read/write stream).  Weights and rotation tables, which every row
+// reuses, use ordinary cached loads.
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
@@ -120,9 +127,11 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Rows per workgroup: four single-wavefront rows (256 threads), two rows of
+// 2-3 wavefronts, one row of 4-16 wavefronts (256-1024 threads).
 template <int WPR>
 struct Layout {
-    static constexpr int kRowsPerBlock = WPR >= 4 ? 1 : 4 / WPR;
+    static constexpr int kRowsPerBlock = WPR == 1 ? 4 : (WPR <= 3 ? 2 : 1);
     static constexpr int kThreads = kWave * WPR * kRowsPerBlock;
     static constexpr int kLanesPerRow = kWave * WPR;
 };
@@ -197,7 +206,7 @@ rmsnorm_kernel(const RmsArgs a) {
         for (int k = 0; k < VPL; ++k) {
             const int v = k * L + t;
             const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
-            xv[k] = in ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+            xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
         }
 
         float part = 0.0f;
@@ -221,7 +230,7 @@ rmsnorm_kernel(const RmsArgs a) {
             widen8(wv[k], g);
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[e] = (f[e] * rstd) * g[e];
-            if (in) yr[v] = narrow8(f);
+            if (in) store_stream(yr + v, narrow8(f));
         }
     }
 }
@@ -292,8 +301,8 @@ rmsnorm_rope_kernel(const RopeArgs a) {
         for (int k = 0; k < UPL; ++k) {
             const bool in = uin[k] && (WPR == 1 || active);
             const u32x4 z = {0u, 0u, 0u, 0u};
-            xa[k] = in ? xr[va[k]] : z;
-            xb[k] = in ? xr[va[k] + a.unit_per_head] : z;
+            xa[k] = in ? load_stream(xr + va[k]) : z;
+            xb[k] = in ? load_stream(xr + va[k] + a.unit_per_head) : z;
         }
 
         float part = 0.0f;
@@ -342,9 +351,102 @@ rmsnorm_rope_kernel(const RopeArgs a) {
                 o2[e] = yb[e] * c[e] + ya[e] * s[e];
             }
             if (in) {
-                yr[va[k]] = narrow8(o1);
-                yr[va[k] + a.unit_per_head] = narrow8(o2);
+                store_stream(yr + va[k], narrow8(o1));
+                store_stream(yr + va[k] + a.unit_per_head, narrow8(o2));
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + rotate-half RoPE with the RMSNorm lane layout, for head_dim a
+// power of two from 16 to 512.  Lane t holds vectors k*L + t (full 1 KiB
+// lines per load instruction).  With P = head_dim / 16 vectors per half
+// head, the partner of vector v is v ^ P: the same slot of lane t ^ P in the
+// same wavefront.  Each lane normalises its own vector and fetches the
+// partner's normalised binary32 values with ds_bpermute (exchanging the
+// finished values rather than raw x halves the VALU work per vector, which
+// matters because with one row per wavefront the whole grid is resident and
+// compute is not hidden behind later loads).  A lane's half (bit P of t) and
+// its table slice (floats 8 * (t mod P) .. + 8) do not depend on the slot, so
+// each lane reads 8 cos and 8 sin values per row.
+// ---------------------------------------------------------------------------
+template <int VPL, int WPR, bool FULL>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_xor_kernel(const RopeArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int L = Layout<WPR>::kLanesPerRow;
+    const int wave = threadIdx.x / kWave;
+    const int slot = wave / WPR;
+    const int wave_in_row = wave % WPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = wave_in_row * kWave + lane;
+    const int P = a.unit_per_head;
+    const int src = ((lane ^ P) & (kWave - 1)) << 2;  // ds_bpermute byte address
+    const float sgn = (t & P) ? 1.0f : -1.0f;  // second half adds, first subtracts
+    const int toff = (t & (P - 1)) * 8;
+
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = k * L + t;
+        const bool in = FULL || v < a.nvec;
+        const u32x4 ones = {kOnesPair, kOnesPair, kOnesPair, kOnesPair};
+        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v] : ones;
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;
+        const int64_t pos = active ? row % a.seq_len : 0;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+
+        u32x4 xv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[8];
+            widen8(xv[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+        }
+        const float rstd = rstd_of(row_sum<WPR>(part, slot, wave_in_row, parity), a.hidden_f, a.eps);
+
+        const f32x4* cp = reinterpret_cast<const f32x4*>(a.cos_tab + pos * a.half + toff);
+        const f32x4* sp = reinterpret_cast<const f32x4*>(a.sin_tab + pos * a.half + toff);
+        const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        // the partner term enters with -sin in the first half, +sin in the second
+        const float ss[8] = {sgn * s0[0], sgn * s0[1], sgn * s0[2], sgn * s0[3],
+                             sgn * s1[0], sgn * s1[1], sgn * s1[2], sgn * s1[3]};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            keep_packed(xv[k]);
+            keep_packed(wv[k]);
+            float own[8], g[8], par[8], o[8];
+            widen8(xv[k], own);
+            widen8(wv[k], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) own[e] = (own[e] * rstd) * g[e];
+            // the partner lane's normalised values, exact binary32 bits
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                par[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, own[e])));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = own[e] * c[e] + par[e] * ss[e];
+            if (in) store_stream(yr + v, narrow8(o));
         }
     }
 }
@@ -359,35 +461,33 @@ struct Plan {
     bool full;  // no masking needed
 };
 
-// Smallest number of wavefronts per row that keeps the slice within
-// `max_per` items per lane, then the fewest items per lane for that count.
-Plan plan_for(int64_t items, int max_per) {
+// How a row is split.  `items` are 16-byte vectors (RMSNorm) or pair units of
+// two vectors (RoPE).  A single wavefront takes the row while each lane holds
+// at most `one_wave_max` items; longer rows are spread over enough
+// wavefronts (up to 16) that each lane holds about `spread` items, and past
+// 16 wavefronts the lanes take more, up to the register budget.  Measured at
+// [16384 x 3072] (384 vectors per row): 3 wavefronts x 2 vectors reached
+// 6.08 TB/s, 2 x 3 6.02, 1 x 6 5.98, 6 x 1 5.46; at hidden 2048 one
+// wavefront x 4 vectors was best (6.11 TB/s) and 4 x 1 the worst.
+Plan plan_for(int64_t items, int one_wave_max, int spread) {
     int wpr = 1;
-    while (items > (int64_t)kWave * wpr * max_per) wpr *= 2;
-    const int lanes = kWave * wpr;
+    if (items > (int64_t)kWave * one_wave_max) {
+        const int64_t w = (items + (int64_t)kWave * spread - 1) / ((int64_t)kWave * spread);
+        wpr = (int)(w < kMaxWavesPerRow ? w : kMaxWavesPerRow);
+    }
+    const int64_t lanes = (int64_t)kWave * wpr;
     const int per = (int)((items + lanes - 1) / lanes);
     return Plan{wpr, per, items == (int64_t)per * lanes};
-}
-
-std::atomic<int> g_cu_count[64];
-
-int cu_count() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = g_cu_count[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        n = 256;
-    g_cu_count[dev].store(n, std::memory_order_relaxed);
-    return n;
 }
 
 template <typename Args>
 ltxnorm_status launch(const void* fn, int threads, int rows_per_block, int64_t rows, Args args,
                       hipStream_t stream) {
+    // One workgroup per group of rows: a grid-stride loop capped at the
+    // resident capacity measured 3-4% slower than letting the dispatcher
+    // stream fresh workgroups, which keeps every CU busy to the last rows.
     const int64_t need = (rows + rows_per_block - 1) / rows_per_block;
-    const int64_t cap = (int64_t)cu_count() * kBlocksPerCU * 256 / threads;
-    const unsigned grid = (unsigned)(need < cap ? need : cap);
+    const unsigned grid = (unsigned)(need < kMaxGrid ? need : kMaxGrid);
     void* params[] = {&args};
     const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), params, 0, stream);
     return e == hipSuccess ? LTXNORM_OK : LTXNORM_ERR_HIP;
@@ -419,6 +519,13 @@ struct RopeLauncher {
     template <int WPR, int PER, bool FULL>
     ltxnorm_status go(const RopeArgs& a, hipStream_t s) const { return launch_rope<WPR, PER, FULL>(a, s); }
 };
+struct RopeXorLauncher {
+    template <int WPR, int PER, bool FULL>
+    ltxnorm_status go(const RopeArgs& a, hipStream_t s) const {
+        return launch((const void*)&rmsnorm_rope_xor_kernel<PER, WPR, FULL>, Layout<WPR>::kThreads,
+                      Layout<WPR>::kRowsPerBlock, a.rows, a, s);
+    }
+};
 
 template <int WPR, int LO, int HI, typename Args, typename L>
 ltxnorm_status by_per(const Plan& p, const Args& a, hipStream_t s, L launcher) {
@@ -430,17 +537,28 @@ ltxnorm_status by_per(const Plan& p, const Args& a, hipStream_t s, L launcher) {
     }
 }
 
-// One wavefront per row covers 1..MAXP items per lane; with several
-// wavefronts the plan always lands in (MAXP/2, MAXP].
-template <int MAXP, typename Args, typename L>
+// Plans that plan_for can produce: one wavefront with 1..ONE items per lane;
+// 3..15 wavefronts with exactly SPREAD items per lane (2 wavefronts never
+// occur: a row too long for one wavefront needs more than 2 * ONE / SPREAD);
+// 16 wavefronts with SPREAD..MAXP items per lane.
+template <int ONE, int SPREAD, int MAXP, typename Args, typename L>
 ltxnorm_status by_plan(const Plan& p, const Args& a, hipStream_t s, L launcher) {
-    constexpr int MID = MAXP / 2 + 1;
     switch (p.wpr) {
-        case 1: return by_per<1, 1, MAXP>(p, a, s, launcher);
-        case 2: return by_per<2, MID, MAXP>(p, a, s, launcher);
-        case 4: return by_per<4, MID, MAXP>(p, a, s, launcher);
-        case 8: return by_per<8, MID, MAXP>(p, a, s, launcher);
-        case 16: return by_per<16, MID, MAXP>(p, a, s, launcher);
+        case 1: return by_per<1, 1, ONE>(p, a, s, launcher);
+        case 3: return by_per<3, SPREAD, SPREAD>(p, a, s, launcher);
+        case 4: return by_per<4, SPREAD, SPREAD>(p, a, s, launcher);
+        case 5: return by_per<5, SPREAD, SPREAD>(p, a, s, launcher);
+        case 6: return by_per<6, SPREAD, SPREAD>(p, a, s, launcher);
+        case 7: return by_per<7, SPREAD, SPREAD>(p, a, s, launcher);
+        case 8: return by_per<8, SPREAD, SPREAD>(p, a, s, launcher);
+        case 9: return by_per<9, SPREAD, SPREAD>(p, a, s, launcher);
+        case 10: return by_per<10, SPREAD, SPREAD>(p, a, s, launcher);
+        case 11: return by_per<11, SPREAD, SPREAD>(p, a, s, launcher);
+        case 12: return by_per<12, SPREAD, SPREAD>(p, a, s, launcher);
+        case 13: return by_per<13, SPREAD, SPREAD>(p, a, s, launcher);
+        case 14: return by_per<14, SPREAD, SPREAD>(p, a, s, launcher);
+        case 15: return by_per<15, SPREAD, SPREAD>(p, a, s, launcher);
+        case 16: return by_per<16, SPREAD, MAXP>(p, a, s, launcher);
         default: return LTXNORM_ERR_UNSUPPORTED;
     }
 }
@@ -485,10 +603,10 @@ ltxnorm_status ltxnorm_rmsnorm_fwd(void* out, const void* x, const void* weight,
     ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, &empty);
     if (st != LTXNORM_OK || empty) return st;
     const int64_t nvec = hidden / kElemsPerVec;
-    const Plan p = plan_for(nvec, kMaxVecPerLane);
+    const Plan p = plan_for(nvec, 4, 2);
     const RmsArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
                     static_cast<const uint16_t*>(weight), rows, (int32_t)nvec, (float)hidden, eps};
-    return by_plan<kMaxVecPerLane>(p, a, stream, RmsLauncher{});
+    return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RmsLauncher{});
 }
 
 ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void* out, const void* x, const void* weight,
@@ -509,12 +627,18 @@ ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void* out, const void* x, const void* we
     if (overlap(out, nbytes, cos_tab, tbytes) || overlap(out, nbytes, sin_tab, tbytes))
         return LTXNORM_ERR_ALIAS;
     const int64_t nunits = hidden / (2 * kElemsPerVec);
-    const Plan p = plan_for(nunits, kMaxVecPerLane / 2);
+    const bool pow2 = (head_dim & (head_dim - 1)) == 0;
     const RopeArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(weight), cos_tab, sin_tab, rows, seq_len,
                      (int32_t)(hidden / kElemsPerVec), (int32_t)nunits, head_dim / 16,
                      head_dim / 2, (float)hidden, eps};
-    return by_plan<kMaxVecPerLane / 2>(p, a, stream, RopeLauncher{});
+    if (pow2 && head_dim <= 16 * 32) {
+        // partner lanes lie within one wavefront: the coalesced layout
+        const Plan p = plan_for(hidden / kElemsPerVec, 4, 2);
+        return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeXorLauncher{});
+    }
+    const Plan p = plan_for(nunits, 2, 1);
+    return by_plan<2, 1, kMaxVecPerLane / 2>(p, a, stream, RopeLauncher{});
 }
 
 const char* ltxnorm_status_str(ltxnorm_status s) {
