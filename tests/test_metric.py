@@ -1,0 +1,65 @@
+"""Metric arithmetic of the benchmark, pinned to the pages' own numbers, and
+the benchmark's host-side contract (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import datagen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "h100_rmsnorm_microbench.tsv")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_table():
+    rows = {}
+    for line in open(GOLDEN):
+        if line.startswith("#") or line.startswith("shape"):
+            continue
+        shape, custom, torch_ms, speedup = line.split()
+        rows[shape] = (float(custom), float(torch_ms), float(speedup))
+    return rows
+
+
+def test_byte_convention_reproduces_the_pages_38_percent():
+    """read x + write y + read the weight once, at 0.157 ms on a 3.35 TB/s
+    part, gives the 38% the page states under its table."""
+    t = load_table()
+    nbytes = datagen.CONFIGS["rms_4x4096x3072"].algorithmic_bytes()
+    assert nbytes == 201_332_736
+    frac = bench.pct_of_peak(bench.gbps(nbytes, t["4x4096x3072"][0] * 1e-3), 3350.0)
+    assert round(frac) == 38 and abs(frac - 38.3) < 0.05
+    assert abs(bench.H100_GBPS_4x4096x3072 - 1282.4) < 0.1
+
+
+def test_table_speedups_are_time_ratios():
+    """The printed speedups are the ms ratios up to the rounding of the
+    printed ms values (0.065 / 0.019 = 3.42 against the printed 3.37)."""
+    for shape, (custom, torch_ms, speedup) in load_table().items():
+        lo = (torch_ms - 0.0005) / (custom + 0.0005)
+        hi = (torch_ms + 0.0005) / (custom - 0.0005)
+        assert lo - 0.005 <= speedup <= hi + 0.005, shape
+
+
+def test_each_page_shape_has_a_workload():
+    shapes = {f"{c.batch}x{c.seq}x{c.hidden}" for c in datagen.CONFIGS.values() if not c.rope}
+    assert set(load_table()) == shapes
+
+
+def test_traffic_file_is_bound_to_the_kernel_sources(tmp_path, monkeypatch):
+    f = tmp_path / "t.txt"
+    f.write_text(f"kernel=rmsnorm workload=w src_sha={bench.source_hash()} fetch_bytes=10 write_bytes=5\n"
+                 f"kernel=other workload=w src_sha=0000 fetch_bytes=1 write_bytes=1\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.read_traffic("rmsnorm", "w") == 15.0
+    assert bench.read_traffic("other", "w") is None      # stale: sources changed since
+    assert bench.read_traffic("missing", "w") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
