@@ -112,9 +112,13 @@ def test_rmsnorm_edge_shapes(rows, hidden):
     check_rms(x, w, label=f"rms {rows}x{hidden}")
 
 
-@pytest.mark.parametrize("heads,head_dim", [(1, 16), (3, 16), (32, 64), (5, 64), (16, 128),
-                                            (24, 128), (8, 256), (64, 128), (96, 128),
-                                            (512, 128), (1, 1024)])
+# power-of-two head_dim 16..512 takes the coalesced kernel (partner lane
+# xor 1..32); other multiples of 16 and head_dim > 512 take pair-in-lane
+@pytest.mark.parametrize("heads,head_dim", [(1, 16), (3, 16), (2, 32), (32, 64), (5, 64),
+                                            (16, 128), (24, 128), (8, 256), (4, 512),
+                                            (6, 512), (64, 128), (96, 128), (512, 128),
+                                            (128, 512), (1, 1024), (3, 1024), (3, 48),
+                                            (5, 80), (6, 96), (2, 112), (40, 80)])
 @pytest.mark.parametrize("rows,seq_len", [(1, 1), (7, 3), (37, 4096), (1000, 17)])
 def test_rope_edge_shapes(heads, head_dim, rows, seq_len):
     hidden = heads * head_dim
