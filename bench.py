@@ -14,10 +14,11 @@ value = algorithmic bytes per step (read x + write y + read weight once,
 201,332,736 B) / seconds per step, in GB/s (10^9 B/s); it is compared with
 MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
 the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
-cos/sin tables) under "rope", and the CPU oracle timed on this host under
+cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
+(adjacent pairs), and the CPU oracle timed on this host under
 "cpu_baseline".  Prints one JSON line.
 
---probe rms|rope|copy runs a few launches only, for rocprofv3 counter passes.
+--probe rms|rope|ropei|copy runs a few launches only, for rocprofv3 counter passes.
 """
 from __future__ import annotations
 
@@ -112,9 +113,10 @@ class Workload:
         c = self.cfg
         k = i % self.nsets
         if c.rope:
-            self.ltx.ltxnorm_rmsnorm_rope_fwd(self.y[k], self.x[k], self.w, self.cos, self.sin,
-                                              c.rows, c.hidden, c.heads, c.head_dim, c.seq,
-                                              c.eps, self.stream)
+            fn = (self.ltx.ltxnorm_rmsnorm_rope_interleaved_fwd if c.interleaved
+                  else self.ltx.ltxnorm_rmsnorm_rope_fwd)
+            fn(self.y[k], self.x[k], self.w, self.cos, self.sin, c.rows, c.hidden, c.heads,
+               c.head_dim, c.seq, c.eps, self.stream)
         else:
             self.ltx.ltxnorm_rmsnorm_fwd(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
                                          self.stream)
@@ -188,7 +190,8 @@ def probe(kind: str, launches: int):
         print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = datagen.CONFIGS[datagen.HEADLINE if kind == "rms" else datagen.ROPE]
+    cfg = datagen.CONFIGS[{"rms": datagen.HEADLINE, "rope": datagen.ROPE,
+                           "ropei": datagen.ROPE_INTERLEAVED}[kind]]
     wl = Workload(cfg, dev, s, max_sets=2)
     for i in range(launches):
         wl.step(i)
@@ -204,7 +207,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-rope", action="store_true", help="skip the RMSNorm+RoPE line item")
-    ap.add_argument("--probe", choices=["rms", "rope", "copy"])
+    ap.add_argument("--probe", choices=["rms", "rope", "ropei", "copy"])
     ap.add_argument("--launches", type=int, default=10)
     args = ap.parse_args()
 
@@ -266,18 +269,21 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_rope:
-        rc = datagen.CONFIGS[datagen.ROPE]
-        rw = Workload(rc, dev, stream)
-        rsec = rw.time_steps(args.steps, args.warmup)
-        rv = gbps(rc.algorithmic_bytes(), rsec)
-        rtraffic = read_traffic("rmsnorm_rope", rc.name)
-        line["rope"] = {"workload": rc.name, "value": round(rv, 2), "unit": "GB/s",
-                        "ms_per_step": round(rsec * 1e3, 6),
-                        "bytes_per_step": rc.algorithmic_bytes(), "rotating_sets": rw.nsets,
-                        "frac": round(rv / HBM_PEAK_GBPS, 4),
-                        "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
-        del rw
-        torch.cuda.empty_cache()
+        for key, name, kernel in (("rope", datagen.ROPE, "rmsnorm_rope"),
+                                  ("rope_interleaved", datagen.ROPE_INTERLEAVED,
+                                   "rmsnorm_rope_interleaved")):
+            rc = datagen.CONFIGS[name]
+            rw = Workload(rc, dev, stream)
+            rsec = rw.time_steps(args.steps, args.warmup)
+            rv = gbps(rc.algorithmic_bytes(), rsec)
+            rtraffic = read_traffic(kernel, rc.name)
+            line[key] = {"workload": rc.name, "value": round(rv, 2), "unit": "GB/s",
+                         "ms_per_step": round(rsec * 1e3, 6),
+                         "bytes_per_step": rc.algorithmic_bytes(), "rotating_sets": rw.nsets,
+                         "frac": round(rv / HBM_PEAK_GBPS, 4),
+                         "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+            del rw
+            torch.cuda.empty_cache()
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, host)

@@ -156,6 +156,7 @@ class Config:
     heads: int = 0
     head_dim: int = 0
     theta: float = 10000.0
+    interleaved: bool = False  # RoPE pairing: rotate-half (False) or adjacent pairs
 
     @property
     def rows(self) -> int:
@@ -186,9 +187,12 @@ CONFIGS = {
     "rms_4x4096x3072": Config("rms_4x4096x3072", 5, 4, 4096, 3072),
     "rope_2x4096x2048_h32d64": Config("rope_2x4096x2048_h32d64", 6, 2, 4096, 2048,
                                       heads=32, head_dim=64, theta=10000.0),
+    "ropei_2x4096x2048_h32d64": Config("ropei_2x4096x2048_h32d64", 7, 2, 4096, 2048,
+                                       heads=32, head_dim=64, theta=10000.0, interleaved=True),
 }
 HEADLINE = "rms_4x4096x3072"
 ROPE = "rope_2x4096x2048_h32d64"
+ROPE_INTERLEAVED = "ropei_2x4096x2048_h32d64"
 
 
 def make_x(rows: int, hidden: int, seed: int = BASE_SEED, stream: int = STREAM_X,
@@ -217,5 +221,6 @@ def make_inputs(cfg: Config, seed: int = BASE_SEED, rows: int | None = None) -> 
     out = {"x": x, "w": w, "eps": cfg.eps}
     if cfg.rope:
         cos_t, sin_t = rope_tables(cfg.seq, cfg.head_dim, cfg.theta)
-        out.update(cos=cos_t, sin=sin_t, heads=cfg.heads, head_dim=cfg.head_dim)
+        out.update(cos=cos_t, sin=sin_t, heads=cfg.heads, head_dim=cfg.head_dim,
+                   interleaved=cfg.interleaved)
     return out

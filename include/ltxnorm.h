@@ -108,6 +108,29 @@ ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *we
                                         int32_t head_dim, int64_t seq_len, float eps,
                                         hipStream_t stream);
 
+/*
+ * Fused RMSNorm over the full row, then RoPE per head on adjacent pairs.
+ *
+ * The LTX-2 ltx-kernels README (introduction) lists a sibling op,
+ * rms_norm_split_rope, next to rms_norm_rope, without defining either; the
+ * two standard pairings are rotate-half (ltxnorm_rmsnorm_rope_fwd) and the
+ * interleaved one computed here:
+ *     out[2i]     = y[2i] * c - y[2i + 1] * s
+ *     out[2i + 1] = y[2i + 1] * c + y[2i] * s
+ * with c = cos_tab[p, i], s = sin_tab[p, i] for i < head_dim/2 within each
+ * head, p = row mod seq_len, on the un-rounded binary32 y.
+ *
+ * Arguments, layouts, ownership and errors as for ltxnorm_rmsnorm_rope_fwd,
+ * except that head_dim need only be a multiple of 8.
+ */
+ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void *out, const void *x,
+                                                    const void *weight,
+                                                    const float *cos_tab,
+                                                    const float *sin_tab, int64_t rows,
+                                                    int64_t hidden, int32_t heads,
+                                                    int32_t head_dim, int64_t seq_len,
+                                                    float eps, hipStream_t stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char *ltxnorm_status_str(ltxnorm_status s);
 

@@ -58,6 +58,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_rmsnorm_rope.argtypes = [p, p, p, p, p, p, i64, i64, i32, i32,
                                         i64, ctypes.c_float]
     lib.oracle_rmsnorm_rope.restype = ctypes.c_int
+    lib.oracle_rmsnorm_rope_interleaved.argtypes = list(lib.oracle_rmsnorm_rope.argtypes)
+    lib.oracle_rmsnorm_rope_interleaved.restype = ctypes.c_int
     lib.oracle_round.argtypes = [p, i64, p, p]
     lib.oracle_round.restype = None
     lib.oracle_bf16_from_f32.argtypes = [ctypes.c_float]
@@ -115,8 +117,9 @@ class Oracle:
         return y
 
     def rmsnorm_rope(self, x, w, cos_tab, sin_tab, heads: int, head_dim: int,
-                     eps: float = 1e-6, with_mag: bool = False):
-        """RMSNorm over the whole row then rotate-half RoPE per head.
+                     eps: float = 1e-6, with_mag: bool = False, interleaved: bool = False):
+        """RMSNorm over the whole row then RoPE per head: rotate-half pairs
+        (i, i + d/2), or with ``interleaved`` adjacent pairs (2i, 2i + 1).
 
         ``x`` bf16 ``[rows, heads*head_dim]`` (any leading shape); tables
         binary32 ``[seq_len, head_dim/2]``; row r uses table row r mod seq_len.
@@ -135,9 +138,9 @@ class Oracle:
         seq_len = cos_tab.shape[0]
         y = np.empty(x.shape, dtype=np.float64)
         mag = np.empty(x.shape, dtype=np.float64) if with_mag else None
-        rc = self.lib.oracle_rmsnorm_rope(
-            _ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(cos_tab), _ptr(sin_tab),
-            rows, hidden, heads, head_dim, seq_len, ctypes.c_float(eps))
+        fn = self.lib.oracle_rmsnorm_rope_interleaved if interleaved else self.lib.oracle_rmsnorm_rope
+        rc = fn(_ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(cos_tab), _ptr(sin_tab),
+                rows, hidden, heads, head_dim, seq_len, ctypes.c_float(eps))
         if rc != 0:
             raise ValueError("oracle_rmsnorm_rope rejected its arguments")
         return (y, mag) if with_mag else y

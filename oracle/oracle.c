@@ -32,6 +32,12 @@
  *    rotate_half([y1, y2]) = [-y2, y1].  Row r sits at position p = r mod
  *    seq_len; the cos/sin tables are inputs, binary32 [seq_len, d/2].
  *    The rotation acts on the un-rounded normalised value (one rounding).
+ *  - RMSNorm + interleaved RoPE.  The README's sibling op name
+ *    (rms_norm_split_rope) implies a second pairing; the pages define
+ *    neither.  The other standard pairing rotates adjacent elements:
+ *        out[2i]     = y[2i] * cos[p, i] - y[2i + 1] * sin[p, i]
+ *        out[2i + 1] = y[2i + 1] * cos[p, i] + y[2i] * sin[p, i]
+ *    with the same [seq_len, head_dim/2] tables and row positions.
  *
  * Data format
  * -----------
@@ -171,6 +177,48 @@ int oracle_rmsnorm_rope(double *y, double *mag, const uint16_t *x,
                     double *m = mag + r * hidden + (int64_t)h * head_dim;
                     m[i] = fabs(a * c) + fabs(b * s);
                     m[i + half] = fabs(b * c) + fabs(a * s);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Fused RMSNorm over the whole hidden row, then RoPE per head on adjacent
+ * pairs (2i, 2i + 1), both rotated by table column i.  Arguments and return
+ * value as for oracle_rmsnorm_rope; mag as there (|a c| + |b s| for the
+ * even element, |b c| + |a s| for the odd one). */
+int oracle_rmsnorm_rope_interleaved(double *y, double *mag, const uint16_t *x,
+                                    const uint16_t *w, const float *cos_tab,
+                                    const float *sin_tab, int64_t rows,
+                                    int64_t hidden, int32_t heads,
+                                    int32_t head_dim, int64_t seq_len,
+                                    float eps)
+{
+    if (!y || !x || !cos_tab || !sin_tab || rows < 0 || hidden <= 0 ||
+        heads <= 0 || head_dim <= 0 || head_dim % 2 != 0 ||
+        (int64_t)heads * head_dim != hidden || seq_len <= 0)
+        return -1;
+    const int32_t half = head_dim / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        double *yr = y + r * hidden;
+        normalise_row(yr, x + r * hidden, w, hidden, eps);
+        const int64_t p = r % seq_len;
+        const float *cp = cos_tab + p * half;
+        const float *sp = sin_tab + p * half;
+        for (int32_t h = 0; h < heads; ++h) {
+            double *head = yr + (int64_t)h * head_dim;
+            for (int32_t i = 0; i < half; ++i) {
+                double a = head[2 * i];     /* even element */
+                double b = head[2 * i + 1]; /* odd element  */
+                double c = (double)cp[i];
+                double s = (double)sp[i];
+                head[2 * i] = a * c - b * s;
+                head[2 * i + 1] = b * c + a * s;
+                if (mag) {
+                    double *m = mag + r * hidden + (int64_t)h * head_dim;
+                    m[2 * i] = fabs(a * c) + fabs(b * s);
+                    m[2 * i + 1] = fabs(b * c) + fabs(a * s);
                 }
             }
         }

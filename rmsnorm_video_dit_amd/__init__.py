@@ -11,6 +11,7 @@ The low-level functions keep the C names and argument order:
     ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, stream)
     ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden,
                              heads, head_dim, seq_len, eps, stream)
+    ltxnorm_rmsnorm_rope_interleaved_fwd(... same arguments ...)
     ltxnorm_status_str(status), ltxnorm_version()
 
 Pointer arguments accept a torch tensor, an integer address or None; ``stream``
@@ -53,6 +54,9 @@ def lib() -> ctypes.CDLL:
         L.ltxnorm_rmsnorm_fwd.restype = ctypes.c_int
         L.ltxnorm_rmsnorm_rope_fwd.argtypes = [p, p, p, p, p, i64, i64, i32, i32, i64, f32, p]
         L.ltxnorm_rmsnorm_rope_fwd.restype = ctypes.c_int
+        L.ltxnorm_rmsnorm_rope_interleaved_fwd.argtypes = [p, p, p, p, p, i64, i64, i32, i32, i64,
+                                                           f32, p]
+        L.ltxnorm_rmsnorm_rope_interleaved_fwd.restype = ctypes.c_int
         L.ltxnorm_status_str.argtypes = [ctypes.c_int]
         L.ltxnorm_status_str.restype = ctypes.c_char_p
         L.ltxnorm_version.argtypes = []
@@ -99,6 +103,13 @@ def ltxnorm_rmsnorm_rope_fwd_status(out, x, weight, cos_tab, sin_tab, rows, hidd
                                           int(head_dim), int(seq_len), float(eps), _stream(stream))
 
 
+def ltxnorm_rmsnorm_rope_interleaved_fwd_status(out, x, weight, cos_tab, sin_tab, rows, hidden,
+                                                heads, head_dim, seq_len, eps, stream) -> int:
+    return lib().ltxnorm_rmsnorm_rope_interleaved_fwd(
+        _addr(out), _addr(x), _addr(weight), _addr(cos_tab), _addr(sin_tab), int(rows),
+        int(hidden), int(heads), int(head_dim), int(seq_len), float(eps), _stream(stream))
+
+
 def ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, stream=None) -> None:
     st = ltxnorm_rmsnorm_fwd_status(out, x, weight, rows, hidden, eps, stream)
     if st != OK:
@@ -111,6 +122,14 @@ def ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden, hea
                                          head_dim, seq_len, eps, stream)
     if st != OK:
         raise LtxnormError(st, "ltxnorm_rmsnorm_rope_fwd")
+
+
+def ltxnorm_rmsnorm_rope_interleaved_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                         head_dim, seq_len, eps, stream=None) -> None:
+    st = ltxnorm_rmsnorm_rope_interleaved_fwd_status(out, x, weight, cos_tab, sin_tab, rows,
+                                                     hidden, heads, head_dim, seq_len, eps, stream)
+    if st != OK:
+        raise LtxnormError(st, "ltxnorm_rmsnorm_rope_interleaved_fwd")
 
 
 def _check_act(x, name):
@@ -142,9 +161,10 @@ def rmsnorm(x, weight=None, eps: float = 1e-6, out=None):
 
 
 def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: float = 1e-6,
-                 out=None):
-    """RMSNorm over the full last dimension (heads*head_dim), then rotate-half
-    RoPE per head; row r uses table row r mod cos_tab.shape[0]."""
+                 out=None, interleaved: bool = False):
+    """RMSNorm over the full last dimension (heads*head_dim), then RoPE per
+    head: rotate-half pairs (i, i + d/2), or adjacent pairs (2i, 2i + 1) with
+    ``interleaved``; row r uses table row r mod cos_tab.shape[0]."""
     import torch
     _check_act(x, "x")
     if weight is not None:
@@ -162,6 +182,6 @@ def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: fl
         if out.shape != x.shape:
             raise ValueError("out must have the shape of x")
     rows = x.numel() // hidden if hidden else 0
-    ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim,
-                             cos_tab.shape[0], eps, None)
+    fn = ltxnorm_rmsnorm_rope_interleaved_fwd if interleaved else ltxnorm_rmsnorm_rope_fwd
+    fn(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim, cos_tab.shape[0], eps, None)
     return out

@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_kernel(const RmsArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar row math
     const int slot = wave / WPR;
     const int wave_in_row = wave % WPR;
     const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_kernel(const RopeArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar row math
     const int slot = wave / WPR;
     const int wave_in_row = wave % WPR;
     const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_xor_kernel(const RopeArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar row math
     const int slot = wave / WPR;
     const int wave_in_row = wave % WPR;
     const int lane = threadIdx.x & (kWave - 1);
@@ -452,6 +452,95 @@ rmsnorm_rope_xor_kernel(const RopeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm + interleaved RoPE: adjacent pairs (2i, 2i + 1) of each head turn
+// by table column i.  A pair is one 32-bit word of a bf16x8 vector, so the
+// RMSNorm lane layout needs no exchange at all; vector v of a row covers
+// pairs 4 * (v mod (head_dim / 8)) .. + 4 of its head, i.e. one float4 of cos
+// and one of sin.  head_dim must be a multiple of 8 (vectors never straddle
+// heads).
+// ---------------------------------------------------------------------------
+template <int VPL, int WPR, bool FULL, bool SHARED>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_interleaved_kernel(const RopeArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int L = Layout<WPR>::kLanesPerRow;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar row math
+    const int slot = wave / WPR;
+    const int wave_in_row = wave % WPR;
+    const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
+    const int vph = a.half / 4;  // vectors per head = head_dim / 8
+
+    u32x4 wv[VPL];
+    int toff[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = k * L + t;
+        const bool in = FULL || v < a.nvec;
+        const u32x4 ones = {kOnesPair, kOnesPair, kOnesPair, kOnesPair};
+        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v] : ones;
+        toff[k] = (v % vph) * 4;
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;
+        const int64_t pos = active ? row % a.seq_len : 0;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+
+        u32x4 xv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[8];
+            widen8(xv[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+        }
+        const float rstd = rstd_of(row_sum<WPR>(part, slot, wave_in_row, parity), a.hidden_f, a.eps);
+
+        // SHARED: head_dim / 8 divides the lanes per row (every power-of-two
+        // head_dim up to 512), so all slots of a lane share one table offset
+        // and the row needs a single float4 of cos and of sin per lane.
+        const float* crow = a.cos_tab + pos * a.half;
+        const float* srow = a.sin_tab + pos * a.half;
+        f32x4 c = *reinterpret_cast<const f32x4*>(crow + toff[0]);
+        f32x4 sn = *reinterpret_cast<const f32x4*>(srow + toff[0]);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            if (!SHARED && k > 0) {
+                c = *reinterpret_cast<const f32x4*>(crow + toff[k]);
+                sn = *reinterpret_cast<const f32x4*>(srow + toff[k]);
+            }
+            keep_packed(xv[k]);
+            keep_packed(wv[k]);
+            float y[8], g[8], o[8];
+            widen8(xv[k], y);
+            widen8(wv[k], g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (y[e] * rstd) * g[e];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                o[2 * j] = y[2 * j] * c[j] - y[2 * j + 1] * sn[j];
+                o[2 * j + 1] = y[2 * j + 1] * c[j] + y[2 * j] * sn[j];
+            }
+            if (in) store_stream(yr + v, narrow8(o));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation, per-hidden dispatch, launch.
 // ---------------------------------------------------------------------------
 
@@ -518,6 +607,14 @@ struct RmsLauncher {
 struct RopeLauncher {
     template <int WPR, int PER, bool FULL>
     ltxnorm_status go(const RopeArgs& a, hipStream_t s) const { return launch_rope<WPR, PER, FULL>(a, s); }
+};
+template <bool SHARED>
+struct RopeInterleavedLauncher {
+    template <int WPR, int PER, bool FULL>
+    ltxnorm_status go(const RopeArgs& a, hipStream_t s) const {
+        return launch((const void*)&rmsnorm_rope_interleaved_kernel<PER, WPR, FULL, SHARED>,
+                      Layout<WPR>::kThreads, Layout<WPR>::kRowsPerBlock, a.rows, a, s);
+    }
 };
 struct RopeXorLauncher {
     template <int WPR, int PER, bool FULL>
@@ -593,6 +690,30 @@ ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_
     return LTXNORM_OK;
 }
 
+// Validation shared by the RoPE entry points; fills `a` when there is work.
+ltxnorm_status check_rope(void* out, const void* x, const void* weight, const float* cos_tab,
+                          const float* sin_tab, int64_t rows, int64_t hidden, int32_t heads,
+                          int32_t head_dim, int64_t seq_len, float eps, int head_dim_multiple,
+                          bool* empty, RopeArgs* a) {
+    if (heads < 1 || head_dim < head_dim_multiple || head_dim % head_dim_multiple != 0 ||
+        seq_len < 1 || (int64_t)heads * head_dim != hidden)
+        return LTXNORM_ERR_SHAPE;
+    if (seq_len > INT64_MAX / (head_dim * 4)) return LTXNORM_ERR_SHAPE;
+    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, empty);
+    if (st != LTXNORM_OK || *empty) return st;
+    if (cos_tab == nullptr || sin_tab == nullptr) return LTXNORM_ERR_NULL;
+    if (misaligned(cos_tab) || misaligned(sin_tab)) return LTXNORM_ERR_ALIGN;
+    const int64_t nbytes = rows * hidden * 2;
+    const int64_t tbytes = seq_len * (head_dim / 2) * 4;
+    if (overlap(out, nbytes, cos_tab, tbytes) || overlap(out, nbytes, sin_tab, tbytes))
+        return LTXNORM_ERR_ALIAS;
+    *a = RopeArgs{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
+                  static_cast<const uint16_t*>(weight), cos_tab, sin_tab, rows, seq_len,
+                  (int32_t)(hidden / kElemsPerVec), (int32_t)(hidden / (2 * kElemsPerVec)),
+                  head_dim / 16, head_dim / 2, (float)hidden, eps};
+    return LTXNORM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -609,36 +730,40 @@ ltxnorm_status ltxnorm_rmsnorm_fwd(void* out, const void* x, const void* weight,
     return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RmsLauncher{});
 }
 
+
 ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void* out, const void* x, const void* weight,
                                         const float* cos_tab, const float* sin_tab, int64_t rows,
                                         int64_t hidden, int32_t heads, int32_t head_dim,
                                         int64_t seq_len, float eps, hipStream_t stream) {
-    if (heads < 1 || head_dim < 16 || head_dim % 16 != 0 || seq_len < 1 ||
-        (int64_t)heads * head_dim != hidden)
-        return LTXNORM_ERR_SHAPE;
-    if (seq_len > INT64_MAX / (head_dim * 4)) return LTXNORM_ERR_SHAPE;
     bool empty = false;
-    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, &empty);
+    RopeArgs a;
+    ltxnorm_status st = check_rope(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                   head_dim, seq_len, eps, 16, &empty, &a);
     if (st != LTXNORM_OK || empty) return st;
-    if (cos_tab == nullptr || sin_tab == nullptr) return LTXNORM_ERR_NULL;
-    if (misaligned(cos_tab) || misaligned(sin_tab)) return LTXNORM_ERR_ALIGN;
-    const int64_t nbytes = rows * hidden * 2;
-    const int64_t tbytes = seq_len * (head_dim / 2) * 4;
-    if (overlap(out, nbytes, cos_tab, tbytes) || overlap(out, nbytes, sin_tab, tbytes))
-        return LTXNORM_ERR_ALIAS;
-    const int64_t nunits = hidden / (2 * kElemsPerVec);
-    const bool pow2 = (head_dim & (head_dim - 1)) == 0;
-    const RopeArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(weight), cos_tab, sin_tab, rows, seq_len,
-                     (int32_t)(hidden / kElemsPerVec), (int32_t)nunits, head_dim / 16,
-                     head_dim / 2, (float)hidden, eps};
-    if (pow2 && head_dim <= 16 * 32) {
+    if ((head_dim & (head_dim - 1)) == 0 && head_dim <= 16 * 32) {
         // partner lanes lie within one wavefront: the coalesced layout
-        const Plan p = plan_for(hidden / kElemsPerVec, 4, 2);
+        const Plan p = plan_for(a.nvec, 4, 2);
         return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeXorLauncher{});
     }
-    const Plan p = plan_for(nunits, 2, 1);
+    const Plan p = plan_for(a.nunits, 2, 1);
     return by_plan<2, 1, kMaxVecPerLane / 2>(p, a, stream, RopeLauncher{});
+}
+
+ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void* out, const void* x, const void* weight,
+                                                    const float* cos_tab, const float* sin_tab,
+                                                    int64_t rows, int64_t hidden, int32_t heads,
+                                                    int32_t head_dim, int64_t seq_len, float eps,
+                                                    hipStream_t stream) {
+    bool empty = false;
+    RopeArgs a;
+    ltxnorm_status st = check_rope(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                   head_dim, seq_len, eps, 8, &empty, &a);
+    if (st != LTXNORM_OK || empty) return st;
+    const Plan p = plan_for(a.nvec, 4, 2);
+    const int vph = head_dim / kElemsPerVec;
+    if ((kWave * p.wpr) % vph == 0)
+        return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeInterleavedLauncher<true>{});
+    return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeInterleavedLauncher<false>{});
 }
 
 const char* ltxnorm_status_str(ltxnorm_status s) {

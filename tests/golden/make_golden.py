@@ -32,12 +32,15 @@ def cases():
     yield "rope_5x32_h2d16_seq3", dict(x=datagen.make_x(5, 32, seed=79, stream=1),
                                        w=datagen.make_w(32, seed=79, stream=2), eps=1e-6,
                                        cos=c, sin=s, heads=2, head_dim=16)
+    yield "ropei_5x32_h2d16_seq3", dict(x=datagen.make_x(5, 32, seed=80, stream=1),
+                                        w=datagen.make_w(32, seed=80, stream=2), eps=1e-6,
+                                        cos=c, sin=s, heads=2, head_dim=16, interleaved=True)
 
 
 def compute(o, inp):
     if "cos" in inp:
         y = o.rmsnorm_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], inp["heads"],
-                           inp["head_dim"], inp["eps"])
+                           inp["head_dim"], inp["eps"], interleaved=inp.get("interleaved", False))
     else:
         y = o.rmsnorm(inp["x"], inp["w"], inp["eps"])
     ref32, ref16 = o.round(y)

@@ -309,6 +309,82 @@ def pin_rope_mag(o):
 
 
 # --------------------------------------------------------------------------
+# RMSNorm + interleaved RoPE pins (adjacent pairs 2i, 2i + 1)
+# --------------------------------------------------------------------------
+
+def pin_rope_il_position_zero_is_rmsnorm(o):
+    rng = np.random.default_rng(53)
+    heads, d = 3, 16
+    x = _rand_bf16(rng, (4, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables([0], d)
+    y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6, interleaved=True)
+    assert np.array_equal(y, o.rmsnorm(x, w, 1e-6))
+
+
+def pin_rope_il_complex_rotation(o):
+    """Adjacent pair (2i, 2i + 1) = complex a + ib turned by c_i + i s_i."""
+    rng = np.random.default_rng(59)
+    heads, d, seq = 2, 8, 4
+    x = _rand_bf16(rng, (seq, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables(np.arange(seq) * 3 + 1, d)
+    y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6, interleaved=True)
+    z = o.rmsnorm(x, w, 1e-6)
+    for r in range(seq):
+        for h in range(heads):
+            for i in range(d // 2):
+                a, b = z[r, h * d + 2 * i], z[r, h * d + 2 * i + 1]
+                rot = complex(a, b) * complex(float(c[r, i]), float(s[r, i]))
+                got = complex(y[r, h * d + 2 * i], y[r, h * d + 2 * i + 1])
+                assert cmath.isclose(got, rot, rel_tol=1e-14, abs_tol=1e-300), (r, h, i)
+
+
+def pin_rope_il_matches_rotate_half_after_reorder(o):
+    """Reordering each head as [evens, odds] turns adjacent pairs into
+    rotate-half pairs: interleaved(x, w) equals rotate-half of the reordered
+    x and w, read back in the original order."""
+    rng = np.random.default_rng(61)
+    heads, d = 4, 32
+    x = _rand_bf16(rng, (5, heads * d))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    c, s = _tables([0, 7, 100, 2047, 4095], d)
+    within = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    perm = np.concatenate([h * d + within for h in range(heads)])
+    il = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6, interleaved=True)
+    rh = o.rmsnorm_rope(x[:, perm], w[perm], c, s, heads, d, 1e-6)
+    back = np.empty_like(rh)
+    back[:, perm] = rh
+    assert np.allclose(il, back, rtol=1e-14, atol=1e-300)
+
+
+def pin_rope_il_constant_row(o):
+    heads, d = 2, 16
+    x = _bf16(np.full((2, heads * d), 1.5))
+    c, s = _tables([3, 11], d)
+    y = o.rmsnorm_rope(x, None, c, s, heads, d, 0.0, interleaved=True)
+    cc, ss = c.astype(np.float64), s.astype(np.float64)
+    for h in range(heads):
+        assert np.allclose(y[:, h * d:(h + 1) * d:2], cc - ss, rtol=1e-15, atol=1e-15)
+        assert np.allclose(y[:, h * d + 1:(h + 1) * d:2], cc + ss, rtol=1e-15, atol=1e-15)
+
+
+def pin_rope_il_mag(o):
+    rng = np.random.default_rng(67)
+    heads, d = 2, 8
+    x = _rand_bf16(rng, (3, heads * d))
+    c, s = _tables([1, 5, 9], d)
+    y, mag = o.rmsnorm_rope(x, None, c, s, heads, d, 1e-6, with_mag=True, interleaved=True)
+    z = o.rmsnorm(x, None, 1e-6)
+    cc, ss = np.repeat(c.astype(np.float64), 2, axis=1), np.repeat(s.astype(np.float64), 2, axis=1)
+    for h in range(heads):
+        zh = z[:, h * d:(h + 1) * d]
+        partner = zh.reshape(3, d // 2, 2)[:, :, ::-1].reshape(3, d)
+        assert np.allclose(mag[:, h * d:(h + 1) * d], np.abs(zh * cc) + np.abs(partner * ss), rtol=1e-15)
+    assert np.all(np.abs(y) <= mag * (1 + 1e-15))
+
+
+# --------------------------------------------------------------------------
 # Rounding pins
 # --------------------------------------------------------------------------
 
@@ -379,5 +455,7 @@ PINS = [
     pin_none_weight_is_ones, pin_rows_independent, pin_permutation, pin_brute_force_exact,
     pin_rope_position_zero_is_rmsnorm, pin_rope_complex_rotation, pin_rope_pair_norm,
     pin_rope_constant_row, pin_rope_row_position, pin_rope_mag,
+    pin_rope_il_position_zero_is_rmsnorm, pin_rope_il_complex_rotation,
+    pin_rope_il_matches_rotate_half_after_reorder, pin_rope_il_constant_row, pin_rope_il_mag,
     pin_bf16_rounding, pin_round_twice,
 ]

@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "ltxnorm.h")
 
 A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
 MB = 1 << 20
+OK_IF_VALID = "shape accepted"  # sentinel: the shape passes, alignment is what fails
 
 
 def declared_functions():
@@ -28,6 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
+                                    "ltxnorm_rmsnorm_rope_interleaved_fwd",
                                     "ltxnorm_status_str", "ltxnorm_version"]
 
 
@@ -114,6 +116,30 @@ def test_rmsnorm_empty_is_ok_without_pointers():
 ])
 def test_rope_validation(kw, status):
     assert rope(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=2048, heads=16, head_dim=64), ltx.ERR_SHAPE),   # hidden != heads * head_dim
+    (dict(hidden=96, heads=8, head_dim=12), ltx.ERR_SHAPE),      # head_dim % 8 != 0
+    (dict(hidden=192, heads=8, head_dim=24), OK_IF_VALID),   # head_dim 24 is accepted
+    (dict(seq_len=0), ltx.ERR_SHAPE),
+    (dict(c=None), ltx.ERR_NULL),
+    (dict(s=A + 129 * MB + 8), ltx.ERR_ALIGN),
+    (dict(c=A + 512), ltx.ERR_ALIAS),
+])
+def test_rope_interleaved_validation(kw, status):
+    args = dict(out=A, x=A + 64 * MB, w=None, c=A + 128 * MB, s=A + 129 * MB, rows=4,
+                hidden=2048, heads=32, head_dim=64, seq_len=16, eps=1e-6)
+    args.update(kw)
+    if status == OK_IF_VALID:
+        # a valid call would launch: check instead that the shape passes by
+        # making only the alignment wrong
+        args["out"] = A + 2
+        status = ltx.ERR_ALIGN
+    st = ltx.ltxnorm_rmsnorm_rope_interleaved_fwd_status(
+        args["out"], args["x"], args["w"], args["c"], args["s"], args["rows"], args["hidden"],
+        args["heads"], args["head_dim"], args["seq_len"], args["eps"], 0)
+    assert st == status
 
 
 def test_python_front_end_refuses_host_tensors():

@@ -44,10 +44,11 @@ def run_rms(x, w, eps=1e-6):
     return host_bits(ltx.rmsnorm(xt, wt, eps))
 
 
-def run_rope(x, w, c, s, heads, head_dim, eps=1e-6):
+def run_rope(x, w, c, s, heads, head_dim, eps=1e-6, interleaved=False):
     xt = dev_bf16(x)
     wt = None if w is None else dev_bf16(w)
-    return host_bits(ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), heads, head_dim, eps))
+    return host_bits(ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), heads, head_dim, eps,
+                                      interleaved=interleaved))
 
 
 def check_rms(x, w, eps=1e-6, label=""):
@@ -59,9 +60,10 @@ def check_rms(x, w, eps=1e-6, label=""):
     return got, rep
 
 
-def check_rope(x, w, c, s, heads, head_dim, eps=1e-6, label=""):
-    got = run_rope(x, w, c, s, heads, head_dim, eps)
-    y, mag = ORC.rmsnorm_rope(x, w, c, s, heads, head_dim, eps, with_mag=True)
+def check_rope(x, w, c, s, heads, head_dim, eps=1e-6, label="", interleaved=False):
+    got = run_rope(x, w, c, s, heads, head_dim, eps, interleaved)
+    y, mag = ORC.rmsnorm_rope(x, w, c, s, heads, head_dim, eps, with_mag=True,
+                              interleaved=interleaved)
     ref32, ref16 = ORC.round(y)
     rep = compare_bf16(got, ref16, mag, ref32)
     print(label, rep, flush=True)
@@ -80,7 +82,7 @@ def test_workload_full_size(name):
     inp = datagen.make_inputs(cfg)
     if cfg.rope:
         got, rep = check_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg.heads, cfg.head_dim,
-                              cfg.eps, label=name)
+                              cfg.eps, label=name, interleaved=cfg.interleaved)
     else:
         got, rep = check_rms(inp["x"], inp["w"], cfg.eps, label=name)
     if cfg.rope:
@@ -129,6 +131,44 @@ def test_rope_edge_shapes(heads, head_dim, rows, seq_len):
     w = datagen.make_w(hidden, seed=hidden + rows, stream=2)
     c, s = datagen.rope_tables(seq_len, head_dim, 10000.0)
     check_rope(x, w, c, s, heads, head_dim, label=f"rope {rows}x{heads}x{head_dim} S={seq_len}")
+
+
+@pytest.mark.parametrize("heads,head_dim", [(1, 8), (3, 16), (5, 24), (32, 64), (16, 128),
+                                            (24, 128), (40, 80), (128, 512), (1, 1024),
+                                            (512, 128)])
+@pytest.mark.parametrize("rows,seq_len", [(1, 1), (7, 3), (37, 4096), (1000, 17)])
+def test_rope_interleaved_edge_shapes(heads, head_dim, rows, seq_len):
+    hidden = heads * head_dim
+    if hidden % 8:
+        pytest.skip("hidden must be a multiple of 8")
+    if rows * hidden > (1 << 24):
+        rows = max(1, (1 << 24) // hidden)
+    announce(f"rope interleaved rows={rows} heads={heads} head_dim={head_dim} seq_len={seq_len}")
+    x = datagen.make_x(rows, hidden, seed=hidden + rows + 5, stream=1)
+    w = datagen.make_w(hidden, seed=hidden + rows + 5, stream=2)
+    c, s = datagen.rope_tables(seq_len, head_dim, 10000.0)
+    check_rope(x, w, c, s, heads, head_dim, interleaved=True,
+               label=f"rope-il {rows}x{heads}x{head_dim} S={seq_len}")
+
+
+def test_rope_interleaved_invariants():
+    """Position 0 is plain RMSNorm; in place equals out of place; a NULL
+    weight equals ones; run to run identical."""
+    announce("rope interleaved invariants")
+    x = datagen.make_x(300, 3072, seed=15, stream=1)
+    w = datagen.make_w(3072, seed=15, stream=2)
+    c0, s0 = datagen.rope_tables(1, 128)
+    assert np.array_equal(run_rope(x, w, c0, s0, 24, 128, interleaved=True), run_rms(x, w))
+    c, s = datagen.rope_tables(77, 128)
+    ref = run_rope(x, w, c, s, 24, 128, interleaved=True)
+    assert np.array_equal(ref, run_rope(x, w, c, s, 24, 128, interleaved=True))
+    xt = dev_bf16(x)
+    ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), 24, 128, 1e-6, out=xt,
+                     interleaved=True)
+    assert np.array_equal(host_bits(xt), ref)
+    ones = np.full(3072, 0x3F80, dtype=np.uint16)
+    assert np.array_equal(run_rope(x, None, c, s, 24, 128, interleaved=True),
+                          run_rope(x, ones, c, s, 24, 128, interleaved=True))
 
 
 def test_rope_outlier_values_and_null_weight():

@@ -37,6 +37,13 @@ MUTANTS = {
     "rope_rounded_input": ("double a = head[i];        /* first half  */",
                            "double a = (double)(float)head[i]; /* first half  */"),
     "mag_signed": ("m[i] = fabs(a * c) + fabs(b * s);", "m[i] = fabs(a * c - b * s);"),
+    "rope_il_sign_first": ("head[2 * i] = a * c - b * s;", "head[2 * i] = a * c + b * s;"),
+    "rope_il_sign_second": ("head[2 * i + 1] = b * c + a * s;", "head[2 * i + 1] = b * c - a * s;"),
+    "rope_il_table_reversed": ("double c = (double)cp[i];\n                double s = (double)sp[i];\n                head[2 * i]",
+                               "double c = (double)cp[half - 1 - i];\n                double s = (double)sp[half - 1 - i];\n                head[2 * i]"),
+    "rope_il_pairs_swapped": ("double a = head[2 * i];     /* even element */\n                double b = head[2 * i + 1]; /* odd element  */",
+                              "double b = head[2 * i];     /* even element */\n                double a = head[2 * i + 1]; /* odd element  */"),
+    "rope_il_mag_signed": ("m[2 * i] = fabs(a * c) + fabs(b * s);", "m[2 * i] = fabs(a * c - b * s);"),
     "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
     "bf16_truncate": ("kept += 1u;", "kept += 0u;"),
     "bf16_ties_odd": ("(kept & 1u))", "!(kept & 1u))"),
