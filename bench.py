@@ -15,10 +15,11 @@ value = algorithmic bytes per step (read x + write y + read weight once,
 MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
 the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
-(adjacent pairs), and the CPU oracle timed on this host under
+(adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
+scale/shift) under "adaln", and the CPU oracle timed on this host under
 "cpu_baseline".  Prints one JSON line.
 
---probe rms|rope|ropei|copy runs a few launches only, for rocprofv3 counter passes.
+--probe rms|rope|ropei|adaln|copy runs a few launches only, for rocprofv3 counter passes.
 """
 from __future__ import annotations
 
@@ -107,12 +108,18 @@ class Workload:
         if cfg.rope:
             self.cos = torch.from_numpy(inp["cos"]).to(dev)
             self.sin = torch.from_numpy(inp["sin"]).to(dev)
+        if cfg.adaln:
+            self.scale = to_device(inp["scale"], dev)
+            self.shift = to_device(inp["shift"], dev)
         torch.cuda.synchronize()
 
     def step(self, i: int):
         c = self.cfg
         k = i % self.nsets
-        if c.rope:
+        if c.adaln:
+            self.ltx.ltxnorm_rmsnorm_adaln_fwd(self.y[k], self.x[k], self.w, self.scale, self.shift,
+                                               c.rows, c.hidden, c.seq, c.eps, self.stream)
+        elif c.rope:
             fn = (self.ltx.ltxnorm_rmsnorm_rope_interleaved_fwd if c.interleaved
                   else self.ltx.ltxnorm_rmsnorm_rope_fwd)
             fn(self.y[k], self.x[k], self.w, self.cos, self.sin, c.rows, c.hidden, c.heads,
@@ -191,7 +198,7 @@ def probe(kind: str, launches: int):
                           "launches": launches}), flush=True)
         return
     cfg = datagen.CONFIGS[{"rms": datagen.HEADLINE, "rope": datagen.ROPE,
-                           "ropei": datagen.ROPE_INTERLEAVED}[kind]]
+                           "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN}[kind]]
     wl = Workload(cfg, dev, s, max_sets=2)
     for i in range(launches):
         wl.step(i)
@@ -206,8 +213,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--no-rope", action="store_true", help="skip the RMSNorm+RoPE line item")
-    ap.add_argument("--probe", choices=["rms", "rope", "ropei", "copy"])
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip the RoPE and AdaLN line items (headline only)")
+    ap.add_argument("--probe", choices=["rms", "rope", "ropei", "adaln", "copy"])
     ap.add_argument("--launches", type=int, default=10)
     args = ap.parse_args()
 
@@ -271,7 +279,8 @@ def main():
     if not args.no_rope:
         for key, name, kernel in (("rope", datagen.ROPE, "rmsnorm_rope"),
                                   ("rope_interleaved", datagen.ROPE_INTERLEAVED,
-                                   "rmsnorm_rope_interleaved")):
+                                   "rmsnorm_rope_interleaved"),
+                                  ("adaln", datagen.ADALN, "rmsnorm_adaln")):
             rc = datagen.CONFIGS[name]
             rw = Workload(rc, dev, stream)
             rsec = rw.time_steps(args.steps, args.warmup)

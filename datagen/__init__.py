@@ -127,6 +127,24 @@ def rope_tables(seq_len: int, head_dim: int, theta: float = 10000.0,
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
+def rope_tables_3d(frames: int, height: int, width: int, head_dim: int, theta: float = 10000.0):
+    """binary32 cos/sin tables with one row per video token of a
+    [frames x height x width] grid, flattened t-major ([batch, t*h*w, heads,
+    head_dim] layout).  The pages give the layout but not how the three
+    coordinates share the head_dim/2 rotation slots; this synthetic recipe
+    assigns slot i to axis i mod 3 (t, h, w) with frequency
+    theta^(-2 * (i // 3) / head_dim) applied to that axis' coordinate.  The
+    rotation kernels treat tables as data, so any recipe exercises them."""
+    half = head_dim // 2
+    i = np.arange(half)
+    axis = i % 3
+    inv_freq = np.exp(-(2.0 * (i // 3) / head_dim) * np.log(theta))
+    t, h, w = np.meshgrid(np.arange(frames), np.arange(height), np.arange(width), indexing="ij")
+    coords = np.stack([t.reshape(-1), h.reshape(-1), w.reshape(-1)], axis=1).astype(np.float64)
+    ang = coords[:, axis] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def fnv1a64(a: np.ndarray) -> str:
     """64-bit FNV-1a of the array's bytes (hex), recorded next to results."""
     data = np.ascontiguousarray(a).view(np.uint8)
@@ -157,6 +175,7 @@ class Config:
     head_dim: int = 0
     theta: float = 10000.0
     interleaved: bool = False  # RoPE pairing: rotate-half (False) or adjacent pairs
+    adaln_sigma: float = 0.0   # > 0: per-sample scale and shift ~ N(0, adaln_sigma), [batch, hidden]
 
     @property
     def rows(self) -> int:
@@ -166,12 +185,18 @@ class Config:
     def rope(self) -> bool:
         return self.heads > 0
 
+    @property
+    def adaln(self) -> bool:
+        return self.adaln_sigma > 0
+
     def algorithmic_bytes(self) -> int:
         """Bytes the op must move at least once: read x, write y (bf16 each),
         read the weight once; for RoPE also read both binary32 tables once."""
         b = 2 * self.rows * self.hidden * 2 + 2 * self.hidden
         if self.rope:
             b += 2 * self.seq * (self.head_dim // 2) * 4
+        if self.adaln:
+            b += 2 * self.batch * self.hidden * 2
         return b
 
 
@@ -189,10 +214,13 @@ CONFIGS = {
                                       heads=32, head_dim=64, theta=10000.0),
     "ropei_2x4096x2048_h32d64": Config("ropei_2x4096x2048_h32d64", 7, 2, 4096, 2048,
                                        heads=32, head_dim=64, theta=10000.0, interleaved=True),
+    "adaln_2x4096x2048": Config("adaln_2x4096x2048", 8, 2, 4096, 2048, adaln_sigma=0.25),
 }
 HEADLINE = "rms_4x4096x3072"
 ROPE = "rope_2x4096x2048_h32d64"
 ROPE_INTERLEAVED = "ropei_2x4096x2048_h32d64"
+ADALN = "adaln_2x4096x2048"
+STREAM_SCALE, STREAM_SHIFT = 4, 5
 
 
 def make_x(rows: int, hidden: int, seed: int = BASE_SEED, stream: int = STREAM_X,
@@ -219,6 +247,10 @@ def make_inputs(cfg: Config, seed: int = BASE_SEED, rows: int | None = None) -> 
                cfg.outlier_scale, off | STREAM_OUTLIER)
     w = make_w(cfg.hidden, seed, off | STREAM_W)
     out = {"x": x, "w": w, "eps": cfg.eps}
+    if cfg.adaln:
+        out.update(scale=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SCALE, cfg.adaln_sigma),
+                   shift=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SHIFT, cfg.adaln_sigma),
+                   rows_per_sample=cfg.seq)
     if cfg.rope:
         cos_t, sin_t = rope_tables(cfg.seq, cfg.head_dim, cfg.theta)
         out.update(cos=cos_t, sin=sin_t, heads=cfg.heads, head_dim=cfg.head_dim,

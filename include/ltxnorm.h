@@ -131,6 +131,29 @@ ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void *out, const void *x,
                                                     int32_t head_dim, int64_t seq_len,
                                                     float eps, hipStream_t stream);
 
+/*
+ * RMSNorm with per-sample adaptive modulation (AdaLN, as used in DiT blocks
+ * for conditioning): Hugging Face cuda-kernels skill page, section
+ * "Kernel-Specific Guidelines", AdaLN, gives norm(x) * weight * (1 + scale)
+ * + shift.  Computed as
+ *     y[r, j] = ((x[r, j] * rstd_r) * w[j]) * (1 + scale[b, j]) + shift[b, j]
+ * with b = r / rows_per_sample (integer division), binary32 arithmetic and
+ * one rounding to bf16.
+ *
+ *   out, x, weight, rows, hidden, eps, stream   as for ltxnorm_rmsnorm_fwd.
+ *   scale, shift  bf16 [ceil(rows / rows_per_sample), hidden], row-major,
+ *           read; NULL means zeros.  With both NULL the result equals
+ *           ltxnorm_rmsnorm_fwd bit for bit.  16-byte aligned; must not
+ *           overlap out.
+ *   rows_per_sample  rows sharing one modulation row (S for [B, S, H] x);
+ *           >= 1, else LTXNORM_ERR_SHAPE.
+ */
+ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void *out, const void *x, const void *weight,
+                                         const void *scale, const void *shift,
+                                         int64_t rows, int64_t hidden,
+                                         int64_t rows_per_sample, float eps,
+                                         hipStream_t stream);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char *ltxnorm_status_str(ltxnorm_status s);
 

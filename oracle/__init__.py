@@ -60,6 +60,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_rmsnorm_rope.restype = ctypes.c_int
     lib.oracle_rmsnorm_rope_interleaved.argtypes = list(lib.oracle_rmsnorm_rope.argtypes)
     lib.oracle_rmsnorm_rope_interleaved.restype = ctypes.c_int
+    lib.oracle_rmsnorm_adaln.argtypes = [p, p, p, p, p, p, i64, i64, i64, ctypes.c_float]
+    lib.oracle_rmsnorm_adaln.restype = ctypes.c_int
     lib.oracle_round.argtypes = [p, i64, p, p]
     lib.oracle_round.restype = None
     lib.oracle_bf16_from_f32.argtypes = [ctypes.c_float]
@@ -143,6 +145,31 @@ class Oracle:
                 rows, hidden, heads, head_dim, seq_len, ctypes.c_float(eps))
         if rc != 0:
             raise ValueError("oracle_rmsnorm_rope rejected its arguments")
+        return (y, mag) if with_mag else y
+
+    def rmsnorm_adaln(self, x, w, scale, shift, rows_per_sample: int, eps: float = 1e-6,
+                      with_mag: bool = False):
+        """RMSNorm then per-sample modulation y * (1 + scale[b]) + shift[b],
+        b = row // rows_per_sample; scale/shift bf16 [samples, H] or None.
+        With ``with_mag`` also returns |y * (1 + scale)| + |shift| per output,
+        which bounds the cancellation of the final sum."""
+        x = _u16(x, "x")
+        hidden = x.shape[-1]
+        rows = x.size // hidden if hidden else 0
+        w = None if w is None else _u16(w, "w")
+        samples = -(-rows // rows_per_sample) if rows else 0
+        for t, n in ((scale, "scale"), (shift, "shift")):
+            if t is not None and np.asarray(t).size != samples * hidden:
+                raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
+        scale = None if scale is None else _u16(scale, "scale")
+        shift = None if shift is None else _u16(shift, "shift")
+        y = np.empty(x.shape, dtype=np.float64)
+        mag = np.empty(x.shape, dtype=np.float64) if with_mag else None
+        rc = self.lib.oracle_rmsnorm_adaln(_ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(scale),
+                                           _ptr(shift), rows, hidden, rows_per_sample,
+                                           ctypes.c_float(eps))
+        if rc != 0:
+            raise ValueError("oracle_rmsnorm_adaln rejected its arguments")
         return (y, mag) if with_mag else y
 
     def round(self, y: np.ndarray):

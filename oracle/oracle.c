@@ -39,6 +39,13 @@
  *        out[2i + 1] = y[2i + 1] * cos[p, i] + y[2i] * sin[p, i]
  *    with the same [seq_len, head_dim/2] tables and row positions.
  *
+ *  - RMSNorm with adaptive modulation (AdaLN).  The skill page (section
+ *    "Kernel-Specific Guidelines", item AdaLN) gives the formula
+ *    norm(x) * weight * (1 + scale) + shift, used in DiT blocks for
+ *    conditioning.  Read with per-sample scale and shift rows: row r of x
+ *    belongs to sample b = r / rows_per_sample and uses scale[b, :] and
+ *    shift[b, :]; norm(x) * weight is the RMSNorm above.  One rounding.
+ *
  * Data format
  * -----------
  *  bf16 values travel as uint16_t bit patterns (the upper half of an IEEE
@@ -221,6 +228,38 @@ int oracle_rmsnorm_rope_interleaved(double *y, double *mag, const uint16_t *x,
                     m[2 * i + 1] = fabs(b * c) + fabs(a * s);
                 }
             }
+        }
+    }
+    return 0;
+}
+
+/* RMSNorm followed by per-sample modulation:
+ *   y[r, j] = x[r, j] * rstd_r * w[j] * (1 + scale[b, j]) + shift[b, j],
+ *   b = r / rows_per_sample.
+ *   mag    out (may be NULL), double [rows * hidden]: |n * (1 + scale)| +
+ *          |shift| for each output (n the normalised value), which bounds
+ *          the cancellation of the final sum.
+ *   scale, shift  in, bf16 bits [ceil(rows / rows_per_sample), hidden], or
+ *                 NULL for zeros.
+ * Returns 0, or -1 on a bad shape or NULL pointer. */
+int oracle_rmsnorm_adaln(double *y, double *mag, const uint16_t *x, const uint16_t *w,
+                         const uint16_t *scale, const uint16_t *shift,
+                         int64_t rows, int64_t hidden, int64_t rows_per_sample,
+                         float eps)
+{
+    if (!y || !x || rows < 0 || hidden <= 0 || rows_per_sample <= 0)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        double *yr = y + r * hidden;
+        normalise_row(yr, x + r * hidden, w, hidden, eps);
+        const int64_t b = r / rows_per_sample;
+        for (int64_t j = 0; j < hidden; ++j) {
+            double sc = scale ? bf16_value(scale[b * hidden + j]) : 0.0;
+            double sh = shift ? bf16_value(shift[b * hidden + j]) : 0.0;
+            double modulated = yr[j] * (1.0 + sc);
+            yr[j] = modulated + sh;
+            if (mag)
+                mag[r * hidden + j] = fabs(modulated) + fabs(sh);
         }
     }
     return 0;

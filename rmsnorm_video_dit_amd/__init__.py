@@ -12,14 +12,17 @@ The low-level functions keep the C names and argument order:
     ltxnorm_rmsnorm_rope_fwd(out, x, weight, cos_tab, sin_tab, rows, hidden,
                              heads, head_dim, seq_len, eps, stream)
     ltxnorm_rmsnorm_rope_interleaved_fwd(... same arguments ...)
+    ltxnorm_rmsnorm_adaln_fwd(out, x, weight, scale, shift, rows, hidden,
+                              rows_per_sample, eps, stream)
     ltxnorm_status_str(status), ltxnorm_version()
 
 Pointer arguments accept a torch tensor, an integer address or None; ``stream``
 accepts a ``torch.cuda.Stream``, an integer handle, or None for torch's
 current stream.  A non-OK status raises ``LtxnormError``.
 
-``rmsnorm(x, weight=None, eps=1e-6, out=None)`` and ``rmsnorm_rope(...)`` are
-the tensor-level forms (functional, or out-variant when ``out`` is given).
+``rmsnorm(x, weight=None, eps=1e-6, out=None)``, ``rmsnorm_rope(...)`` and
+``rmsnorm_adaln(...)`` are the tensor-level forms (functional, or out-variant
+when ``out`` is given).
 """
 from __future__ import annotations
 
@@ -57,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.ltxnorm_rmsnorm_rope_interleaved_fwd.argtypes = [p, p, p, p, p, i64, i64, i32, i32, i64,
                                                            f32, p]
         L.ltxnorm_rmsnorm_rope_interleaved_fwd.restype = ctypes.c_int
+        L.ltxnorm_rmsnorm_adaln_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, f32, p]
+        L.ltxnorm_rmsnorm_adaln_fwd.restype = ctypes.c_int
         L.ltxnorm_status_str.argtypes = [ctypes.c_int]
         L.ltxnorm_status_str.restype = ctypes.c_char_p
         L.ltxnorm_version.argtypes = []
@@ -108,6 +113,21 @@ def ltxnorm_rmsnorm_rope_interleaved_fwd_status(out, x, weight, cos_tab, sin_tab
     return lib().ltxnorm_rmsnorm_rope_interleaved_fwd(
         _addr(out), _addr(x), _addr(weight), _addr(cos_tab), _addr(sin_tab), int(rows),
         int(hidden), int(heads), int(head_dim), int(seq_len), float(eps), _stream(stream))
+
+
+def ltxnorm_rmsnorm_adaln_fwd_status(out, x, weight, scale, shift, rows, hidden, rows_per_sample,
+                                     eps, stream) -> int:
+    return lib().ltxnorm_rmsnorm_adaln_fwd(_addr(out), _addr(x), _addr(weight), _addr(scale),
+                                           _addr(shift), int(rows), int(hidden),
+                                           int(rows_per_sample), float(eps), _stream(stream))
+
+
+def ltxnorm_rmsnorm_adaln_fwd(out, x, weight, scale, shift, rows, hidden, rows_per_sample, eps,
+                              stream=None) -> None:
+    st = ltxnorm_rmsnorm_adaln_fwd_status(out, x, weight, scale, shift, rows, hidden,
+                                          rows_per_sample, eps, stream)
+    if st != OK:
+        raise LtxnormError(st, "ltxnorm_rmsnorm_adaln_fwd")
 
 
 def ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, stream=None) -> None:
@@ -184,4 +204,36 @@ def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: fl
     rows = x.numel() // hidden if hidden else 0
     fn = ltxnorm_rmsnorm_rope_interleaved_fwd if interleaved else ltxnorm_rmsnorm_rope_fwd
     fn(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim, cos_tab.shape[0], eps, None)
+    return out
+
+
+def rmsnorm_adaln(x, weight, scale, shift, eps: float = 1e-6, out=None, rows_per_sample=None):
+    """RMSNorm then per-sample modulation: norm(x) * weight * (1 + scale) + shift.
+
+    ``x`` bf16 ``[B, S, H]`` (or ``[rows, H]`` with ``rows_per_sample``);
+    ``scale`` and ``shift`` bf16 ``[B, H]`` or None (zeros); row r uses
+    sample r // S."""
+    import torch
+    _check_act(x, "x")
+    for t, n in ((weight, "weight"), (scale, "scale"), (shift, "shift")):
+        if t is not None:
+            _check_act(t, n)
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    if rows_per_sample is None:
+        if x.dim() != 3:
+            raise ValueError("give rows_per_sample for x that is not [B, S, H]")
+        rows_per_sample = x.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_act(out, "out")
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    samples = -(-rows // rows_per_sample) if rows else 0
+    for t, n in ((scale, "scale"), (shift, "shift")):
+        if t is not None and t.numel() != samples * hidden:
+            raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
+    ltxnorm_rmsnorm_adaln_fwd(out, x, weight, scale, shift, rows, hidden, max(rows_per_sample, 1),
+                              eps, None)
     return out

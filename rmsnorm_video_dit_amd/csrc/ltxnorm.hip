@@ -540,6 +540,99 @@ rmsnorm_rope_interleaved_kernel(const RopeArgs a) {
     }
 }
 
+struct AdaArgs {
+    uint16_t* out;
+    const uint16_t* x;
+    const uint16_t* w;
+    const uint16_t* scale;  // [samples, hidden] or null (zeros)
+    const uint16_t* shift;  // [samples, hidden] or null (zeros)
+    int64_t rows;
+    int64_t rows_per_sample;
+    int32_t nvec;
+    float hidden_f;
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// RMSNorm with per-sample adaptive modulation (AdaLN, as in DiT blocks):
+// y = ((x * rstd) * w) * (1 + scale[b]) + shift[b], b = row / rows_per_sample,
+// all in binary32 and rounded once.  The RMSNorm layout and reduction; the
+// modulation rows are shared by every row of a sample and come from L2 after
+// the reduction.  A null scale reads as +0 (factor exactly 1) and a null
+// shift as -0 (x + -0 == x for every x, signed zeros included), so with both
+// null the result equals plain RMSNorm bit for bit.
+// ---------------------------------------------------------------------------
+template <int VPL, int WPR, bool FULL>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_adaln_kernel(const AdaArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int L = Layout<WPR>::kLanesPerRow;
+    constexpr uint32_t kNegZeroPair = 0x80008000u;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: scalar row math
+    const int slot = wave / WPR;
+    const int wave_in_row = wave % WPR;
+    const int t = wave_in_row * kWave + (threadIdx.x & (kWave - 1));
+
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = k * L + t;
+        const bool in = FULL || v < a.nvec;
+        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v]
+                                        : u32x4{kOnesPair, kOnesPair, kOnesPair, kOnesPair};
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+        const int64_t sample = active ? row / a.rows_per_sample : 0;
+        const u32x4* sr = reinterpret_cast<const u32x4*>(a.scale) + sample * a.nvec;
+        const u32x4* hr = reinterpret_cast<const u32x4*>(a.shift) + sample * a.nvec;
+
+        u32x4 xv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[8];
+            widen8(xv[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf(f[e], f[e], part);
+        }
+        const float rstd = rstd_of(row_sum<WPR>(part, slot, wave_in_row, parity), a.hidden_f, a.eps);
+
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = k * L + t;
+            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+            const u32x4 sv = (a.scale != nullptr && in) ? sr[v] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 hv = (a.shift != nullptr && in)
+                                 ? hr[v]
+                                 : u32x4{kNegZeroPair, kNegZeroPair, kNegZeroPair, kNegZeroPair};
+            keep_packed(xv[k]);
+            keep_packed(wv[k]);
+            float f[8], g[8], sc[8], sh[8];
+            widen8(xv[k], f);
+            widen8(wv[k], g);
+            widen8(sv, sc);
+            widen8(hv, sh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = ((f[e] * rstd) * g[e]) * (1.0f + sc[e]) + sh[e];
+            if (in) store_stream(yr + v, narrow8(f));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: validation, per-hidden dispatch, launch.
 // ---------------------------------------------------------------------------
@@ -607,6 +700,13 @@ struct RmsLauncher {
 struct RopeLauncher {
     template <int WPR, int PER, bool FULL>
     ltxnorm_status go(const RopeArgs& a, hipStream_t s) const { return launch_rope<WPR, PER, FULL>(a, s); }
+};
+struct AdaLauncher {
+    template <int WPR, int PER, bool FULL>
+    ltxnorm_status go(const AdaArgs& a, hipStream_t s) const {
+        return launch((const void*)&rmsnorm_adaln_kernel<PER, WPR, FULL>, Layout<WPR>::kThreads,
+                      Layout<WPR>::kRowsPerBlock, a.rows, a, s);
+    }
 };
 template <bool SHARED>
 struct RopeInterleavedLauncher {
@@ -764,6 +864,29 @@ ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void* out, const void* x, co
     if ((kWave * p.wpr) % vph == 0)
         return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeInterleavedLauncher<true>{});
     return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, RopeInterleavedLauncher<false>{});
+}
+
+ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void* out, const void* x, const void* weight,
+                                         const void* scale, const void* shift, int64_t rows,
+                                         int64_t hidden, int64_t rows_per_sample, float eps,
+                                         hipStream_t stream) {
+    if (rows_per_sample < 1) return LTXNORM_ERR_SHAPE;
+    bool empty = false;
+    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, &empty);
+    if (st != LTXNORM_OK || empty) return st;
+    if ((scale && misaligned(scale)) || (shift && misaligned(shift))) return LTXNORM_ERR_ALIGN;
+    const int64_t samples = (rows + rows_per_sample - 1) / rows_per_sample;
+    const int64_t nbytes = rows * hidden * 2;
+    const int64_t mbytes = samples * hidden * 2;
+    if ((scale && overlap(out, nbytes, scale, mbytes)) || (shift && overlap(out, nbytes, shift, mbytes)))
+        return LTXNORM_ERR_ALIAS;
+    const int64_t nvec = hidden / kElemsPerVec;
+    const AdaArgs a{static_cast<uint16_t*>(out), static_cast<const uint16_t*>(x),
+                    static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(scale),
+                    static_cast<const uint16_t*>(shift), rows, rows_per_sample, (int32_t)nvec,
+                    (float)hidden, eps};
+    const Plan p = plan_for(nvec, 4, 2);
+    return by_plan<4, 2, kMaxVecPerLane>(p, a, stream, AdaLauncher{});
 }
 
 const char* ltxnorm_status_str(ltxnorm_status s) {

@@ -385,6 +385,100 @@ def pin_rope_il_mag(o):
 
 
 # --------------------------------------------------------------------------
+# AdaLN pins: y = norm(x) * w * (1 + scale[b]) + shift[b], b = r // S
+# --------------------------------------------------------------------------
+
+def pin_adaln_zero_modulation_is_rmsnorm(o):
+    rng = np.random.default_rng(71)
+    x = _rand_bf16(rng, (6, 40))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 40))
+    zeros = np.zeros((3, 40), dtype=np.uint16)
+    assert np.array_equal(o.rmsnorm_adaln(x, w, None, None, 2), o.rmsnorm(x, w, 1e-6))
+    assert np.array_equal(o.rmsnorm_adaln(x, w, zeros, zeros, 2), o.rmsnorm(x, w, 1e-6))
+
+
+def pin_adaln_scale_minus_one_gives_shift(o):
+    """1 + scale = 0 removes the normalised value: the output is the shift."""
+    rng = np.random.default_rng(73)
+    x = _rand_bf16(rng, (4, 24))
+    minus1 = np.full((2, 24), 0xBF80, dtype=np.uint16)
+    shift = _rand_bf16(rng, (2, 24))
+    y = o.rmsnorm_adaln(x, None, minus1, shift, 2)
+    assert np.array_equal(y, np.repeat(_val(shift), 2, axis=0))
+
+
+def pin_adaln_exact_closed_form(o):
+    """Constant row c = 2^-3 with eps = 0 normalises to exactly 1, so
+    y = w * (1 + scale) + shift, evaluated exactly with fractions."""
+    rng = np.random.default_rng(79)
+    hidden, S = 16, 3
+    x = _bf16(np.full((2 * S, hidden), 0.125))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, hidden))
+    scale = _rand_bf16(rng, (2, hidden), scale=0.3)
+    shift = _rand_bf16(rng, (2, hidden), scale=0.3)
+    y = o.rmsnorm_adaln(x, w, scale, shift, S, eps=0.0)
+    for r in range(2 * S):
+        b = r // S
+        for j in range(hidden):
+            want = (Fraction(float(_val(w[j]))) * (1 + Fraction(float(_val(scale[b, j]))))
+                    + Fraction(float(_val(shift[b, j]))))
+            assert Fraction(y[r, j]) == want, (r, j)
+
+
+def pin_adaln_sample_rows(o):
+    """Row r uses sample r // S: each row alone with its own sample's
+    modulation rows (S = 1) gives the same values."""
+    rng = np.random.default_rng(83)
+    hidden, S = 24, 3
+    x = _rand_bf16(rng, (8, hidden))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, hidden))
+    scale = _rand_bf16(rng, (3, hidden), scale=0.2)
+    shift = _rand_bf16(rng, (3, hidden), scale=0.2)
+    y = o.rmsnorm_adaln(x, w, scale, shift, S)
+    for r in range(8):
+        b = r // S
+        yr = o.rmsnorm_adaln(x[r:r + 1], w, scale[b:b + 1], shift[b:b + 1], 1)
+        assert np.array_equal(yr[0], y[r]), r
+
+
+def pin_adaln_brute_force(o):
+    """Tiny rows against exact fractions / 60-digit decimals."""
+    rng = np.random.default_rng(89)
+    for hidden in (1, 8, 32):
+        x = _rand_bf16(rng, (4, hidden))
+        w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, hidden))
+        scale = _rand_bf16(rng, (2, hidden), scale=0.4)
+        shift = _rand_bf16(rng, (2, hidden), scale=0.4)
+        y = o.rmsnorm_adaln(x, w, scale, shift, 2)
+        for r in range(4):
+            b = r // 2
+            n = _exact_rms_row(_val(x[r]), _val(w), EPS32)
+            for j in range(hidden):
+                e = n[j] * (1 + Decimal(float(_val(scale[b, j])))) + Decimal(float(_val(shift[b, j])))
+                tol = Decimal((hidden + 12) * 2.0 ** -53) * (abs(n[j]) * 2 + abs(e) + Decimal(1e-300))
+                assert abs(Decimal(y[r, j]) - e) <= tol, (hidden, r, j)
+
+
+def pin_adaln_mag(o):
+    """The magnitude sum is |n (1 + scale)| + |shift| with n the RMSNorm
+    value: it bounds the output and equals its magnitude when the two terms
+    have one sign."""
+    rng = np.random.default_rng(97)
+    x = _rand_bf16(rng, (4, 16))
+    w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, 16))
+    scale = _rand_bf16(rng, (2, 16), scale=0.5)
+    shift = _rand_bf16(rng, (2, 16), scale=0.5)
+    y, mag = o.rmsnorm_adaln(x, w, scale, shift, 2, with_mag=True)
+    n = o.rmsnorm(x, w, 1e-6)
+    sc = np.repeat(_val(scale), 2, axis=0)
+    sh = np.repeat(_val(shift), 2, axis=0)
+    assert np.allclose(mag, np.abs(n * (1 + sc)) + np.abs(sh), rtol=1e-15)
+    assert np.all(np.abs(y) <= mag * (1 + 1e-15))
+    same = np.sign(n * (1 + sc)) == np.sign(sh)
+    assert np.allclose(np.abs(y[same]), mag[same], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
 # Rounding pins
 # --------------------------------------------------------------------------
 
@@ -457,5 +551,7 @@ PINS = [
     pin_rope_constant_row, pin_rope_row_position, pin_rope_mag,
     pin_rope_il_position_zero_is_rmsnorm, pin_rope_il_complex_rotation,
     pin_rope_il_matches_rotate_half_after_reorder, pin_rope_il_constant_row, pin_rope_il_mag,
+    pin_adaln_zero_modulation_is_rmsnorm, pin_adaln_scale_minus_one_gives_shift,
+    pin_adaln_exact_closed_form, pin_adaln_sample_rows, pin_adaln_brute_force, pin_adaln_mag,
     pin_bf16_rounding, pin_round_twice,
 ]

@@ -4,10 +4,10 @@ Rule, per element: |gpu - ref16| <= max(ulp16(ref16), 2^-16 * m), where
 ref16 is the oracle's binary32 result rounded to bf16 (nearest-even),
 ulp16(v) = 2^(floor(log2|v|) - 7) is the bf16 spacing at v's binade (the
 smallest subnormal spacing 2^-133 for v = 0 or subnormal v, so zeros must
-match up to sign), and m is the oracle's magnitude sum |a c| + |b s| of the
-two products a rotated output comes from (m = 0 for plain RMSNorm).  The
-floor term only binds where the rotation cancels more than ~8 bits.  NaN
-must meet NaN.  This is the "1 bf16 ulp against the oracle's binary32 result
+match up to sign), and m is the oracle's magnitude sum of the two terms an
+output is the sum of: |a c| + |b s| for a rotated output, |n (1 + scale)| +
+|shift| for a modulated one, m = 0 for plain RMSNorm.  The floor term only
+binds where those two terms cancel more than ~8 bits.  NaN must meet NaN.  This is the "1 bf16 ulp against the oracle's binary32 result
 rounded to bf16" bar; the derivation of the floor is in the design notes.
 """
 from __future__ import annotations

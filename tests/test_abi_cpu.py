@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
+    assert declared_functions() == ["ltxnorm_rmsnorm_adaln_fwd", "ltxnorm_rmsnorm_fwd",
+                                    "ltxnorm_rmsnorm_rope_fwd",
                                     "ltxnorm_rmsnorm_rope_interleaved_fwd",
                                     "ltxnorm_status_str", "ltxnorm_version"]
 
@@ -139,6 +140,27 @@ def test_rope_interleaved_validation(kw, status):
     st = ltx.ltxnorm_rmsnorm_rope_interleaved_fwd_status(
         args["out"], args["x"], args["w"], args["c"], args["s"], args["rows"], args["hidden"],
         args["heads"], args["head_dim"], args["seq_len"], args["eps"], 0)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows_per_sample=0), ltx.ERR_SHAPE),
+    (dict(hidden=12), ltx.ERR_UNSUPPORTED),
+    (dict(eps=-1.0), ltx.ERR_VALUE),
+    (dict(out=None), ltx.ERR_NULL),
+    (dict(scale=A + 200 * MB + 2), ltx.ERR_ALIGN),
+    (dict(shift=A + 201 * MB + 8), ltx.ERR_ALIGN),
+    (dict(scale=A + 1024), ltx.ERR_ALIAS),
+    (dict(shift=A - 64), ltx.ERR_ALIAS),
+    (dict(rows=0, out=None, x=None), ltx.OK),
+])
+def test_adaln_validation(kw, status):
+    args = dict(out=A, x=A + 64 * MB, w=None, scale=A + 200 * MB, shift=A + 201 * MB, rows=8,
+                hidden=2048, rows_per_sample=4, eps=1e-6)
+    args.update(kw)
+    st = ltx.ltxnorm_rmsnorm_adaln_fwd_status(args["out"], args["x"], args["w"], args["scale"],
+                                              args["shift"], args["rows"], args["hidden"],
+                                              args["rows_per_sample"], args["eps"], 0)
     assert st == status
 
 

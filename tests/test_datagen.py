@@ -66,6 +66,7 @@ def test_recipes():
     assert c[datagen.HEADLINE].rows == 16384 and c[datagen.HEADLINE].hidden == 3072
     assert c[datagen.HEADLINE].algorithmic_bytes() == 201_332_736
     assert c[datagen.ROPE].algorithmic_bytes() == 68_161_536
+    assert c[datagen.ADALN].algorithmic_bytes() == 4 * 8192 * 2048 + 2 * 2048 + 2 * 2 * 2 * 2048
     assert [c[k].algorithmic_bytes() for k in ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
                                                "rms_2x4096x3072_outliers")] == \
         [8_392_704, 16_781_312, 33_558_528, 100_669_440]
@@ -104,3 +105,16 @@ def test_golden_hashes_and_oracle_fixture():
         ref32, ref16 = compute(o, inp)
         assert [format(int(v), "08x") for v in ref32.view("uint32").reshape(-1)] == want["ref32_hex"], name
         assert [format(int(v), "04x") for v in ref16.reshape(-1)] == want["ref16_hex"], name
+
+
+def test_rope_tables_3d():
+    c, s = datagen.rope_tables_3d(3, 4, 5, 64)
+    assert c.shape == (60, 32) and s.shape == (60, 32)
+    # token (t, h, w) = (2, 1, 3) sits at row (2*4 + 1)*5 + 3 = 48
+    r = 48
+    for i in range(32):
+        coord = (2, 1, 3)[i % 3]
+        ang = coord * 10000.0 ** (-2 * (i // 3) / 64)
+        assert abs(c[r, i] - np.float32(math.cos(ang))) <= 1.2e-7
+        assert abs(s[r, i] - np.float32(math.sin(ang))) <= 1.2e-7
+    assert np.all(c[0] == 1.0) and np.all(s[0] == 0.0)

@@ -60,6 +60,24 @@ def check_rms(x, w, eps=1e-6, label=""):
     return got, rep
 
 
+def run_adaln(x, w, scale, shift, rows_per_sample, eps=1e-6):
+    xt = dev_bf16(x)
+    wt = None if w is None else dev_bf16(w)
+    st = None if scale is None else dev_bf16(scale)
+    ht = None if shift is None else dev_bf16(shift)
+    return host_bits(ltx.rmsnorm_adaln(xt, wt, st, ht, eps, rows_per_sample=rows_per_sample))
+
+
+def check_adaln(x, w, scale, shift, rows_per_sample, eps=1e-6, label=""):
+    got = run_adaln(x, w, scale, shift, rows_per_sample, eps)
+    y, mag = ORC.rmsnorm_adaln(x, w, scale, shift, rows_per_sample, eps, with_mag=True)
+    ref32, ref16 = ORC.round(y)
+    rep = compare_bf16(got, ref16, mag, ref32)
+    print(label, rep, flush=True)
+    assert rep["pass"], (label, rep)
+    return got, rep
+
+
 def check_rope(x, w, c, s, heads, head_dim, eps=1e-6, label="", interleaved=False):
     got = run_rope(x, w, c, s, heads, head_dim, eps, interleaved)
     y, mag = ORC.rmsnorm_rope(x, w, c, s, heads, head_dim, eps, with_mag=True,
@@ -83,10 +101,13 @@ def test_workload_full_size(name):
     if cfg.rope:
         got, rep = check_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg.heads, cfg.head_dim,
                               cfg.eps, label=name, interleaved=cfg.interleaved)
+    elif cfg.adaln:
+        got, rep = check_adaln(inp["x"], inp["w"], inp["scale"], inp["shift"],
+                               inp["rows_per_sample"], cfg.eps, label=name)
     else:
         got, rep = check_rms(inp["x"], inp["w"], cfg.eps, label=name)
-    if cfg.rope:
-        # only outputs whose two products cancel may differ by more than an
+    if cfg.rope or cfg.adaln:
+        # only outputs whose two terms cancel may differ by more than an
         # ulp of their (small) value, and only within the 2^-16 * m floor
         assert rep["n_floor_bound"] <= 1e-5 * rep["n"]
     else:
@@ -171,11 +192,59 @@ def test_rope_interleaved_invariants():
                           run_rope(x, ones, c, s, 24, 128, interleaved=True))
 
 
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rope_video_3d_tables(interleaved):
+    """3D video positions: one table row per t*h*w token ([batch, t*h*w,
+    heads, head_dim]); a batch of 2 clips of 7 x 12 x 16 tokens."""
+    announce(f"rope 3d tables interleaved={interleaved}")
+    c, s = datagen.rope_tables_3d(7, 12, 16, 64)
+    rows = 2 * c.shape[0]
+    x = datagen.make_x(rows, 2048, seed=16, stream=1)
+    w = datagen.make_w(2048, seed=16, stream=2)
+    check_rope(x, w, c, s, 32, 64, interleaved=interleaved, label=f"rope 3d il={interleaved}")
+
+
 def test_rope_outlier_values_and_null_weight():
     announce("rope outliers, weight None")
     x = datagen.make_x(300, 2048, seed=5, stream=1, sigma=2.0, outlier_p=0.01, outlier_scale=50.0)
     c, s = datagen.rope_tables(4096, 64, 10000.0)
     check_rope(x, None, c, s, 32, 64, label="rope outliers")
+
+
+@pytest.mark.parametrize("hidden", [8, 520, 2048, 3072, 4104, 16384, 65536])
+@pytest.mark.parametrize("rows,rows_per_sample", [(1, 1), (7, 3), (1023, 1023), (4000, 1000)])
+def test_adaln_edge_shapes(rows, rows_per_sample, hidden):
+    if rows * hidden > (1 << 24):
+        rows = max(1, (1 << 24) // hidden)
+        rows_per_sample = max(1, min(rows_per_sample, rows))
+    samples = -(-rows // rows_per_sample)
+    announce(f"adaln rows={rows} hidden={hidden} rows_per_sample={rows_per_sample}")
+    seed = hidden + rows + 3 * rows_per_sample
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1)
+    w = datagen.make_w(hidden, seed=seed, stream=2)
+    sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.3)
+    sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.3)
+    check_adaln(x, w, sc, sh, rows_per_sample, label=f"adaln {rows}x{hidden} S={rows_per_sample}")
+
+
+def test_adaln_invariants():
+    """Null modulation equals RMSNorm bit for bit; null weight equals ones;
+    scale = -1 gives the shift exactly; in place equals out of place."""
+    announce("adaln invariants")
+    x = datagen.make_x(600, 3072, seed=17, stream=1)
+    w = datagen.make_w(3072, seed=17, stream=2)
+    assert np.array_equal(run_adaln(x, w, None, None, 200), run_rms(x, w))
+    sc = datagen.make_x(3, 3072, seed=17, stream=4, sigma=0.3)
+    sh = datagen.make_x(3, 3072, seed=17, stream=5, sigma=0.3)
+    ones = np.full(3072, 0x3F80, dtype=np.uint16)
+    ref = run_adaln(x, w, sc, sh, 200)
+    assert np.array_equal(run_adaln(x, None, sc, sh, 200), run_adaln(x, ones, sc, sh, 200))
+    minus1 = np.full((3, 3072), 0xBF80, dtype=np.uint16)
+    got = run_adaln(x, w, minus1, sh, 200)
+    assert np.array_equal(got, np.repeat(sh, 200, axis=0))
+    xt = dev_bf16(x)
+    ltx.rmsnorm_adaln(xt, dev_bf16(w), dev_bf16(sc), dev_bf16(sh), 1e-6, out=xt, rows_per_sample=200)
+    assert np.array_equal(host_bits(xt), ref)
 
 
 # ---------------------------------------------------------------------------

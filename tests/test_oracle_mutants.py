@@ -44,6 +44,14 @@ MUTANTS = {
     "rope_il_pairs_swapped": ("double a = head[2 * i];     /* even element */\n                double b = head[2 * i + 1]; /* odd element  */",
                               "double b = head[2 * i];     /* even element */\n                double a = head[2 * i + 1]; /* odd element  */"),
     "rope_il_mag_signed": ("m[2 * i] = fabs(a * c) + fabs(b * s);", "m[2 * i] = fabs(a * c - b * s);"),
+    "adaln_scale_not_plus_one": ("double modulated = yr[j] * (1.0 + sc);", "double modulated = yr[j] * sc;"),
+    "adaln_shift_subtracted": ("yr[j] = modulated + sh;", "yr[j] = modulated - sh;"),
+    "adaln_shift_dropped": ("yr[j] = modulated + sh;", "yr[j] = modulated;"),
+    "adaln_shift_scaled": ("yr[j] = modulated + sh;", "yr[j] = modulated + sh * (1.0 + sc);"),
+    "adaln_mag_signed": ("mag[r * hidden + j] = fabs(modulated) + fabs(sh);", "mag[r * hidden + j] = fabs(modulated + sh);"),
+    "adaln_sample_mod": ("const int64_t b = r / rows_per_sample;", "const int64_t b = r % rows_per_sample % (rows / rows_per_sample > 0 ? rows / rows_per_sample : 1);"),
+    "adaln_scale_transposed": ("double sc = scale ? bf16_value(scale[b * hidden + j]) : 0.0;",
+                               "double sc = scale ? bf16_value(scale[b * hidden + (hidden - 1 - j)]) : 0.0;"),
     "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
     "bf16_truncate": ("kept += 1u;", "kept += 0u;"),
     "bf16_ties_odd": ("(kept & 1u))", "!(kept & 1u))"),
