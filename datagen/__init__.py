@@ -223,33 +223,50 @@ ADALN = "adaln_2x4096x2048"
 STREAM_SCALE, STREAM_SHIFT = 4, 5
 
 
+def encode(v: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Doubles as inputs of the given type: bf16 bit patterns (uint16), or
+    float16 / float32 arrays (numpy's round-to-nearest-even cast)."""
+    if dtype == "bf16":
+        return to_bf16_bits(v)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return np.asarray(v).astype(np.float16)
+    if dtype == "f32":
+        return np.asarray(v).astype(np.float32)
+    raise ValueError(dtype)
+
+
 def make_x(rows: int, hidden: int, seed: int = BASE_SEED, stream: int = STREAM_X,
            sigma: float = 1.0, outlier_p: float = 0.0, outlier_scale: float = 1.0,
-           outlier_stream: int = STREAM_OUTLIER) -> np.ndarray:
+           outlier_stream: int = STREAM_OUTLIER, dtype: str = "bf16") -> np.ndarray:
     n = rows * hidden
     v = normal(seed, stream, n) * sigma
     if outlier_p > 0.0:
         mask = uniform(seed, outlier_stream, n) < outlier_p
         v[mask] *= outlier_scale
-    return to_bf16_bits(v).reshape(rows, hidden)
+    return encode(v, dtype).reshape(rows, hidden)
 
 
-def make_w(hidden: int, seed: int = BASE_SEED, stream: int = STREAM_W) -> np.ndarray:
-    return to_bf16_bits(0.5 + uniform(seed, stream, hidden))
+def make_w(hidden: int, seed: int = BASE_SEED, stream: int = STREAM_W, dtype: str = "bf16") -> np.ndarray:
+    return encode(0.5 + uniform(seed, stream, hidden), dtype)
 
 
-def make_inputs(cfg: Config, seed: int = BASE_SEED, rows: int | None = None) -> dict:
-    """Inputs for a workload; ``rows`` < cfg.rows gives the leading rows only
-    (the same values the full workload has there)."""
+def make_inputs(cfg: Config, seed: int = BASE_SEED, rows: int | None = None,
+                dtype: str = "bf16") -> dict:
+    """Inputs for a workload in the given I/O type ("bf16", "f16", "f32");
+    ``rows`` < cfg.rows gives the leading rows only (the same values the
+    full workload has there)."""
     off = cfg.config_id << 8
     r = cfg.rows if rows is None else rows
     x = make_x(r, cfg.hidden, seed, off | STREAM_X, cfg.sigma, cfg.outlier_p,
-               cfg.outlier_scale, off | STREAM_OUTLIER)
-    w = make_w(cfg.hidden, seed, off | STREAM_W)
+               cfg.outlier_scale, off | STREAM_OUTLIER, dtype=dtype)
+    w = make_w(cfg.hidden, seed, off | STREAM_W, dtype=dtype)
     out = {"x": x, "w": w, "eps": cfg.eps}
     if cfg.adaln:
-        out.update(scale=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SCALE, cfg.adaln_sigma),
-                   shift=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SHIFT, cfg.adaln_sigma),
+        out.update(scale=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SCALE, cfg.adaln_sigma,
+                                dtype=dtype),
+                   shift=make_x(cfg.batch, cfg.hidden, seed, off | STREAM_SHIFT, cfg.adaln_sigma,
+                                dtype=dtype),
                    rows_per_sample=cfg.seq)
     if cfg.rope:
         cos_t, sin_t = rope_tables(cfg.seq, cfg.head_dim, cfg.theta)

@@ -36,6 +36,12 @@
  *   - Arguments are validated on the host before any HIP call; a rejected
  *     call enqueues nothing.  No C++ exception crosses this boundary.
  *   - Calls are thread-safe and reentrant; the library keeps no state.
+ *   - Each operation has a bf16 entry point and a `_dt` twin taking the I/O
+ *     dtype (the skill page, "Supported Data Types", lists FP16, BF16 and
+ *     FP32); x, out, weight, scale and shift all use that dtype, the
+ *     rotation tables are always binary32, and arithmetic is binary32 with
+ *     one rounding to the output type (round to nearest even; NaN stays NaN;
+ *     fp16 overflows to infinity).
  */
 #ifndef LTXNORM_H
 #define LTXNORM_H
@@ -47,11 +53,20 @@
 extern "C" {
 #endif
 
-#define LTXNORM_ABI_VERSION 1
+#define LTXNORM_ABI_VERSION 2
 
-/* Largest supported hidden size: 16 wavefronts x 64 lanes x 8 vectors of 8
- * bf16 values per row, all held in registers. */
+#define LTXNORM_API __attribute__((visibility("default")))
+
+/* Largest supported hidden size: 16 wavefronts x 64 lanes x 8 vectors of 16
+ * bytes per row, all held in registers: 65536 bf16/fp16 or 32768 fp32. */
 #define LTXNORM_MAX_HIDDEN 65536
+#define LTXNORM_MAX_HIDDEN_F32 32768
+
+typedef enum ltxnorm_dtype {
+    LTXNORM_BF16 = 0,  /* bfloat16 (8 values per 16-byte vector) */
+    LTXNORM_F16 = 1,   /* IEEE binary16 (8 per vector)           */
+    LTXNORM_F32 = 2    /* IEEE binary32 (4 per vector)           */
+} ltxnorm_dtype;
 
 typedef enum ltxnorm_status {
     LTXNORM_OK = 0,
@@ -59,7 +74,9 @@ typedef enum ltxnorm_status {
     LTXNORM_ERR_SHAPE = 2,       /* rows < 0, hidden <= 0, size overflow, or a RoPE
                                     shape that does not fit (see below)             */
     LTXNORM_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                 */
-    LTXNORM_ERR_UNSUPPORTED = 4, /* hidden % 8 != 0 or hidden > LTXNORM_MAX_HIDDEN   */
+    LTXNORM_ERR_UNSUPPORTED = 4, /* unknown dtype, hidden not a whole number of
+                                    16-byte vectors (8 bf16/fp16, 4 fp32) or above
+                                    LTXNORM_MAX_HIDDEN(_F32)                         */
     LTXNORM_ERR_ALIAS = 5,       /* out partially overlaps x, or overlaps an input
                                     that is only read (weight, tables)              */
     LTXNORM_ERR_VALUE = 6,       /* eps negative, infinite or NaN                    */
@@ -82,9 +99,15 @@ typedef enum ltxnorm_status {
  *   stream  HIP stream to enqueue on.
  * out, x and weight must be 16-byte aligned.
  */
-ltxnorm_status ltxnorm_rmsnorm_fwd(void *out, const void *x, const void *weight,
-                                   int64_t rows, int64_t hidden, float eps,
-                                   hipStream_t stream);
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_fwd(void *out, const void *x, const void *weight,
+                                               int64_t rows, int64_t hidden, float eps,
+                                               hipStream_t stream);
+
+/* ltxnorm_rmsnorm_fwd for any ltxnorm_dtype; hidden a multiple of 8 (bf16,
+ * fp16) or 4 (fp32). */
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_fwd_dt(void *out, const void *x, const void *weight,
+                                                  int64_t rows, int64_t hidden, float eps,
+                                                  ltxnorm_dtype dtype, hipStream_t stream);
 
 /*
  * Fused RMSNorm over the full row, then rotate-half RoPE per head.
@@ -102,11 +125,21 @@ ltxnorm_status ltxnorm_rmsnorm_fwd(void *out, const void *x, const void *weight,
  * Shape errors (hidden != heads*head_dim, head_dim % 16 != 0, seq_len < 1)
  * give LTXNORM_ERR_SHAPE.
  */
-ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *weight,
-                                        const float *cos_tab, const float *sin_tab,
-                                        int64_t rows, int64_t hidden, int32_t heads,
-                                        int32_t head_dim, int64_t seq_len, float eps,
-                                        hipStream_t stream);
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *weight,
+                                                    const float *cos_tab, const float *sin_tab,
+                                                    int64_t rows, int64_t hidden, int32_t heads,
+                                                    int32_t head_dim, int64_t seq_len, float eps,
+                                                    hipStream_t stream);
+
+/* ltxnorm_rmsnorm_rope_fwd for any ltxnorm_dtype; head_dim a multiple of 16
+ * (bf16, fp16) or 8 (fp32). */
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd_dt(void *out, const void *x,
+                                                       const void *weight, const float *cos_tab,
+                                                       const float *sin_tab, int64_t rows,
+                                                       int64_t hidden, int32_t heads,
+                                                       int32_t head_dim, int64_t seq_len,
+                                                       float eps, ltxnorm_dtype dtype,
+                                                       hipStream_t stream);
 
 /*
  * Fused RMSNorm over the full row, then RoPE per head on adjacent pairs.
@@ -123,13 +156,17 @@ ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *we
  * Arguments, layouts, ownership and errors as for ltxnorm_rmsnorm_rope_fwd,
  * except that head_dim need only be a multiple of 8.
  */
-ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void *out, const void *x,
-                                                    const void *weight,
-                                                    const float *cos_tab,
-                                                    const float *sin_tab, int64_t rows,
-                                                    int64_t hidden, int32_t heads,
-                                                    int32_t head_dim, int64_t seq_len,
-                                                    float eps, hipStream_t stream);
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(
+    void *out, const void *x, const void *weight, const float *cos_tab, const float *sin_tab,
+    int64_t rows, int64_t hidden, int32_t heads, int32_t head_dim, int64_t seq_len, float eps,
+    hipStream_t stream);
+
+/* ltxnorm_rmsnorm_rope_interleaved_fwd for any ltxnorm_dtype; head_dim a
+ * multiple of 8 (bf16, fp16) or 4 (fp32). */
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd_dt(
+    void *out, const void *x, const void *weight, const float *cos_tab, const float *sin_tab,
+    int64_t rows, int64_t hidden, int32_t heads, int32_t head_dim, int64_t seq_len, float eps,
+    ltxnorm_dtype dtype, hipStream_t stream);
 
 /*
  * RMSNorm with per-sample adaptive modulation (AdaLN, as used in DiT blocks
@@ -148,17 +185,26 @@ ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(void *out, const void *x,
  *   rows_per_sample  rows sharing one modulation row (S for [B, S, H] x);
  *           >= 1, else LTXNORM_ERR_SHAPE.
  */
-ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void *out, const void *x, const void *weight,
-                                         const void *scale, const void *shift,
-                                         int64_t rows, int64_t hidden,
-                                         int64_t rows_per_sample, float eps,
-                                         hipStream_t stream);
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void *out, const void *x,
+                                                     const void *weight, const void *scale,
+                                                     const void *shift, int64_t rows,
+                                                     int64_t hidden, int64_t rows_per_sample,
+                                                     float eps, hipStream_t stream);
+
+/* ltxnorm_rmsnorm_adaln_fwd for any ltxnorm_dtype (scale and shift in the
+ * same dtype as x). */
+LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd_dt(void *out, const void *x,
+                                                        const void *weight, const void *scale,
+                                                        const void *shift, int64_t rows,
+                                                        int64_t hidden, int64_t rows_per_sample,
+                                                        float eps, ltxnorm_dtype dtype,
+                                                        hipStream_t stream);
 
 /* Static, never-NULL description of a status code (unknown codes included). */
-const char *ltxnorm_status_str(ltxnorm_status s);
+LTXNORM_API const char *ltxnorm_status_str(ltxnorm_status s);
 
 /* LTXNORM_ABI_VERSION of the built library. */
-int ltxnorm_version(void);
+LTXNORM_API int ltxnorm_version(void);
 
 #ifdef __cplusplus
 }

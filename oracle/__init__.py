@@ -5,8 +5,10 @@ and the benchmark's CPU-baseline leg may import this package.  It shares no
 code with the HIP library ``rmsnorm_video_dit_amd`` and never imports it.
 
 The arithmetic lives in ``oracle.c`` (plain C, IEEE double, built with gcc);
-this module only marshals numpy arrays into it.  bf16 tensors travel as
-``numpy.uint16`` bit patterns.
+this module only marshals numpy arrays into it.  The input type follows the
+numpy dtype: ``uint16`` arrays are bf16 bit patterns, ``float16`` arrays are
+IEEE binary16 and ``float32`` arrays IEEE binary32 (the three precisions of
+the skill page's "Supported Data Types").
 
 What is computed, and the reading of the pages behind it, is documented at the
 top of ``oracle.c``: RMSNorm per the Hugging Face cuda-kernels skill page
@@ -49,21 +51,55 @@ def build(src: str = _SRC, out: str = _LIB) -> str:
     return out
 
 
+BF16, F16, F32 = 0, 1, 2
+_NAMES = {"bf16": BF16, "f16": F16, "f32": F32}
+
+
+def dtype_of(a: np.ndarray) -> int:
+    """Oracle type code of an input array: uint16 = bf16 bit patterns,
+    float16 = binary16, float32 = binary32."""
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float16:
+        return F16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"unsupported input dtype {a.dtype}: use uint16 (bf16 bits), float16 or float32")
+
+
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
     i32 = ctypes.c_int32
-    lib.oracle_rmsnorm.argtypes = [p, p, p, i64, i64, ctypes.c_float]
-    lib.oracle_rmsnorm.restype = ctypes.c_int
-    lib.oracle_rmsnorm_rope.argtypes = [p, p, p, p, p, p, i64, i64, i32, i32,
-                                        i64, ctypes.c_float]
-    lib.oracle_rmsnorm_rope.restype = ctypes.c_int
-    lib.oracle_rmsnorm_rope_interleaved.argtypes = list(lib.oracle_rmsnorm_rope.argtypes)
-    lib.oracle_rmsnorm_rope_interleaved.restype = ctypes.c_int
-    lib.oracle_rmsnorm_adaln.argtypes = [p, p, p, p, p, p, i64, i64, i64, ctypes.c_float]
-    lib.oracle_rmsnorm_adaln.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    c_int = ctypes.c_int
+    lib.oracle_rmsnorm.argtypes = [p, p, p, i64, i64, f32]
+    lib.oracle_rmsnorm.restype = c_int
+    lib.oracle_rmsnorm_dt.argtypes = [p, p, p, i64, i64, f32, c_int]
+    lib.oracle_rmsnorm_dt.restype = c_int
+    rope = [p, p, p, p, p, p, i64, i64, i32, i32, i64, f32]
+    lib.oracle_rmsnorm_rope.argtypes = rope
+    lib.oracle_rmsnorm_rope.restype = c_int
+    lib.oracle_rmsnorm_rope_dt.argtypes = rope + [c_int]
+    lib.oracle_rmsnorm_rope_dt.restype = c_int
+    lib.oracle_rmsnorm_rope_interleaved.argtypes = rope
+    lib.oracle_rmsnorm_rope_interleaved.restype = c_int
+    lib.oracle_rmsnorm_rope_interleaved_dt.argtypes = rope + [c_int]
+    lib.oracle_rmsnorm_rope_interleaved_dt.restype = c_int
+    lib.oracle_rmsnorm_adaln.argtypes = [p, p, p, p, p, p, i64, i64, i64, f32]
+    lib.oracle_rmsnorm_adaln.restype = c_int
+    lib.oracle_rmsnorm_adaln_dt.argtypes = [p, p, p, p, p, p, i64, i64, i64, f32, c_int]
+    lib.oracle_rmsnorm_adaln_dt.restype = c_int
     lib.oracle_round.argtypes = [p, i64, p, p]
     lib.oracle_round.restype = None
+    lib.oracle_round_dt.argtypes = [p, i64, p, p, c_int]
+    lib.oracle_round_dt.restype = None
+    lib.oracle_f16_from_f32.argtypes = [f32]
+    lib.oracle_f16_from_f32.restype = ctypes.c_uint16
+    lib.oracle_decode.argtypes = [p, i64, c_int, p]
+    lib.oracle_decode.restype = None
+    lib.oracle_f16_array.argtypes = [p, i64, p]
+    lib.oracle_f16_array.restype = None
     lib.oracle_bf16_from_f32.argtypes = [ctypes.c_float]
     lib.oracle_bf16_from_f32.restype = ctypes.c_uint16
     lib.oracle_bf16_array.argtypes = [p, i64, p]
@@ -88,10 +124,13 @@ def _ptr(a: np.ndarray | None):
     return None if a is None else ctypes.c_void_p(a.ctypes.data)
 
 
-def _u16(a, name):
+def _same(a, dt, name):
+    """Contiguous array of the input type `dt` (None passes through)."""
+    if a is None:
+        return None
     a = np.ascontiguousarray(a)
-    if a.dtype != np.uint16:
-        raise TypeError(f"{name} must hold bf16 bit patterns as uint16, got {a.dtype}")
+    if dtype_of(a) != dt:
+        raise TypeError(f"{name} must have the dtype of x, got {a.dtype}")
     return a
 
 
@@ -103,17 +142,18 @@ class Oracle:
         self.lib = lib if lib is not None else load()
 
     def rmsnorm(self, x, w, eps: float = 1e-6) -> np.ndarray:
-        """RMSNorm of bf16 ``x[..., H]`` with bf16 weight ``w[H]`` (or None);
-        returns the double result with the shape of ``x``."""
-        x = _u16(x, "x")
+        """RMSNorm of ``x[..., H]`` with weight ``w[H]`` of the same type (or
+        None); returns the double result with the shape of ``x``."""
+        x = np.ascontiguousarray(x)
+        dt = dtype_of(x)
         hidden = x.shape[-1]
         rows = x.size // hidden if hidden else 0
+        w = _same(w, dt, "w")
         if w is not None:
-            w = _u16(w, "w")
             assert w.shape == (hidden,)
         y = np.empty(x.shape, dtype=np.float64)
-        rc = self.lib.oracle_rmsnorm(_ptr(y), _ptr(x), _ptr(w), rows, hidden,
-                                     ctypes.c_float(eps))
+        rc = self.lib.oracle_rmsnorm_dt(_ptr(y), _ptr(x), _ptr(w), rows, hidden,
+                                        ctypes.c_float(eps), dt)
         if rc != 0:
             raise ValueError("oracle_rmsnorm rejected its arguments")
         return y
@@ -128,11 +168,11 @@ class Oracle:
         Returns the double result, and with ``with_mag`` also the per-output
         magnitude sum |a*c| + |b*s| that bounds its cancellation.
         """
-        x = _u16(x, "x")
+        x = np.ascontiguousarray(x)
+        dt = dtype_of(x)
         hidden = x.shape[-1]
         rows = x.size // hidden if hidden else 0
-        if w is not None:
-            w = _u16(w, "w")
+        w = _same(w, dt, "w")
         cos_tab = np.ascontiguousarray(cos_tab, dtype=np.float32)
         sin_tab = np.ascontiguousarray(sin_tab, dtype=np.float32)
         if cos_tab.ndim != 2 or cos_tab.shape != sin_tab.shape or cos_tab.shape[1] != head_dim // 2:
@@ -140,9 +180,10 @@ class Oracle:
         seq_len = cos_tab.shape[0]
         y = np.empty(x.shape, dtype=np.float64)
         mag = np.empty(x.shape, dtype=np.float64) if with_mag else None
-        fn = self.lib.oracle_rmsnorm_rope_interleaved if interleaved else self.lib.oracle_rmsnorm_rope
+        fn = (self.lib.oracle_rmsnorm_rope_interleaved_dt if interleaved
+              else self.lib.oracle_rmsnorm_rope_dt)
         rc = fn(_ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(cos_tab), _ptr(sin_tab),
-                rows, hidden, heads, head_dim, seq_len, ctypes.c_float(eps))
+                rows, hidden, heads, head_dim, seq_len, ctypes.c_float(eps), dt)
         if rc != 0:
             raise ValueError("oracle_rmsnorm_rope rejected its arguments")
         return (y, mag) if with_mag else y
@@ -153,33 +194,53 @@ class Oracle:
         b = row // rows_per_sample; scale/shift bf16 [samples, H] or None.
         With ``with_mag`` also returns |y * (1 + scale)| + |shift| per output,
         which bounds the cancellation of the final sum."""
-        x = _u16(x, "x")
+        x = np.ascontiguousarray(x)
+        dt = dtype_of(x)
         hidden = x.shape[-1]
         rows = x.size // hidden if hidden else 0
-        w = None if w is None else _u16(w, "w")
+        w = _same(w, dt, "w")
         samples = -(-rows // rows_per_sample) if rows else 0
         for t, n in ((scale, "scale"), (shift, "shift")):
             if t is not None and np.asarray(t).size != samples * hidden:
                 raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
-        scale = None if scale is None else _u16(scale, "scale")
-        shift = None if shift is None else _u16(shift, "shift")
+        scale = _same(scale, dt, "scale")
+        shift = _same(shift, dt, "shift")
         y = np.empty(x.shape, dtype=np.float64)
         mag = np.empty(x.shape, dtype=np.float64) if with_mag else None
-        rc = self.lib.oracle_rmsnorm_adaln(_ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(scale),
-                                           _ptr(shift), rows, hidden, rows_per_sample,
-                                           ctypes.c_float(eps))
+        rc = self.lib.oracle_rmsnorm_adaln_dt(_ptr(y), _ptr(mag), _ptr(x), _ptr(w), _ptr(scale),
+                                              _ptr(shift), rows, hidden, rows_per_sample,
+                                              ctypes.c_float(eps), dt)
         if rc != 0:
             raise ValueError("oracle_rmsnorm_adaln rejected its arguments")
         return (y, mag) if with_mag else y
 
-    def round(self, y: np.ndarray):
-        """Round double results once to binary32 (ref32) and that to bf16
-        (ref16, uint16 bit patterns), both round-to-nearest-even."""
+    def round(self, y: np.ndarray, out_dtype: str = "bf16"):
+        """Round double results once to binary32 (ref32) and that to the
+        output type, both round-to-nearest-even: bf16 bit patterns (uint16),
+        binary16 (float16 array) or binary32 (float32, equal to ref32)."""
         y = np.ascontiguousarray(y, dtype=np.float64)
+        dt = _NAMES[out_dtype]
         ref32 = np.empty(y.shape, dtype=np.float32)
-        ref16 = np.empty(y.shape, dtype=np.uint16)
-        self.lib.oracle_round(_ptr(y), y.size, _ptr(ref32), _ptr(ref16))
-        return ref32, ref16
+        ref = np.empty(y.shape, dtype={BF16: np.uint16, F16: np.uint16, F32: np.float32}[dt])
+        self.lib.oracle_round_dt(_ptr(y), y.size, _ptr(ref32), _ptr(ref), dt)
+        if dt == F16:
+            ref = ref.view(np.float16)
+        return ref32, ref
+
+    def decode(self, x: np.ndarray) -> np.ndarray:
+        """Values of an input array (bf16 bits, float16 or float32) as doubles."""
+        x = np.ascontiguousarray(x)
+        out = np.empty(x.shape, dtype=np.float64)
+        self.lib.oracle_decode(_ptr(x), x.size, dtype_of(x), _ptr(out))
+        return out
+
+    def f16_from_f32(self, f: np.ndarray) -> np.ndarray:
+        """Round binary32 values (any bit pattern) to binary16 bit patterns
+        (uint16) with the oracle's round-to-nearest-even."""
+        f = np.ascontiguousarray(f, dtype=np.float32)
+        out = np.empty(f.shape, dtype=np.uint16)
+        self.lib.oracle_f16_array(_ptr(f), f.size, _ptr(out))
+        return out
 
     def bf16_from_f32(self, f: np.ndarray) -> np.ndarray:
         """Round binary32 values (any bit pattern, NaNs included) to bf16 bit

@@ -14,6 +14,7 @@ The low-level functions keep the C names and argument order:
     ltxnorm_rmsnorm_rope_interleaved_fwd(... same arguments ...)
     ltxnorm_rmsnorm_adaln_fwd(out, x, weight, scale, shift, rows, hidden,
                               rows_per_sample, eps, stream)
+    and a ``_dt`` twin of each taking ``dtype`` (BF16, F16 or F32) before stream
     ltxnorm_status_str(status), ltxnorm_version()
 
 Pointer arguments accept a torch tensor, an integer address or None; ``stream``
@@ -22,7 +23,7 @@ current stream.  A non-OK status raises ``LtxnormError``.
 
 ``rmsnorm(x, weight=None, eps=1e-6, out=None)``, ``rmsnorm_rope(...)`` and
 ``rmsnorm_adaln(...)`` are the tensor-level forms (functional, or out-variant
-when ``out`` is given).
+when ``out`` is given); they take bfloat16, float16 or float32 tensors.
 """
 from __future__ import annotations
 
@@ -32,7 +33,9 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libltxnorm.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_ALIAS, ERR_VALUE, ERR_HIP = range(8)
+BF16, F16, F32 = 0, 1, 2
 MAX_HIDDEN = 65536
+MAX_HIDDEN_F32 = 32768
 
 _lib = None
 
@@ -62,6 +65,13 @@ def lib() -> ctypes.CDLL:
         L.ltxnorm_rmsnorm_rope_interleaved_fwd.restype = ctypes.c_int
         L.ltxnorm_rmsnorm_adaln_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, f32, p]
         L.ltxnorm_rmsnorm_adaln_fwd.restype = ctypes.c_int
+        c_int = ctypes.c_int
+        for name in ("ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
+                     "ltxnorm_rmsnorm_rope_interleaved_fwd", "ltxnorm_rmsnorm_adaln_fwd"):
+            base = getattr(L, name)
+            twin = getattr(L, name + "_dt")
+            twin.argtypes = list(base.argtypes[:-1]) + [c_int, p]
+            twin.restype = ctypes.c_int
         L.ltxnorm_status_str.argtypes = [ctypes.c_int]
         L.ltxnorm_status_str.restype = ctypes.c_char_p
         L.ltxnorm_version.argtypes = []
@@ -99,6 +109,68 @@ def ltxnorm_rmsnorm_fwd_status(out, x, weight, rows, hidden, eps, stream) -> int
     """Same call, returning the raw status code instead of raising."""
     return lib().ltxnorm_rmsnorm_fwd(_addr(out), _addr(x), _addr(weight), int(rows), int(hidden),
                                      float(eps), _stream(stream))
+
+
+def ltxnorm_rmsnorm_fwd_dt_status(out, x, weight, rows, hidden, eps, dtype, stream) -> int:
+    return lib().ltxnorm_rmsnorm_fwd_dt(_addr(out), _addr(x), _addr(weight), int(rows),
+                                        int(hidden), float(eps), int(dtype), _stream(stream))
+
+
+def ltxnorm_rmsnorm_rope_fwd_dt_status(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                       head_dim, seq_len, eps, dtype, stream) -> int:
+    return lib().ltxnorm_rmsnorm_rope_fwd_dt(_addr(out), _addr(x), _addr(weight), _addr(cos_tab),
+                                             _addr(sin_tab), int(rows), int(hidden), int(heads),
+                                             int(head_dim), int(seq_len), float(eps), int(dtype),
+                                             _stream(stream))
+
+
+def ltxnorm_rmsnorm_rope_interleaved_fwd_dt_status(out, x, weight, cos_tab, sin_tab, rows, hidden,
+                                                   heads, head_dim, seq_len, eps, dtype,
+                                                   stream) -> int:
+    return lib().ltxnorm_rmsnorm_rope_interleaved_fwd_dt(
+        _addr(out), _addr(x), _addr(weight), _addr(cos_tab), _addr(sin_tab), int(rows),
+        int(hidden), int(heads), int(head_dim), int(seq_len), float(eps), int(dtype),
+        _stream(stream))
+
+
+def ltxnorm_rmsnorm_adaln_fwd_dt_status(out, x, weight, scale, shift, rows, hidden,
+                                        rows_per_sample, eps, dtype, stream) -> int:
+    return lib().ltxnorm_rmsnorm_adaln_fwd_dt(_addr(out), _addr(x), _addr(weight), _addr(scale),
+                                              _addr(shift), int(rows), int(hidden),
+                                              int(rows_per_sample), float(eps), int(dtype),
+                                              _stream(stream))
+
+
+def _raise_if(st, where):
+    if st != OK:
+        raise LtxnormError(st, where)
+
+
+def ltxnorm_rmsnorm_fwd_dt(out, x, weight, rows, hidden, eps, dtype, stream=None) -> None:
+    _raise_if(ltxnorm_rmsnorm_fwd_dt_status(out, x, weight, rows, hidden, eps, dtype, stream),
+              "ltxnorm_rmsnorm_fwd_dt")
+
+
+def ltxnorm_rmsnorm_rope_fwd_dt(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim,
+                                seq_len, eps, dtype, stream=None) -> None:
+    _raise_if(ltxnorm_rmsnorm_rope_fwd_dt_status(out, x, weight, cos_tab, sin_tab, rows, hidden,
+                                                 heads, head_dim, seq_len, eps, dtype, stream),
+              "ltxnorm_rmsnorm_rope_fwd_dt")
+
+
+def ltxnorm_rmsnorm_rope_interleaved_fwd_dt(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
+                                            head_dim, seq_len, eps, dtype, stream=None) -> None:
+    _raise_if(ltxnorm_rmsnorm_rope_interleaved_fwd_dt_status(out, x, weight, cos_tab, sin_tab,
+                                                             rows, hidden, heads, head_dim,
+                                                             seq_len, eps, dtype, stream),
+              "ltxnorm_rmsnorm_rope_interleaved_fwd_dt")
+
+
+def ltxnorm_rmsnorm_adaln_fwd_dt(out, x, weight, scale, shift, rows, hidden, rows_per_sample, eps,
+                                 dtype, stream=None) -> None:
+    _raise_if(ltxnorm_rmsnorm_adaln_fwd_dt_status(out, x, weight, scale, shift, rows, hidden,
+                                                  rows_per_sample, eps, dtype, stream),
+              "ltxnorm_rmsnorm_adaln_fwd_dt")
 
 
 def ltxnorm_rmsnorm_rope_fwd_status(out, x, weight, cos_tab, sin_tab, rows, hidden, heads,
@@ -152,31 +224,40 @@ def ltxnorm_rmsnorm_rope_interleaved_fwd(out, x, weight, cos_tab, sin_tab, rows,
         raise LtxnormError(st, "ltxnorm_rmsnorm_rope_interleaved_fwd")
 
 
-def _check_act(x, name):
+def _dtype_code(t):
     import torch
+    codes = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16, float16 or float32")
+    return codes[t.dtype]
+
+
+def _check_act(x, name, like=None):
     if not x.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (no host path exists)")
-    if x.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    _dtype_code(x)
+    if like is not None and x.dtype != like.dtype:
+        raise TypeError(f"{name} must have the dtype of x ({like.dtype}), got {x.dtype}")
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
 def rmsnorm(x, weight=None, eps: float = 1e-6, out=None):
-    """RMSNorm over the last dimension of bf16 ``x`` (weight bf16 [H] or None)."""
+    """RMSNorm over the last dimension of ``x`` (bf16, fp16 or fp32; weight
+    [H] of the same dtype, or None)."""
     import torch
     _check_act(x, "x")
     if weight is not None:
-        _check_act(weight, "weight")
+        _check_act(weight, "weight", x)
     hidden = x.shape[-1]
     if out is None:
         out = torch.empty_like(x)
     else:
-        _check_act(out, "out")
+        _check_act(out, "out", x)
         if out.shape != x.shape:
             raise ValueError("out must have the shape of x")
     rows = x.numel() // hidden if hidden else 0
-    ltxnorm_rmsnorm_fwd(out, x, weight, rows, hidden, eps, None)
+    ltxnorm_rmsnorm_fwd_dt(out, x, weight, rows, hidden, eps, _dtype_code(x), None)
     return out
 
 
@@ -188,7 +269,7 @@ def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: fl
     import torch
     _check_act(x, "x")
     if weight is not None:
-        _check_act(weight, "weight")
+        _check_act(weight, "weight", x)
     for t, n in ((cos_tab, "cos_tab"), (sin_tab, "sin_tab")):
         if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous float32 GPU tensor")
@@ -198,12 +279,13 @@ def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: fl
     if out is None:
         out = torch.empty_like(x)
     else:
-        _check_act(out, "out")
+        _check_act(out, "out", x)
         if out.shape != x.shape:
             raise ValueError("out must have the shape of x")
     rows = x.numel() // hidden if hidden else 0
-    fn = ltxnorm_rmsnorm_rope_interleaved_fwd if interleaved else ltxnorm_rmsnorm_rope_fwd
-    fn(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim, cos_tab.shape[0], eps, None)
+    fn = ltxnorm_rmsnorm_rope_interleaved_fwd_dt if interleaved else ltxnorm_rmsnorm_rope_fwd_dt
+    fn(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim, cos_tab.shape[0], eps,
+       _dtype_code(x), None)
     return out
 
 
@@ -217,7 +299,7 @@ def rmsnorm_adaln(x, weight, scale, shift, eps: float = 1e-6, out=None, rows_per
     _check_act(x, "x")
     for t, n in ((weight, "weight"), (scale, "scale"), (shift, "shift")):
         if t is not None:
-            _check_act(t, n)
+            _check_act(t, n, x)
     hidden = x.shape[-1]
     rows = x.numel() // hidden if hidden else 0
     if rows_per_sample is None:
@@ -227,13 +309,13 @@ def rmsnorm_adaln(x, weight, scale, shift, eps: float = 1e-6, out=None, rows_per
     if out is None:
         out = torch.empty_like(x)
     else:
-        _check_act(out, "out")
+        _check_act(out, "out", x)
         if out.shape != x.shape:
             raise ValueError("out must have the shape of x")
     samples = -(-rows // rows_per_sample) if rows else 0
     for t, n in ((scale, "scale"), (shift, "shift")):
         if t is not None and t.numel() != samples * hidden:
             raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
-    ltxnorm_rmsnorm_adaln_fwd(out, x, weight, scale, shift, rows, hidden, max(rows_per_sample, 1),
-                              eps, None)
+    ltxnorm_rmsnorm_adaln_fwd_dt(out, x, weight, scale, shift, rows, hidden,
+                                 max(rows_per_sample, 1), eps, _dtype_code(x), None)
     return out

@@ -543,6 +543,101 @@ def pin_round_twice(o):
     assert list(ref16) == [0x3F80, 0x3F82, 0x3F81, 0x3F80, 0x4000, 0xBFC1, 0xBFC0, 0x0000]
 
 
+# --------------------------------------------------------------------------
+# fp16 and fp32 inputs ("Supported Data Types" on the skill page)
+# --------------------------------------------------------------------------
+
+def pin_f16_decode_all_patterns(o):
+    """Every binary16 bit pattern decodes to numpy's float16 value."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = o.decode(bits.view(np.float16))
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_f16_encode(o):
+    """binary32 -> binary16 round-to-nearest-even against numpy's
+    float32 -> float16 conversion: random values over the whole range,
+    exact ties between neighbours (normal and subnormal), the overflow edge
+    and the subnormal/normal boundary."""
+    rng = np.random.default_rng(101)
+    r = rng.standard_normal(200000).astype(np.float32) * np.exp2(
+        rng.uniform(-30, 17, 200000)).astype(np.float32)
+    neigh = np.arange(0, 0x7C00, 7, dtype=np.uint16).view(np.float16).astype(np.float32)
+    nxt = (np.arange(0, 0x7C00, 7, dtype=np.uint16) + 1).view(np.float16).astype(np.float32)
+    ties = ((neigh.astype(np.float64) + nxt.astype(np.float64)) / 2).astype(np.float32)
+    edges = np.array([65504, 65519.99, 65520, 65536, 1e9, 6.1035156e-05, 6.0975552e-05,
+                      2 ** -24, 2 ** -25, 2 ** -25 * 1.0001, 3 * 2 ** -26, 0.0, np.inf],
+                     dtype=np.float32)
+    f = np.concatenate([r, ties, -ties, edges, -edges])
+    got = o.f16_from_f32(f)
+    with np.errstate(over="ignore"):
+        want = f.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), f[got != want][:5]
+    nan = o.f16_from_f32(np.array([np.nan, -np.nan], dtype=np.float32))
+    assert np.all((nan & 0x7C00) == 0x7C00) and np.all((nan & 0x3FF) != 0) and np.all(nan & 0x200)
+
+
+def pin_lowp_constant_rows(o):
+    """Constant rows in fp16 and fp32 with eps = 0 normalise to exactly
+    sign(c), so the output equals sign(c) * w in the input type."""
+    rng = np.random.default_rng(103)
+    for dt in (np.float16, np.float32):
+        w = rng.uniform(0.5, 1.5, 40).astype(dt)
+        for c in (0.375, -2.0, 1000.0):
+            x = np.full((2, 40), c, dtype=dt)
+            y = o.rmsnorm(x, w, 0.0)
+            assert np.array_equal(y, np.sign(c) * np.broadcast_to(w.astype(np.float64), y.shape)), (dt, c)
+
+
+def pin_lowp_brute_force(o):
+    """fp16 and fp32 rows against exact fractions / 60-digit decimals, and
+    the rounded outputs against the exact value rounded by numpy."""
+    rng = np.random.default_rng(107)
+    for dt, name in ((np.float16, "f16"), (np.float32, "f32")):
+        for hidden in (1, 3, 16, 48):
+            x = (rng.standard_normal((3, hidden)) * np.exp2(rng.uniform(-6, 6, (3, hidden)))).astype(dt)
+            w = rng.uniform(0.5, 1.5, hidden).astype(dt)
+            y = o.rmsnorm(x, w, 1e-6)
+            ref32, ref = o.round(y, name)
+            for r in range(3):
+                exact = _exact_rms_row(x[r].astype(np.float64), w.astype(np.float64), EPS32)
+                for j in range(hidden):
+                    e = exact[j]
+                    tol = Decimal((hidden + 8) * 2.0 ** -53) * abs(e)
+                    assert abs(Decimal(y[r, j]) - e) <= tol, (name, hidden, r, j)
+            assert np.array_equal(ref, ref32.astype(dt)) or name == "f16"
+            if name == "f16":
+                assert np.array_equal(ref.view(np.uint16), ref32.astype(np.float16).view(np.uint16))
+
+
+def pin_lowp_rope_matches_widened_bf16_path(o):
+    """The same values given as fp32, fp16 or bf16 inputs (all exactly
+    representable) give identical double results for every operation."""
+    rng = np.random.default_rng(109)
+    heads, d = 2, 16
+    xb = _rand_bf16(rng, (5, heads * d))
+    wb = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+    # bf16 values with |x| in a range fp16 also holds exactly (8 significant bits)
+    xb = datagen.to_bf16_bits(np.clip(_val(xb), -60000, 60000))
+    xv, wv = _val(xb), _val(wb)
+    assert np.all(xv.astype(np.float16).astype(np.float64) == xv)
+    c, s = _tables([3, 5, 7, 9, 11], d)
+    for conv in (np.float32, np.float16):
+        xc, wc = xv.astype(conv), wv.astype(conv)
+        assert np.array_equal(o.rmsnorm(xc, wc, 1e-6), o.rmsnorm(xb, wb, 1e-6))
+        for il in (False, True):
+            assert np.array_equal(o.rmsnorm_rope(xc, wc, c, s, heads, d, 1e-6, interleaved=il),
+                                  o.rmsnorm_rope(xb, wb, c, s, heads, d, 1e-6, interleaved=il))
+        sc = _rand_bf16(rng, (1, heads * d), scale=0.3)
+        sh = _rand_bf16(rng, (1, heads * d), scale=0.3)
+        assert np.array_equal(o.rmsnorm_adaln(xc, wc, _val(sc).astype(conv), _val(sh).astype(conv), 5),
+                              o.rmsnorm_adaln(xb, wb, sc, sh, 5))
+
+
 PINS = [
     pin_eps_inside_root, pin_constant_row_gives_weight, pin_constant_row_small_value,
     pin_zero_row, pin_scale_invariance, pin_sign_symmetry, pin_textbook_norm,
@@ -554,4 +649,6 @@ PINS = [
     pin_adaln_zero_modulation_is_rmsnorm, pin_adaln_scale_minus_one_gives_shift,
     pin_adaln_exact_closed_form, pin_adaln_sample_rows, pin_adaln_brute_force, pin_adaln_mag,
     pin_bf16_rounding, pin_round_twice,
+    pin_f16_decode_all_patterns, pin_f16_encode, pin_lowp_constant_rows, pin_lowp_brute_force,
+    pin_lowp_rope_matches_widened_bf16_path,
 ]

@@ -1,4 +1,5 @@
-"""Element-wise comparison of bf16 kernel output with the oracle.
+"""Element-wise comparison of kernel output with the oracle, for bf16, fp16
+and fp32 outputs.
 
 Rule, per element: |gpu - ref16| <= max(ulp16(ref16), 2^-16 * m), where
 ref16 is the oracle's binary32 result rounded to bf16 (nearest-even),
@@ -7,7 +8,15 @@ smallest subnormal spacing 2^-133 for v = 0 or subnormal v, so zeros must
 match up to sign), and m is the oracle's magnitude sum of the two terms an
 output is the sum of: |a c| + |b s| for a rotated output, |n (1 + scale)| +
 |shift| for a modulated one, m = 0 for plain RMSNorm.  The floor term only
-binds where those two terms cancel more than ~8 bits.  NaN must meet NaN.  This is the "1 bf16 ulp against the oracle's binary32 result
+binds where those two terms cancel more than ~8 bits.  NaN must meet NaN.
+
+fp16 outputs use the same rule with the binary16 spacing 2^(floor(log2|v|)
+- 10) (2^-24 for subnormals).  fp32 outputs are the kernel's own binary32
+result, so the bound is the evaluation error itself: |gpu - ref32| <=
+2^-18 * (|ref32| + m), twice the worst-case bound of the binary32
+evaluation (about 32 units of 2^-24 from up to 32 per-lane terms, a 6-level
+tree and up to 16 cross-wavefront partial sums, halved by the root, plus a
+few roundings).  This is the "1 bf16 ulp against the oracle's binary32 result
 rounded to bf16" bar; the derivation of the floor is in the design notes.
 """
 from __future__ import annotations
@@ -26,6 +35,52 @@ def ulp16(v: np.ndarray) -> np.ndarray:
     _, e = np.frexp(np.abs(v))
     u = np.ldexp(1.0, e - 8)
     return np.maximum(u, MIN_ULP)
+
+
+def ulp_f16(v: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(v))
+    return np.maximum(np.ldexp(1.0, e - 11), 2.0 ** -24)
+
+
+def compare(got, ref, mag=None, ref32=None) -> dict:
+    """Compare kernel output `got` with the oracle's rounded output `ref`:
+    uint16 arrays are bf16 bit patterns, float16 and float32 arrays values."""
+    ref = np.asarray(ref)
+    if ref.dtype == np.uint16:
+        return compare_bf16(got, ref, mag, ref32)
+    got = np.asarray(got, dtype=ref.dtype).reshape(-1)
+    ref = ref.reshape(-1)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    m = np.zeros_like(r) if mag is None else np.asarray(mag, dtype=np.float64).reshape(-1)
+    gnan, rnan = np.isnan(g), np.isnan(r)
+    both = ~(gnan | rnan)
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both & (g != r), np.abs(g - r), 0.0)  # inf == inf is a match
+    if ref.dtype == np.float16:
+        u = ulp_f16(np.where(both, r, 1.0))
+        tol = np.maximum(u, FLOOR * m)
+    else:
+        u = np.maximum(np.abs(np.spacing(np.where(both, r, 1.0).astype(np.float32))).astype(np.float64),
+                       2.0 ** -149)
+        tol = 2.0 ** -18 * (np.abs(np.where(both, r, 0.0)) + m)
+        tol = np.maximum(tol, 2.0 ** -149)
+    bad = (diff > tol) | (gnan != rnan)
+    # elements that pass only thanks to the magnitude term m
+    own = u if ref.dtype == np.float16 else 2.0 ** -18 * np.abs(np.where(both, r, 0.0))
+    rep = {"n": int(g.size), "pass": bool(not bad.any()), "n_bad": int(bad.sum()),
+           "n_exact": int((g == r).sum() + (gnan & rnan).sum()),
+           "max_ulp": float((diff / u).max()) if diff.size else 0.0,
+           "n_floor_bound": int(((diff > own) & (diff <= tol)).sum())}
+    if ref32 is not None:
+        r32 = np.asarray(ref32, dtype=np.float32).reshape(-1).astype(np.float64)
+        ok = both & ~np.isnan(r32) & np.isfinite(g)
+        rep["max_abs_err"] = float(np.abs(g[ok] - r32[ok]).max()) if ok.any() else 0.0
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        rep["first_bad"] = {"index": i, "got": float(g[i]), "ref": float(r[i]), "tol": float(tol[i])}
+    return rep
 
 
 def compare_bf16(got_bits, ref16, mag=None, ref32=None) -> dict:

@@ -28,10 +28,10 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["ltxnorm_rmsnorm_adaln_fwd", "ltxnorm_rmsnorm_fwd",
-                                    "ltxnorm_rmsnorm_rope_fwd",
-                                    "ltxnorm_rmsnorm_rope_interleaved_fwd",
-                                    "ltxnorm_status_str", "ltxnorm_version"]
+    ops = ["ltxnorm_rmsnorm_adaln_fwd", "ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
+           "ltxnorm_rmsnorm_rope_interleaved_fwd"]
+    assert declared_functions() == sorted(ops + [o + "_dt" for o in ops] +
+                                          ["ltxnorm_status_str", "ltxnorm_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,7 +51,7 @@ def test_library_targets_gfx950_only():
 
 
 def test_version_and_status_strings():
-    assert ltx.ltxnorm_version() == 1
+    assert ltx.ltxnorm_version() == 2
     seen = set()
     for code in range(8):
         s = ltx.ltxnorm_status_str(code)
@@ -164,11 +164,58 @@ def test_adaln_validation(kw, status):
     assert st == status
 
 
+# (dtype, hidden) -> status; only shapes the library rejects (a valid call
+# would launch)
+@pytest.mark.parametrize("dtype,hidden,status", [
+    (3, 2048, ltx.ERR_UNSUPPORTED),             # unknown dtype
+    (-1, 2048, ltx.ERR_UNSUPPORTED),
+    (ltx.F16, 2044, ltx.ERR_UNSUPPORTED),        # fp16: 8 per vector
+    (ltx.F32, 2042, ltx.ERR_UNSUPPORTED),        # fp32: 4 per vector
+    (ltx.F32, 32772, ltx.ERR_UNSUPPORTED),       # fp32 cap 32768
+    (ltx.F16, 65544, ltx.ERR_UNSUPPORTED),       # fp16 cap 65536
+    (ltx.F32, 0, ltx.ERR_SHAPE),
+])
+def test_dtype_validation(dtype, hidden, status):
+    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A, A + 64 * MB, None, 4, hidden, 1e-6, dtype, 0) == status
+    assert ltx.ltxnorm_rmsnorm_adaln_fwd_dt_status(A, A + 64 * MB, None, None, None, 4, hidden, 2,
+                                                   1e-6, dtype, 0) == status
+
+
+def test_dtype_shapes_that_pass_validation():
+    """fp32 rows of 4k elements and fp16 rows of 8k are accepted: shown by
+    making only the alignment wrong."""
+    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 2052, 1e-6, ltx.F32, 0) == ltx.ERR_ALIGN
+    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 32768, 1e-6, ltx.F32, 0) == ltx.ERR_ALIGN
+    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 2056, 1e-6, ltx.F16, 0) == ltx.ERR_ALIGN
+
+
+@pytest.mark.parametrize("dtype,interleaved,head_dim,status", [
+    (ltx.F32, False, 8, ltx.ERR_ALIGN),      # fp32 rotate-half: head_dim % 8
+    (ltx.F32, False, 12, ltx.ERR_SHAPE),
+    (ltx.F32, True, 4, ltx.ERR_ALIGN),       # fp32 interleaved: head_dim % 4
+    (ltx.F32, True, 6, ltx.ERR_SHAPE),
+    (ltx.F16, False, 16, ltx.ERR_ALIGN),
+    (ltx.F16, False, 8, ltx.ERR_SHAPE),
+    (ltx.F16, True, 8, ltx.ERR_ALIGN),
+    (ltx.F16, True, 12, ltx.ERR_SHAPE),
+])
+def test_rope_dtype_head_dim_rules(dtype, interleaved, head_dim, status):
+    """ERR_ALIGN means the shape passed (out is deliberately misaligned)."""
+    heads = 24
+    fn = (ltx.ltxnorm_rmsnorm_rope_interleaved_fwd_dt_status if interleaved
+          else ltx.ltxnorm_rmsnorm_rope_fwd_dt_status)
+    st = fn(A + 2, A + 64 * MB, None, A + 128 * MB, A + 129 * MB, 4, heads * head_dim, heads,
+            head_dim, 16, 1e-6, dtype, 0)
+    assert st == status
+
+
 def test_python_front_end_refuses_host_tensors():
     import torch
     x = torch.zeros(2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ltx.rmsnorm(x)
+    with pytest.raises(ValueError):
+        ltx.rmsnorm(x.to(torch.float16))
     with pytest.raises(ValueError):
         ltx.rmsnorm_rope(x, None, torch.zeros(4, 8), torch.zeros(4, 8), 4, 16)
 

@@ -22,9 +22,10 @@ MUTANTS = {
     "mean_over_hidden_minus_one": ("sum_sq / (double)hidden", "sum_sq / (double)(hidden > 1 ? hidden - 1 : 1)"),
     "eps_dropped": ("mean_sq + (double)eps", "mean_sq"),
     "square_dropped": ("sum_sq += v * v;", "sum_sq += fabs(v);"),
-    "weight_dropped": ("z[j] = bf16_value(x[j]) * rstd * wj;", "z[j] = bf16_value(x[j]) * rstd;"),
-    "weight_reversed": ("bf16_value(w[j])", "bf16_value(w[hidden - 1 - j])"),
-    "weight_none_zero": ("w ? bf16_value(w[j]) : 1.0", "w ? bf16_value(w[j]) : 0.5"),
+    "weight_dropped": ("z[j] = value_at(x, row * hidden + j, dtype) * rstd * wj;",
+                       "z[j] = value_at(x, row * hidden + j, dtype) * rstd;"),
+    "weight_reversed": ("value_at(w, j, dtype)", "value_at(w, hidden - 1 - j, dtype)"),
+    "weight_none_zero": ("w ? value_at(w, j, dtype) : 1.0", "w ? value_at(w, j, dtype) : 0.5"),
     "rope_sign_first": ("head[i] = a * c - b * s;", "head[i] = a * c + b * s;"),
     "rope_sign_second": ("head[i + half] = b * c + a * s;", "head[i + half] = b * c - a * s;"),
     "rope_cos_sin_swapped": ("double c = (double)cp[i];", "double c = (double)sp[i];"),
@@ -50,8 +51,16 @@ MUTANTS = {
     "adaln_shift_scaled": ("yr[j] = modulated + sh;", "yr[j] = modulated + sh * (1.0 + sc);"),
     "adaln_mag_signed": ("mag[r * hidden + j] = fabs(modulated) + fabs(sh);", "mag[r * hidden + j] = fabs(modulated + sh);"),
     "adaln_sample_mod": ("const int64_t b = r / rows_per_sample;", "const int64_t b = r % rows_per_sample % (rows / rows_per_sample > 0 ? rows / rows_per_sample : 1);"),
-    "adaln_scale_transposed": ("double sc = scale ? bf16_value(scale[b * hidden + j]) : 0.0;",
-                               "double sc = scale ? bf16_value(scale[b * hidden + (hidden - 1 - j)]) : 0.0;"),
+    "adaln_scale_transposed": ("double sc = scale ? value_at(scale, b * hidden + j, dtype) : 0.0;",
+                               "double sc = scale ? value_at(scale, b * hidden + (hidden - 1 - j), dtype) : 0.0;"),
+    "f16_bias_14": ("ldexp((double)(1024 + fraction), exponent - 25)", "ldexp((double)(1024 + fraction), exponent - 24)"),
+    "f16_subnormal_scale": ("v = ldexp((double)fraction, -24);", "v = ldexp((double)fraction, -25);"),
+    "f16_sign_dropped": ("return sign ? -v : v;", "return v;"),
+    "f16_overflow_at_max": ("if (a >= 65520.0)", "if (a >= 65504.0)"),
+    "f16_truncate": ("double units = nearbyint(ldexp(a, 10 - e));", "double units = floor(ldexp(a, 10 - e));"),
+    "f16_ties_away": ("double units = nearbyint(ldexp(a, 10 - e));", "double units = round(ldexp(a, 10 - e));"),
+    "f16_no_subnormal_floor": ("    if (a == 0.0 || e < -14)\n        e = -14;", "    if (a == 0.0)\n        e = -14;"),
+    "decode_f32_as_bf16": ("    return (double)((const float *)base)[i];", "    return bf16_value(((const uint16_t *)base)[i]);"),
     "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
     "bf16_truncate": ("kept += 1u;", "kept += 0u;"),
     "bf16_ties_odd": ("(kept & 1u))", "!(kept & 1u))"),
