@@ -16,15 +16,18 @@ MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
 the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
-scale/shift) under "adaln", and the CPU oracle timed on this host under
+scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
+"rms_f16" / "rms_f32", and the CPU oracle timed on this host under
 "cpu_baseline".  Prints one JSON line.
 
---probe rms|rope|ropei|adaln|copy runs a few launches only, for rocprofv3 counter passes.
+--probe rms|rms_f16|rms_f32|rope|ropei|adaln|copy runs a few launches only, for
+rocprofv3 counter passes.
 """
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import glob
 import hashlib
 import json
 import os
@@ -45,8 +48,11 @@ METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, RMSNorm 
 H100_GBPS_4x4096x3072 = 201_332_736 / 0.157e-3 / 1e9
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "ltxnorm.hip"),
-                  os.path.join(ROOT, "include", "ltxnorm.h")]
+KERNEL_SOURCES = (sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.hip")))
+                  + sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.h")))
+                  + [os.path.join(ROOT, "include", "ltxnorm.h")])
+DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
+ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
 def gbps(nbytes: float, seconds: float) -> float:
@@ -82,21 +88,28 @@ def read_traffic(kernel: str, workload: str):
     return None
 
 
-def to_device(bits, dev):
+def to_device(a, dev):
+    """bf16 bit patterns (uint16) become a bfloat16 tensor; float16/float32
+    arrays keep their type."""
     import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
 
 
 class Workload:
     """Rotating device buffers for one config, and the launch of one step."""
 
-    def __init__(self, cfg: datagen.Config, dev, stream, max_sets=None):
+    def __init__(self, cfg: datagen.Config, dev, stream, max_sets=None, dtype: str = "bf16"):
         import torch
         import rmsnorm_video_dit_amd as ltx
         self.cfg, self.ltx, self.stream = cfg, ltx, stream
-        inp = datagen.make_inputs(cfg)
+        self.dtype, self.code = dtype, DTYPE_CODE[dtype]
+        self.nbytes = cfg.algorithmic_bytes(ELEM_BYTES[dtype])
+        inp = datagen.make_inputs(cfg, dtype=dtype)
         self.host = inp
-        per_set = 2 * cfg.rows * cfg.hidden * 2
+        per_set = 2 * cfg.rows * cfg.hidden * ELEM_BYTES[dtype]
         n = max(2, -(-ROTATE_BYTES // per_set))
         if max_sets:
             n = min(n, max_sets)
@@ -117,16 +130,17 @@ class Workload:
         c = self.cfg
         k = i % self.nsets
         if c.adaln:
-            self.ltx.ltxnorm_rmsnorm_adaln_fwd(self.y[k], self.x[k], self.w, self.scale, self.shift,
-                                               c.rows, c.hidden, c.seq, c.eps, self.stream)
+            self.ltx.ltxnorm_rmsnorm_adaln_fwd_dt(self.y[k], self.x[k], self.w, self.scale,
+                                                  self.shift, c.rows, c.hidden, c.seq, c.eps,
+                                                  self.code, self.stream)
         elif c.rope:
-            fn = (self.ltx.ltxnorm_rmsnorm_rope_interleaved_fwd if c.interleaved
-                  else self.ltx.ltxnorm_rmsnorm_rope_fwd)
+            fn = (self.ltx.ltxnorm_rmsnorm_rope_interleaved_fwd_dt if c.interleaved
+                  else self.ltx.ltxnorm_rmsnorm_rope_fwd_dt)
             fn(self.y[k], self.x[k], self.w, self.cos, self.sin, c.rows, c.hidden, c.heads,
-               c.head_dim, c.seq, c.eps, self.stream)
+               c.head_dim, c.seq, c.eps, self.code, self.stream)
         else:
-            self.ltx.ltxnorm_rmsnorm_fwd(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
-                                         self.stream)
+            self.ltx.ltxnorm_rmsnorm_fwd_dt(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
+                                            self.code, self.stream)
 
     def time_steps(self, steps: int, warmup: int):
         """Warm up, then time exactly `steps` launches with HIP events on
@@ -197,14 +211,16 @@ def probe(kind: str, launches: int):
         print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = datagen.CONFIGS[{"rms": datagen.HEADLINE, "rope": datagen.ROPE,
+    cfg = datagen.CONFIGS[{"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE,
+                           "rms_f32": datagen.HEADLINE, "rope": datagen.ROPE,
                            "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN}[kind]]
-    wl = Workload(cfg, dev, s, max_sets=2)
+    dtype = kind[4:] if kind.startswith("rms_") else "bf16"
+    wl = Workload(cfg, dev, s, max_sets=2, dtype=dtype)
     for i in range(launches):
         wl.step(i)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": kind, "workload": cfg.name, "launches": launches,
-                      "algorithmic_bytes": cfg.algorithmic_bytes()}), flush=True)
+    print(json.dumps({"probe": kind, "workload": cfg.name, "dtype": dtype, "launches": launches,
+                      "algorithmic_bytes": wl.nbytes}), flush=True)
 
 
 def main():
@@ -215,7 +231,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the RoPE and AdaLN line items (headline only)")
-    ap.add_argument("--probe", choices=["rms", "rope", "ropei", "adaln", "copy"])
+    ap.add_argument("--probe", choices=["rms", "rms_f16", "rms_f32", "rope", "ropei", "adaln",
+                                        "copy"])
     ap.add_argument("--launches", type=int, default=10)
     args = ap.parse_args()
 
@@ -277,18 +294,20 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_rope:
-        for key, name, kernel in (("rope", datagen.ROPE, "rmsnorm_rope"),
-                                  ("rope_interleaved", datagen.ROPE_INTERLEAVED,
-                                   "rmsnorm_rope_interleaved"),
-                                  ("adaln", datagen.ADALN, "rmsnorm_adaln")):
+        for key, name, kernel, dtype in (
+                ("rope", datagen.ROPE, "rmsnorm_rope", "bf16"),
+                ("rope_interleaved", datagen.ROPE_INTERLEAVED, "rmsnorm_rope_interleaved", "bf16"),
+                ("adaln", datagen.ADALN, "rmsnorm_adaln", "bf16"),
+                ("rms_f16", datagen.HEADLINE, "rmsnorm_f16", "f16"),
+                ("rms_f32", datagen.HEADLINE, "rmsnorm_f32", "f32")):
             rc = datagen.CONFIGS[name]
-            rw = Workload(rc, dev, stream)
+            rw = Workload(rc, dev, stream, dtype=dtype)
             rsec = rw.time_steps(args.steps, args.warmup)
-            rv = gbps(rc.algorithmic_bytes(), rsec)
+            rv = gbps(rw.nbytes, rsec)
             rtraffic = read_traffic(kernel, rc.name)
-            line[key] = {"workload": rc.name, "value": round(rv, 2), "unit": "GB/s",
-                         "ms_per_step": round(rsec * 1e3, 6),
-                         "bytes_per_step": rc.algorithmic_bytes(), "rotating_sets": rw.nsets,
+            line[key] = {"workload": rc.name, "io_dtype": dtype, "value": round(rv, 2),
+                         "unit": "GB/s", "ms_per_step": round(rsec * 1e3, 6),
+                         "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
                          "frac": round(rv / HBM_PEAK_GBPS, 4),
                          "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
             del rw

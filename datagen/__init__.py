@@ -189,14 +189,17 @@ class Config:
     def adaln(self) -> bool:
         return self.adaln_sigma > 0
 
-    def algorithmic_bytes(self) -> int:
-        """Bytes the op must move at least once: read x, write y (bf16 each),
-        read the weight once; for RoPE also read both binary32 tables once."""
-        b = 2 * self.rows * self.hidden * 2 + 2 * self.hidden
+    def algorithmic_bytes(self, elem_bytes: int = 2) -> int:
+        """Bytes the op must move at least once: read x, write y, read the
+        weight once (elements of `elem_bytes`: 2 for bf16/fp16, 4 for fp32);
+        for RoPE also both binary32 tables once; for AdaLN the per-sample
+        scale and shift rows once."""
+        e = elem_bytes
+        b = 2 * self.rows * self.hidden * e + self.hidden * e
         if self.rope:
             b += 2 * self.seq * (self.head_dim // 2) * 4
         if self.adaln:
-            b += 2 * self.batch * self.hidden * 2
+            b += 2 * self.batch * self.hidden * e
         return b
 
 
