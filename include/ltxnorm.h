@@ -1,6 +1,7 @@
 /*
- * ltxnorm.h -- C ABI of libltxnorm.so: row-wise RMSNorm and fused RMSNorm +
- * rotate-half RoPE over bf16 activations, as HIP kernels for gfx950 (MI355X).
+ * ltxnorm.h -- C ABI of libltxnorm.so: row-wise RMSNorm, fused RMSNorm + RoPE
+ * (rotate-half and interleaved pairs) and AdaLN-modulated RMSNorm over bf16,
+ * fp16 or fp32 activations, as HIP kernels for gfx950 (MI355X).
  *
  * Operations
  *   RMSNorm over the innermost dimension of [..., hidden] activations, with
@@ -53,14 +54,15 @@
 extern "C" {
 #endif
 
-#define LTXNORM_ABI_VERSION 2
+#define LTXNORM_ABI_VERSION 3
 
 #define LTXNORM_API __attribute__((visibility("default")))
 
-/* Largest supported hidden size: 16 wavefronts x 64 lanes x 8 vectors of 16
- * bytes per row, all held in registers: 65536 bf16/fp16 or 32768 fp32. */
-#define LTXNORM_MAX_HIDDEN 65536
-#define LTXNORM_MAX_HIDDEN_F32 32768
+/* Largest supported hidden size, every dtype.  Rows of up to 65536 bf16/fp16
+ * or 32768 fp32 elements are held in registers and read from HBM once;
+ * longer rows are read twice (once for the sum of squares, once to
+ * normalise). */
+#define LTXNORM_MAX_HIDDEN (1 << 24)
 
 typedef enum ltxnorm_dtype {
     LTXNORM_BF16 = 0,  /* bfloat16 (8 values per 16-byte vector) */
@@ -74,9 +76,7 @@ typedef enum ltxnorm_status {
     LTXNORM_ERR_SHAPE = 2,       /* rows < 0, hidden <= 0, size overflow, or a RoPE
                                     shape that does not fit (see below)             */
     LTXNORM_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                 */
-    LTXNORM_ERR_UNSUPPORTED = 4, /* unknown dtype, hidden not a whole number of
-                                    16-byte vectors (8 bf16/fp16, 4 fp32) or above
-                                    LTXNORM_MAX_HIDDEN(_F32)                         */
+    LTXNORM_ERR_UNSUPPORTED = 4, /* unknown dtype, or hidden > LTXNORM_MAX_HIDDEN    */
     LTXNORM_ERR_ALIAS = 5,       /* out partially overlaps x, or overlaps an input
                                     that is only read (weight, tables)              */
     LTXNORM_ERR_VALUE = 6,       /* eps negative, infinite or NaN                    */
@@ -93,7 +93,9 @@ typedef enum ltxnorm_status {
  *           to passing ones).
  *   rows    number of rows (B*S); 0 returns LTXNORM_OK and enqueues nothing
  *           (pointers may then be NULL).
- *   hidden  row length H; a multiple of 8, 8 <= H <= LTXNORM_MAX_HIDDEN.
+ *   hidden  row length H, 1 <= H <= LTXNORM_MAX_HIDDEN.  Rows of a whole
+ *           number of 16-byte vectors (H a multiple of 8 for bf16/fp16, of 4
+ *           for fp32) take the fastest kernels; any other H is supported.
  *   eps     added to the mean of squares inside the root; finite, >= 0.
  *           With eps = 0 an all-zero row gives NaN (0 * inf), as IEEE does.
  *   stream  HIP stream to enqueue on.
@@ -103,8 +105,7 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_fwd(void *out, const void *x, const v
                                                int64_t rows, int64_t hidden, float eps,
                                                hipStream_t stream);
 
-/* ltxnorm_rmsnorm_fwd for any ltxnorm_dtype; hidden a multiple of 8 (bf16,
- * fp16) or 4 (fp32). */
+/* ltxnorm_rmsnorm_fwd for any ltxnorm_dtype. */
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_fwd_dt(void *out, const void *x, const void *weight,
                                                   int64_t rows, int64_t hidden, float eps,
                                                   ltxnorm_dtype dtype, hipStream_t stream);
@@ -120,9 +121,13 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_fwd_dt(void *out, const void *x, cons
  *           Both must be 16-byte aligned and must not overlap out.
  *   hidden  must equal heads * head_dim.
  *   heads   number of heads, >= 1.
- *   head_dim  a multiple of 16 (each lane rotates 8-wide halves in place).
+ *   head_dim  even, >= 2.  A head_dim that is a multiple of 16 (bf16/fp16)
+ *           or 8 (fp32), with hidden a whole number of 16-byte vectors, takes
+ *           the vector kernels; other even head_dims pair through LDS (rows
+ *           up to 16320 elements held in registers) or, for longer rows,
+ *           through the two-pass path.
  *   seq_len number of table rows, >= 1.
- * Shape errors (hidden != heads*head_dim, head_dim % 16 != 0, seq_len < 1)
+ * Shape errors (hidden != heads*head_dim, head_dim odd or < 2, seq_len < 1)
  * give LTXNORM_ERR_SHAPE.
  */
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, const void *weight,
@@ -131,8 +136,7 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd(void *out, const void *x, co
                                                     int32_t head_dim, int64_t seq_len, float eps,
                                                     hipStream_t stream);
 
-/* ltxnorm_rmsnorm_rope_fwd for any ltxnorm_dtype; head_dim a multiple of 16
- * (bf16, fp16) or 8 (fp32). */
+/* ltxnorm_rmsnorm_rope_fwd for any ltxnorm_dtype. */
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd_dt(void *out, const void *x,
                                                        const void *weight, const float *cos_tab,
                                                        const float *sin_tab, int64_t rows,
@@ -153,16 +157,16 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_fwd_dt(void *out, const void *x,
  * with c = cos_tab[p, i], s = sin_tab[p, i] for i < head_dim/2 within each
  * head, p = row mod seq_len, on the un-rounded binary32 y.
  *
- * Arguments, layouts, ownership and errors as for ltxnorm_rmsnorm_rope_fwd,
- * except that head_dim need only be a multiple of 8.
+ * Arguments, layouts, ownership and errors as for ltxnorm_rmsnorm_rope_fwd
+ * (head_dim even; multiples of 8 bf16/fp16 or 4 fp32 with hidden a whole
+ * number of vectors take the vector kernel).
  */
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd(
     void *out, const void *x, const void *weight, const float *cos_tab, const float *sin_tab,
     int64_t rows, int64_t hidden, int32_t heads, int32_t head_dim, int64_t seq_len, float eps,
     hipStream_t stream);
 
-/* ltxnorm_rmsnorm_rope_interleaved_fwd for any ltxnorm_dtype; head_dim a
- * multiple of 8 (bf16, fp16) or 4 (fp32). */
+/* ltxnorm_rmsnorm_rope_interleaved_fwd for any ltxnorm_dtype. */
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd_dt(
     void *out, const void *x, const void *weight, const float *cos_tab, const float *sin_tab,
     int64_t rows, int64_t hidden, int32_t heads, int32_t head_dim, int64_t seq_len, float eps,

@@ -34,8 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libltxnorm.
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_ALIAS, ERR_VALUE, ERR_HIP = range(8)
 BF16, F16, F32 = 0, 1, 2
-MAX_HIDDEN = 65536
-MAX_HIDDEN_F32 = 32768
+MAX_HIDDEN = 1 << 24
 
 _lib = None
 

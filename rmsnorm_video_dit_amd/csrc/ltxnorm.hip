@@ -1,7 +1,8 @@
 // ltxnorm.hip -- C ABI of libltxnorm.so (declared in include/ltxnorm.h):
 // host-side validation of every argument before any HIP call, then dispatch
 // to the kernels of the I/O dtype (ltxnorm_bf16.hip, ltxnorm_f16.hip,
-// ltxnorm_f32.hip; the kernels themselves are in ltxnorm_kernels.h).
+// ltxnorm_f32.hip; the kernels themselves are in ltxnorm_kernels.h and
+// ltxnorm_general.h).
 //
 // Operations: RMSNorm over [..., hidden] with optional weight and eps (Hugging
 // Face cuda-kernels skill page, "Kernel-Specific Guidelines", RMSNorm); the
@@ -23,8 +24,6 @@ using ltxnorm_detail::Request;
 
 namespace {
 
-constexpr int kMaxVectorsPerRow = 16 * 64 * 8;  // 16 wavefronts x 64 lanes x 8 vectors
-
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // Half-open byte ranges [a, a + na) and [b, b + nb) overlap.
@@ -43,7 +42,7 @@ ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_
     if (epv == 0) return LTXNORM_ERR_UNSUPPORTED;
     const int eb = ltxnorm_detail::elem_bytes(dtype);
     if (rows < 0 || hidden <= 0) return LTXNORM_ERR_SHAPE;
-    if (hidden % epv != 0 || hidden > (int64_t)kMaxVectorsPerRow * epv) return LTXNORM_ERR_UNSUPPORTED;
+    if (hidden > LTXNORM_MAX_HIDDEN) return LTXNORM_ERR_UNSUPPORTED;
     if (rows > INT64_MAX / (hidden * eb)) return LTXNORM_ERR_SHAPE;
     if (!std::isfinite(eps) || eps < 0.0f) return LTXNORM_ERR_VALUE;
     if (rows == 0) {
@@ -58,16 +57,14 @@ ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_
     return LTXNORM_OK;
 }
 
-// Validation shared by the RoPE entry points.  head_dim must be a multiple
-// of `head_dim_vectors` 16-byte vectors' worth of elements.
+// Validation shared by the RoPE entry points: rotation pairs need an even
+// head_dim, and the heads must tile the row.
 ltxnorm_status check_rope(void* out, const void* x, const void* weight, const float* cos_tab,
                           const float* sin_tab, int64_t rows, int64_t hidden, int32_t heads,
                           int32_t head_dim, int64_t seq_len, float eps, ltxnorm_dtype dtype,
-                          int head_dim_vectors, bool* empty) {
-    const int epv = ltxnorm_detail::elems_per_vec(dtype);
-    if (epv == 0) return LTXNORM_ERR_UNSUPPORTED;
-    const int multiple = epv * head_dim_vectors;
-    if (heads < 1 || head_dim < multiple || head_dim % multiple != 0 || seq_len < 1 ||
+                          bool* empty) {
+    if (ltxnorm_detail::elems_per_vec(dtype) == 0) return LTXNORM_ERR_UNSUPPORTED;
+    if (heads < 1 || head_dim < 2 || head_dim % 2 != 0 || seq_len < 1 ||
         (int64_t)heads * head_dim != hidden)
         return LTXNORM_ERR_SHAPE;
     if (seq_len > INT64_MAX / ((int64_t)head_dim * 4)) return LTXNORM_ERR_SHAPE;
@@ -95,12 +92,9 @@ ltxnorm_status rope(Op op, void* out, const void* x, const void* weight, const f
                     const float* sin_tab, int64_t rows, int64_t hidden, int32_t heads,
                     int32_t head_dim, int64_t seq_len, float eps, ltxnorm_dtype dtype,
                     hipStream_t stream) {
-    // rotate-half pairs whole vectors of the two halves; interleaved pairs
-    // sit inside one vector, so a head need only be whole vectors
-    const int head_dim_vectors = op == Op::kRopeRotateHalf ? 2 : 1;
     bool empty = false;
     ltxnorm_status st = check_rope(out, x, weight, cos_tab, sin_tab, rows, hidden, heads, head_dim,
-                                   seq_len, eps, dtype, head_dim_vectors, &empty);
+                                   seq_len, eps, dtype, &empty);
     if (st != LTXNORM_OK || empty) return st;
     const Request r{out, x, weight, cos_tab, sin_tab, nullptr, nullptr, rows, hidden,
                     seq_len, 1, head_dim, eps};
@@ -199,9 +193,7 @@ LTXNORM_API const char* ltxnorm_status_str(ltxnorm_status s) {
         case LTXNORM_ERR_SHAPE:
             return "invalid shape (rows, hidden, heads, head_dim, seq_len or rows_per_sample)";
         case LTXNORM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case LTXNORM_ERR_UNSUPPORTED:
-            return "unsupported dtype, or hidden not a whole number of 16-byte vectors, or above "
-                   "the maximum";
+        case LTXNORM_ERR_UNSUPPORTED: return "unsupported dtype, or hidden above LTXNORM_MAX_HIDDEN";
         case LTXNORM_ERR_ALIAS: return "out overlaps an input other than exactly x";
         case LTXNORM_ERR_VALUE: return "eps must be finite and non-negative";
         case LTXNORM_ERR_HIP: return "the HIP runtime rejected the kernel launch";

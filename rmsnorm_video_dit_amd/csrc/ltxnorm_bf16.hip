@@ -1,7 +1,7 @@
 // ltxnorm_bf16.hip -- kernel instances for bfloat16 activations, weights and
-// outputs (binary32 arithmetic).  The kernels are in ltxnorm_kernels.h; one
-// translation unit per I/O type keeps builds parallel.
-#include "ltxnorm_kernels.h"
+// outputs (binary32 arithmetic).  The kernels are in ltxnorm_kernels.h and
+// ltxnorm_general.h; one translation unit per I/O type keeps builds parallel.
+#include "ltxnorm_dispatch.h"
 
 namespace ltxnorm_detail {
 

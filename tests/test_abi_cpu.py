@@ -51,7 +51,7 @@ def test_library_targets_gfx950_only():
 
 
 def test_version_and_status_strings():
-    assert ltx.ltxnorm_version() == 2
+    assert ltx.ltxnorm_version() == 3
     seen = set()
     for code in range(8):
         s = ltx.ltxnorm_status_str(code)
@@ -75,9 +75,11 @@ def rope(out=A, x=A + 64 * MB, w=None, c=A + 128 * MB, s=A + 129 * MB, rows=4, h
     (dict(rows=-1), ltx.ERR_SHAPE),
     (dict(hidden=0), ltx.ERR_SHAPE),
     (dict(hidden=-8), ltx.ERR_SHAPE),
-    (dict(hidden=2047), ltx.ERR_UNSUPPORTED),
-    (dict(hidden=12), ltx.ERR_UNSUPPORTED),
-    (dict(hidden=65544), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=(1 << 24) + 1), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=1 << 30), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=2047, out=A + 2), ltx.ERR_ALIGN),   # any H passes the shape check
+    (dict(hidden=1, out=A + 2), ltx.ERR_ALIGN),
+    (dict(hidden=65544, out=A + 2), ltx.ERR_ALIGN),  # beyond the registers: two-pass
     (dict(rows=1 << 62), ltx.ERR_SHAPE),
     (dict(eps=-1e-6), ltx.ERR_VALUE),
     (dict(eps=float("nan")), ltx.ERR_VALUE),
@@ -102,8 +104,11 @@ def test_rmsnorm_empty_is_ok_without_pointers():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=2048, heads=16), ltx.ERR_SHAPE),         # hidden != heads * head_dim
-    (dict(hidden=1280, heads=32, head_dim=40), ltx.ERR_SHAPE),  # head_dim % 16 != 0
-    (dict(hidden=256, heads=32, head_dim=8), ltx.ERR_SHAPE),
+    (dict(hidden=1280, heads=32, head_dim=40, out=A + 2), ltx.ERR_ALIGN),  # any even head_dim
+    (dict(hidden=256, heads=32, head_dim=8, out=A + 2), ltx.ERR_ALIGN),
+    (dict(hidden=66, heads=33, head_dim=2, out=A + 2), ltx.ERR_ALIGN),
+    (dict(hidden=96, heads=32, head_dim=3), ltx.ERR_SHAPE),    # odd head_dim
+    (dict(hidden=0, heads=32, head_dim=0), ltx.ERR_SHAPE),
     (dict(heads=0), ltx.ERR_SHAPE),
     (dict(seq_len=0), ltx.ERR_SHAPE),
     (dict(c=None), ltx.ERR_NULL),
@@ -121,8 +126,9 @@ def test_rope_validation(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=2048, heads=16, head_dim=64), ltx.ERR_SHAPE),   # hidden != heads * head_dim
-    (dict(hidden=96, heads=8, head_dim=12), ltx.ERR_SHAPE),      # head_dim % 8 != 0
-    (dict(hidden=192, heads=8, head_dim=24), OK_IF_VALID),   # head_dim 24 is accepted
+    (dict(hidden=96, heads=8, head_dim=12), OK_IF_VALID),     # any even head_dim
+    (dict(hidden=192, heads=8, head_dim=24), OK_IF_VALID),
+    (dict(hidden=88, heads=8, head_dim=11), ltx.ERR_SHAPE),    # odd head_dim
     (dict(seq_len=0), ltx.ERR_SHAPE),
     (dict(c=None), ltx.ERR_NULL),
     (dict(s=A + 129 * MB + 8), ltx.ERR_ALIGN),
@@ -145,7 +151,8 @@ def test_rope_interleaved_validation(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(rows_per_sample=0), ltx.ERR_SHAPE),
-    (dict(hidden=12), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=(1 << 24) + 8), ltx.ERR_UNSUPPORTED),
+    (dict(hidden=12, out=A + 2), ltx.ERR_ALIGN),   # any H passes the shape check
     (dict(eps=-1.0), ltx.ERR_VALUE),
     (dict(out=None), ltx.ERR_NULL),
     (dict(scale=A + 200 * MB + 2), ltx.ERR_ALIGN),
@@ -169,10 +176,8 @@ def test_adaln_validation(kw, status):
 @pytest.mark.parametrize("dtype,hidden,status", [
     (3, 2048, ltx.ERR_UNSUPPORTED),             # unknown dtype
     (-1, 2048, ltx.ERR_UNSUPPORTED),
-    (ltx.F16, 2044, ltx.ERR_UNSUPPORTED),        # fp16: 8 per vector
-    (ltx.F32, 2042, ltx.ERR_UNSUPPORTED),        # fp32: 4 per vector
-    (ltx.F32, 32772, ltx.ERR_UNSUPPORTED),       # fp32 cap 32768
-    (ltx.F16, 65544, ltx.ERR_UNSUPPORTED),       # fp16 cap 65536
+    (ltx.F16, (1 << 24) + 2, ltx.ERR_UNSUPPORTED),   # above LTXNORM_MAX_HIDDEN
+    (ltx.F32, (1 << 24) + 1, ltx.ERR_UNSUPPORTED),
     (ltx.F32, 0, ltx.ERR_SHAPE),
 ])
 def test_dtype_validation(dtype, hidden, status):
@@ -181,26 +186,32 @@ def test_dtype_validation(dtype, hidden, status):
                                                    1e-6, dtype, 0) == status
 
 
-def test_dtype_shapes_that_pass_validation():
-    """fp32 rows of 4k elements and fp16 rows of 8k are accepted: shown by
-    making only the alignment wrong."""
-    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 2052, 1e-6, ltx.F32, 0) == ltx.ERR_ALIGN
-    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 32768, 1e-6, ltx.F32, 0) == ltx.ERR_ALIGN
-    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, 2056, 1e-6, ltx.F16, 0) == ltx.ERR_ALIGN
+@pytest.mark.parametrize("dtype,hidden", [
+    (ltx.F32, 2052), (ltx.F32, 32768), (ltx.F16, 2056), (ltx.F16, 2044), (ltx.F32, 2042),
+    (ltx.F32, 32772), (ltx.F16, 65544), (ltx.BF16, 1 << 24), (ltx.F32, 1 << 24), (ltx.F16, 3),
+])
+def test_dtype_shapes_that_pass_validation(dtype, hidden):
+    """Any hidden from 1 to LTXNORM_MAX_HIDDEN is accepted in every dtype:
+    shown by making only the alignment wrong."""
+    assert ltx.ltxnorm_rmsnorm_fwd_dt_status(A + 4, A + 64 * MB, None, 4, hidden, 1e-6, dtype, 0) == ltx.ERR_ALIGN
 
 
 @pytest.mark.parametrize("dtype,interleaved,head_dim,status", [
-    (ltx.F32, False, 8, ltx.ERR_ALIGN),      # fp32 rotate-half: head_dim % 8
-    (ltx.F32, False, 12, ltx.ERR_SHAPE),
-    (ltx.F32, True, 4, ltx.ERR_ALIGN),       # fp32 interleaved: head_dim % 4
-    (ltx.F32, True, 6, ltx.ERR_SHAPE),
+    (ltx.F32, False, 8, ltx.ERR_ALIGN),
+    (ltx.F32, False, 12, ltx.ERR_ALIGN),
+    (ltx.F32, True, 4, ltx.ERR_ALIGN),
+    (ltx.F32, True, 6, ltx.ERR_ALIGN),
     (ltx.F16, False, 16, ltx.ERR_ALIGN),
-    (ltx.F16, False, 8, ltx.ERR_SHAPE),
+    (ltx.F16, False, 8, ltx.ERR_ALIGN),
     (ltx.F16, True, 8, ltx.ERR_ALIGN),
-    (ltx.F16, True, 12, ltx.ERR_SHAPE),
+    (ltx.F16, True, 12, ltx.ERR_ALIGN),
+    (ltx.F16, True, 7, ltx.ERR_SHAPE),       # odd head_dim: no pairs
+    (ltx.F32, False, 5, ltx.ERR_SHAPE),
+    (ltx.BF16, False, 0, ltx.ERR_SHAPE),
 ])
 def test_rope_dtype_head_dim_rules(dtype, interleaved, head_dim, status):
-    """ERR_ALIGN means the shape passed (out is deliberately misaligned)."""
+    """Any even head_dim passes in every dtype (ERR_ALIGN: the shape passed;
+    out is deliberately misaligned)."""
     heads = 24
     fn = (ltx.ltxnorm_rmsnorm_rope_interleaved_fwd_dt_status if interleaved
           else ltx.ltxnorm_rmsnorm_rope_fwd_dt_status)
@@ -222,5 +233,5 @@ def test_python_front_end_refuses_host_tensors():
 
 def test_error_raises_with_status():
     with pytest.raises(ltx.LtxnormError) as e:
-        ltx.ltxnorm_rmsnorm_fwd(A, A + 64 * MB, None, 4, 2047, 1e-6, 0)
+        ltx.ltxnorm_rmsnorm_fwd(A, A + 64 * MB, None, 4, (1 << 24) + 1, 1e-6, 0)
     assert e.value.status == ltx.ERR_UNSUPPORTED

@@ -1,0 +1,194 @@
+"""GPU parity of the kernels for rows of any length, through the C ABI,
+against the CPU oracle (same rule as every parity test: parity.py).
+
+* Hidden sizes that are not a whole number of 16-byte vectors (rows start
+  part-way into a vector; the row's end vectors are shared with the
+  neighbouring rows), in bf16, fp16 and fp32, for RMSNorm and AdaLN.
+* RoPE head sizes the vector kernels cannot pair (any even head_dim),
+  rotate-half (partners exchanged through LDS) and interleaved.
+* Rows beyond the register budget (two-pass kernel), every operation.
+* In place = out of place, NULL weight = ones, run-to-run identity, and
+  guard bands around the output, on each of these paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import rmsnorm_video_dit_amd as ltx
+from test_gpu_parity import (DEV, announce, check_adaln, check_rms, check_rope, dev_bf16,
+                             dev_f32, host_bits, run_adaln, run_rms, run_rope)
+
+pytestmark = pytest.mark.gpu
+
+# rows that start inside a 16-byte vector, rows shorter than one vector,
+# rows one element past a vector, up to the register budget
+ODD_HIDDEN = {
+    "bf16": [1, 2, 3, 5, 7, 9, 15, 17, 100, 255, 257, 1001, 2047, 2049, 3070, 3076, 4097, 6150,
+             12289, 65529],
+    "f16": [1, 3, 7, 9, 1001, 2050, 3076, 6150],
+    "f32": [1, 2, 3, 5, 6, 1023, 1025, 2050, 3070, 8191, 32765],
+}
+
+
+def _cases():
+    for dt, hs in ODD_HIDDEN.items():
+        for h in hs:
+            yield dt, h
+
+
+@pytest.mark.parametrize("dtype,hidden", list(_cases()))
+@pytest.mark.parametrize("rows", [1, 7, 333])
+def test_any_hidden(dtype, hidden, rows):
+    rows = max(1, min(rows, (1 << 22) // hidden))
+    announce(f"any-hidden {dtype} rows={rows} hidden={hidden}")
+    seed = 3 * hidden + rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    got, rep = check_rms(x, w, label=f"rms {dtype} {rows}x{hidden}")
+    if dtype != "f32":
+        assert rep["max_ulp"] <= 1.0
+    rps = max(1, -(-rows // 3))           # three samples (fewer for tiny batches)
+    samples = -(-rows // rps)
+    sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    check_adaln(x, w, sc, sh, rps, label=f"adaln {dtype} {rows}x{hidden}")
+
+
+# beyond the register budget: 65536 bf16/fp16 or 32768 fp32 per row (and rows
+# whose vectors straddle one more than that)
+LONG = [("bf16", 65537), ("bf16", 65544), ("bf16", 70001), ("bf16", 131072), ("bf16", 262147),
+        ("f16", 65544), ("f16", 100003), ("f32", 32767), ("f32", 32772), ("f32", 40001),
+        ("f32", 65536)]
+
+
+@pytest.mark.parametrize("dtype,hidden", LONG)
+@pytest.mark.parametrize("rows", [1, 3, 6])
+def test_long_rows(dtype, hidden, rows):
+    announce(f"long rows {dtype} rows={rows} hidden={hidden}")
+    seed = hidden + rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    got, rep = check_rms(x, w, label=f"long rms {dtype} {rows}x{hidden}")
+    if dtype != "f32":
+        assert rep["max_ulp"] <= 1.0
+    rps = 2
+    samples = -(-rows // rps)
+    sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    check_adaln(x, w, sc, sh, rps, label=f"long adaln {dtype} {rows}x{hidden}")
+
+
+# (heads, head_dim): head sizes the vector kernels cannot pair, rows that are
+# not whole vectors, and rows beyond the LDS exchange (two-pass)
+ROPE_SHAPES = [(1, 2), (33, 2), (5, 6), (7, 10), (4, 24), (16, 72), (32, 40), (3, 130),
+               (2, 136), (24, 88), (13, 14), (1, 1000), (9, 18), (20, 52)]
+LONG_ROPE = [(129, 136), (2, 40000), (1, 70002), (255, 258), (64, 1026)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("heads,head_dim", ROPE_SHAPES)
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("rows,seq_len", [(7, 3), (300, 4096)])
+def test_any_head_dim_rope(dtype, heads, head_dim, interleaved, rows, seq_len):
+    hidden = heads * head_dim
+    announce(f"any-head rope {dtype} {heads}x{head_dim} il={interleaved} rows={rows}")
+    seed = hidden + head_dim + rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    c, s = datagen.rope_tables(seq_len, head_dim)
+    check_rope(x, w, c, s, heads, head_dim, interleaved=interleaved,
+               label=f"rope {dtype} {rows}x{heads}x{head_dim} il={interleaved}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("heads,head_dim", LONG_ROPE)
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_long_rope(dtype, heads, head_dim, interleaved):
+    hidden = heads * head_dim
+    rows = 3
+    announce(f"long rope {dtype} {heads}x{head_dim} il={interleaved}")
+    x = datagen.make_x(rows, hidden, seed=hidden + 1, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=hidden + 1, stream=2, dtype=dtype)
+    c, s = datagen.rope_tables(5, head_dim)
+    check_rope(x, w, c, s, heads, head_dim, interleaved=interleaved,
+               label=f"long rope {dtype} {heads}x{head_dim} il={interleaved}")
+
+
+# one shape per path: general RMSNorm/AdaLN, general rotate-half (LDS),
+# general interleaved, two-pass RMSNorm/AdaLN, two-pass rotate-half and
+# interleaved
+PATHS = [
+    ("rms", 3076, 0), ("adaln", 3070, 0), ("half", 16 * 72, 72), ("il", 7 * 10, 10),
+    ("rms", 70001, 0), ("adaln", 65544, 0), ("half", 129 * 136, 136), ("il", 255 * 258, 258),
+    ("half", 2 * 40000, 40000),
+]
+
+
+def _run(op, x, w, c, s, d, out=None):
+    xt = x if torch.is_tensor(x) else dev_bf16(x)
+    wt = None if w is None else dev_bf16(w)
+    rows, hidden = xt.shape
+    if op == "rms":
+        return ltx.rmsnorm(xt, wt, 1e-6, out=out)
+    if op == "adaln":
+        sc = dev_bf16(datagen.make_x(2, hidden, seed=5, stream=4, sigma=0.25))
+        sh = dev_bf16(datagen.make_x(2, hidden, seed=5, stream=5, sigma=0.25))
+        return ltx.rmsnorm_adaln(xt, wt, sc, sh, 1e-6, out=out, rows_per_sample=-(-rows // 2))
+    return ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), hidden // d, d, 1e-6, out=out,
+                            interleaved=(op == "il"))
+
+
+@pytest.mark.parametrize("op,hidden,d", PATHS)
+def test_paths_invariants(op, hidden, d):
+    """In place equals out of place; run to run identical; NULL weight equals
+    ones; position 0 equals RMSNorm (RoPE); writes stay inside out."""
+    rows = 5
+    announce(f"path invariants {op} hidden={hidden} d={d}")
+    x = datagen.make_x(rows, hidden, seed=hidden, stream=1)
+    w = datagen.make_w(hidden, seed=hidden, stream=2)
+    c, s = datagen.rope_tables(7, d) if d else (None, None)
+    ref = host_bits(_run(op, x, w, c, s, d))
+    assert np.array_equal(ref, host_bits(_run(op, x, w, c, s, d)))
+    # in place
+    xt = dev_bf16(x)
+    _run(op, xt, w, c, s, d, out=xt)
+    assert np.array_equal(host_bits(xt), ref)
+    # NULL weight = ones
+    ones = np.full(hidden, 0x3F80, dtype=np.uint16)
+    assert np.array_equal(host_bits(_run(op, x, None, c, s, d)), host_bits(_run(op, x, ones, c, s, d)))
+    if d:
+        c0, s0 = datagen.rope_tables(1, d)
+        assert np.array_equal(host_bits(_run(op, x, w, c0, s0, d)), host_bits(_run("rms", x, w, None, None, 0)))
+    # guard bands: out is a 16-byte aligned window of a larger buffer filled
+    # with a sentinel; nothing outside the window changes
+    pad = 64
+    big = torch.full((rows * hidden + 2 * pad,), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = big[pad: pad + rows * hidden].view(rows, hidden)
+    _run(op, x, w, c, s, d, out=out)
+    b = host_bits(big)
+    sentinel = np.array([-7.0], dtype=np.float32).view(np.uint32)[0] >> 16
+    assert np.all(b[:pad] == sentinel) and np.all(b[pad + rows * hidden:] == sentinel)
+    assert np.array_equal(b[pad: pad + rows * hidden].reshape(rows, hidden), ref)
+
+
+def test_adaln_null_modulation_any_hidden():
+    """NULL scale and shift give RMSNorm bit for bit on the general and
+    two-pass kernels too."""
+    for hidden in (3076, 70001):
+        announce(f"adaln null modulation hidden={hidden}")
+        x = datagen.make_x(4, hidden, seed=9, stream=1)
+        w = datagen.make_w(hidden, seed=9, stream=2)
+        assert np.array_equal(run_adaln(x, w, None, None, 2), run_rms(x, w))
+
+
+def test_rope_position_zero_long():
+    announce("rope position zero, two-pass and LDS exchange")
+    for heads, d in ((16, 72), (129, 136)):
+        hidden = heads * d
+        x = datagen.make_x(3, hidden, seed=d, stream=1)
+        w = datagen.make_w(hidden, seed=d, stream=2)
+        c0, s0 = datagen.rope_tables(1, d)
+        base = run_rms(x, w)
+        assert np.array_equal(run_rope(x, w, c0, s0, heads, d), base)
+        assert np.array_equal(run_rope(x, w, c0, s0, heads, d, interleaved=True), base)
