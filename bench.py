@@ -17,11 +17,13 @@ the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
 scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
-"rms_f16" / "rms_f32", and the CPU oracle timed on this host under
-"cpu_baseline".  Prints one JSON line.
+"rms_f16" / "rms_f32", three shapes served by the kernels for rows of any
+length under "general" (hidden 3076, a 16 x 72 rotate-half head, rows of
+262144), and the CPU oracle timed on this host under "cpu_baseline".  Prints
+one JSON line.
 
---probe rms|rms_f16|rms_f32|rope|ropei|adaln|copy runs a few launches only, for
-rocprofv3 counter passes.
+--probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|copy runs
+a few launches only, for rocprofv3 counter passes.
 """
 from __future__ import annotations
 
@@ -52,6 +54,10 @@ KERNEL_SOURCES = (sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "
                   + sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.h")))
                   + [os.path.join(ROOT, "include", "ltxnorm.h")])
 DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
+PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datagen.HEADLINE,
+          "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
+          "rms_odd": "rms_4x4096x3076", "rope_d72": "rope_2x4096x1152_h16d72",
+          "rms_long": "rms_1x256x262144"}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
@@ -211,10 +217,8 @@ def probe(kind: str, launches: int):
         print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = datagen.CONFIGS[{"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE,
-                           "rms_f32": datagen.HEADLINE, "rope": datagen.ROPE,
-                           "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN}[kind]]
-    dtype = kind[4:] if kind.startswith("rms_") else "bf16"
+    cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[PROBES[kind]]
+    dtype = kind[4:] if kind in ("rms_f16", "rms_f32") else "bf16"
     wl = Workload(cfg, dev, s, max_sets=2, dtype=dtype)
     for i in range(launches):
         wl.step(i)
@@ -231,8 +235,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the RoPE and AdaLN line items (headline only)")
-    ap.add_argument("--probe", choices=["rms", "rms_f16", "rms_f32", "rope", "ropei", "adaln",
-                                        "copy"])
+    ap.add_argument("--probe", choices=sorted(PROBES) + ["copy"])
     ap.add_argument("--launches", type=int, default=10)
     args = ap.parse_args()
 
@@ -310,6 +313,24 @@ def main():
                          "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
                          "frac": round(rv / HBM_PEAK_GBPS, 4),
                          "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+            del rw
+            torch.cuda.empty_cache()
+        # shapes served by the kernels for rows of any length
+        line["general"] = {}
+        for name, kernel, path in (
+                ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
+                ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "general one-pass, LDS exchange"),
+                ("rms_1x256x262144", "rmsnorm_long", "two-pass")):
+            rc = datagen.GENERAL_CONFIGS[name]
+            rw = Workload(rc, dev, stream)
+            rsec = rw.time_steps(args.steps, args.warmup)
+            rv = gbps(rw.nbytes, rsec)
+            rtraffic = read_traffic(kernel, rc.name)
+            line["general"][name] = {
+                "path": path, "value": round(rv, 2), "unit": "GB/s",
+                "ms_per_step": round(rsec * 1e3, 6), "bytes_per_step": rw.nbytes,
+                "rotating_sets": rw.nsets, "frac": round(rv / HBM_PEAK_GBPS, 4),
+                "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
             del rw
             torch.cuda.empty_cache()
 

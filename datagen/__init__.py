@@ -219,6 +219,16 @@ CONFIGS = {
                                        heads=32, head_dim=64, theta=10000.0, interleaved=True),
     "adaln_2x4096x2048": Config("adaln_2x4096x2048", 8, 2, 4096, 2048, adaln_sigma=0.25),
 }
+# Shapes outside the pages' set that exercise the kernels for rows of any
+# length, with the same value recipe: a hidden size that is not a whole number
+# of 16-byte vectors, a head size the vector kernels cannot pair (16 heads x
+# 72, rotate-half), and rows longer than the register budget.
+GENERAL_CONFIGS = {
+    "rms_4x4096x3076": Config("rms_4x4096x3076", 9, 4, 4096, 3076),
+    "rope_2x4096x1152_h16d72": Config("rope_2x4096x1152_h16d72", 10, 2, 4096, 1152,
+                                      heads=16, head_dim=72, theta=10000.0),
+    "rms_1x256x262144": Config("rms_1x256x262144", 11, 1, 256, 262144),
+}
 HEADLINE = "rms_4x4096x3072"
 ROPE = "rope_2x4096x2048_h32d64"
 ROPE_INTERLEAVED = "ropei_2x4096x2048_h32d64"

@@ -80,6 +80,11 @@ struct AdaL {
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL>; }
 };
+template <typename IO, bool ODD>
+struct RopePackedL {
+    template <int WPR, int PER, bool FULL>
+    static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD>; }
+};
 // The general kernel masks every row itself: FULL does not select anything.
 template <typename IO, GOp OP>
 struct GeneralL {
@@ -170,13 +175,28 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
             if (fits) return by_plan<GeneralL<IO, GOp::kAda>, 4, 2, kMaxVecPerLane>(gp, a, stream);
             return launch_long<IO, GOp::kAda>(a, stream);
         case Op::kRopeRotateHalf: {
-            if (whole && fits && r.head_dim % (2 * E) == 0) {
+            const bool even = r.head_dim % (2 * E) == 0;    // half heads of whole vectors
+            const bool odd = E == 8 && r.head_dim % E == 0 && !even;  // ... of 4-element groups
+            if (whole && fits && even) {
                 const int P = a.vec_per_half;
                 if ((P & (P - 1)) == 0 && P <= kWave / 2)  // partner lanes within one wavefront
                     return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane>(plan_for(a.nvec, 4, 2), a, stream);
+            }
+            if (whole && fits && (even || odd) && a.vec_per_head <= kWave / 2) {
+                // heads packed into wavefronts (lw of 64 lanes used)
+                const int lw = kWave - kWave % a.vec_per_head;
+                Plan p = plan_for(((int64_t)a.nvec * kWave + lw - 1) / lw, 4, 2);
+                p.per = (int)((a.nvec + (int64_t)lw * p.wpr - 1) / ((int64_t)lw * p.wpr));
+                p.full = false;
+                if (p.per <= kMaxVecPerLane) {
+                    if constexpr (E == 8)
+                        if (odd) return by_plan<RopePackedL<IO, true>, 4, 2, kMaxVecPerLane>(p, a, stream);
+                    return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane>(p, a, stream);
+                }
+            }
+            if (whole && fits && even)
                 return by_plan<RopePairL<IO>, 2, 1, kMaxVecPerLane / 2>(plan_for(a.nunits, 2, 1), a,
                                                                         stream);
-            }
             const size_t lds_row = (size_t)r.hidden * sizeof(float);
             if (fits && lds_row * rows_per_block(gp.wpr) <= kMaxExchangeLds)
                 return by_plan<GeneralL<IO, GOp::kRopeHalf>, 4, 2, kMaxVecPerLane>(gp, a, stream, lds_row);

@@ -40,7 +40,9 @@ enum class GOp { kRms, kAda, kRopeHalf, kRopeIl };
 
 constexpr int kLongThreads = 1024;                  // one row per workgroup
 constexpr int kLongWaves = kLongThreads / kWave;
-constexpr int kLongUnroll = 4;                      // vectors in flight per thread
+// vectors in flight per thread (fp32 rows keep two: four spill at 1024 threads)
+template <typename IO>
+constexpr int kLongUnroll = IO::kEpv == 8 ? 4 : 2;
 
 // Elements base[start + i], i < kEpv, read one by one where lo <= start + i
 // < hi, zero elsewhere, packed as one 16-byte vector.
@@ -328,7 +330,7 @@ __global__ void __launch_bounds__(kLongThreads)
 rmsnorm_long_kernel(const KArgs a) {
     constexpr int E = IO::kEpv;
     constexpr int T = kLongThreads;
-    constexpr int U = kLongUnroll;
+    constexpr int U = kLongUnroll<IO>;
     __shared__ float partials[2][kLongWaves];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);

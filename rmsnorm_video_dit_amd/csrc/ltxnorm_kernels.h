@@ -93,12 +93,22 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 
         u32x4 xv[VPL];
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
+        // The table slice is an L2 hit.  With several wavefronts per row it is
+        // fetched together with x, off the critical path behind the row's
+        // barrier (H = 3072, d = 128: 69.6 -> 74.1 % of peak; H = 2304:
+        // 58.0 -> 64.3 %); with one wavefront per row either order measured
+        // the same, and fetching it after the reduction keeps registers free.
+        float c[E], ss[E];
+        if constexpr (WPR > 1) {
+            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
+            load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+        }
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-
-        float c[E], ss[E];
-        load_floats<E>(a.cos_tab + pos * a.half + toff, c);
-        load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+        if constexpr (WPR == 1) {
+            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
+            load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+        }
         // the partner term enters with -sin in the first half, +sin in the second
 #pragma unroll
         for (int e = 0; e < E; ++e) ss[e] *= sgn;
@@ -117,6 +127,129 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 par[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, own[e])));
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + par[e] * ss[e];
+            if (in) store_stream(yr + v, IO::narrow(o));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + rotate-half RoPE with head-packed lanes, for heads of vph =
+// head_dim / kEpv <= 64 vectors.  Each wavefront uses its first
+// lw = 64 - 64 mod vph lanes (the rest idle) for lw consecutive vectors, so
+// it always holds whole heads: lane l holds vector l mod vph of a head in
+// every slot, and the vector's partner half a head away is in the same
+// wavefront.  One load instruction still covers lw * 16 contiguous bytes.
+//  * EVEN (head_dim / 2 a multiple of kEpv): the partner is the whole vector
+//    of lane l + vph/2 (first half) or l - vph/2 (second half).
+//  * ODD (16-bit types, head_dim / 2 an odd multiple of 4): a vector holds
+//    two 4-element groups and the half-head offset is an odd number of
+//    groups, so group 0's partner is group 1 of some lane and group 1's
+//    partner is group 0 of another: two ds_bpermute sources, each fetching a
+//    fixed register.
+// The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot
+// and is read once per row, as in the power-of-two kernel.
+// ---------------------------------------------------------------------------
+template <typename IO, int VPL, int WPR, bool ODD>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_packed_kernel(const KArgs a) {
+    constexpr int RPB = Layout<WPR>::kRowsPerBlock;
+    constexpr int E = IO::kEpv;
+    constexpr int G = E / 2;  // elements per group (ODD)
+    static_assert(!ODD || E == 8, "the odd layout splits 8-element vectors");
+    const Lane<WPR> ln;
+    const int vph = a.vec_per_head;
+    const int lw = kWave - kWave % vph;
+    const int l = ln.lane;
+    const int hv = l % vph;                 // vector within its head
+    const int head0 = l - hv;               // first lane of the head
+    // partner lanes (ds_bpermute byte addresses), signs and table columns
+    int src0, src1, col0, col1;
+    float sg0, sg1;
+    if constexpr (ODD) {
+        const int gh = a.half / G;          // groups per half head (odd)
+        const int g0 = 2 * hv, g1 = 2 * hv + 1;
+        const bool lo0 = g0 < gh, lo1 = g1 < gh;
+        const int p0 = lo0 ? g0 + gh : g0 - gh;   // odd: group 1 of its vector
+        const int p1 = lo1 ? g1 + gh : g1 - gh;   // even: group 0 of its vector
+        src0 = (head0 + (p0 >> 1)) << 2;
+        src1 = (head0 + (p1 >> 1)) << 2;
+        sg0 = lo0 ? -1.0f : 1.0f;
+        sg1 = lo1 ? -1.0f : 1.0f;
+        col0 = (lo0 ? g0 : g0 - gh) * G;
+        col1 = (lo1 ? g1 : g1 - gh) * G;
+    } else {
+        const int P = vph / 2;
+        const bool lo = hv < P;
+        src0 = src1 = (lo ? l + P : l - P) << 2;
+        sg0 = sg1 = lo ? -1.0f : 1.0f;
+        col0 = (lo ? hv : hv - P) * E;
+        col1 = col0 + G;
+    }
+    auto vec_of = [&](int k) { return (k * WPR + ln.wave_in_row) * lw + l; };
+
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int v = vec_of(k);
+        const bool in = l < lw && v < a.nvec;
+        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+    }
+
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+        const int64_t row = base + ln.slot;
+        const bool active = row < a.rows;
+        if (WPR == 1 && !active) continue;
+        const int64_t pos = active ? row % a.seq_len : 0;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+
+        u32x4 xv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vec_of(k);
+            const bool in = l < lw && v < a.nvec && (WPR == 1 || active);
+            xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float c[E], ss[E];
+        auto load_tables = [&]() {
+            load_floats<G>(a.cos_tab + pos * a.half + col0, c);
+            load_floats<G>(a.cos_tab + pos * a.half + col1, c + G);
+            load_floats<G>(a.sin_tab + pos * a.half + col0, ss);
+            load_floats<G>(a.sin_tab + pos * a.half + col1, ss + G);
+        };
+        if constexpr (WPR > 1) load_tables();  // with x, as in the power-of-two kernel
+        const float part = sum_squares<IO, VPL>(xv);
+        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        if constexpr (WPR == 1) load_tables();
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            ss[e] *= sg0;
+            ss[e + G] *= sg1;
+        }
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vec_of(k);
+            const bool in = l < lw && v < a.nvec && (WPR == 1 || active);
+            keep_packed(xv[k]);
+            keep_packed(wv[k]);
+            float own[E], g[E], par[E], o[E];
+            IO::widen(xv[k], own);
+            IO::widen(wv[k], g);
+#pragma unroll
+            for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
+            // group 0 takes the partner lane's second group (ODD) or first
+            // group (EVEN); group 1 the other way round
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+                const int from0 = ODD ? e + G : e;
+                const int from1 = ODD ? e : e + G;
+                par[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src0, __builtin_bit_cast(int, own[from0])));
+                par[e + G] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, own[from1])));
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + par[e] * ss[e];
             if (in) store_stream(yr + v, IO::narrow(o));
@@ -260,14 +393,19 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
 
         u32x4 xv[VPL];
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
-        const float part = sum_squares<IO, VPL>(xv);
-        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-
         const float* crow = a.cos_tab + pos * a.half;
         const float* srow = a.sin_tab + pos * a.half;
         float c[NP], sn[NP];
-        load_floats<NP>(crow + toff[0], c);
-        load_floats<NP>(srow + toff[0], sn);
+        if constexpr (WPR > 1) {  // with x, as in the rotate-half kernels
+            load_floats<NP>(crow + toff[0], c);
+            load_floats<NP>(srow + toff[0], sn);
+        }
+        const float part = sum_squares<IO, VPL>(xv);
+        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        if constexpr (WPR == 1) {
+            load_floats<NP>(crow + toff[0], c);
+            load_floats<NP>(srow + toff[0], sn);
+        }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = k * L + ln.t;

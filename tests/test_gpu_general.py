@@ -192,3 +192,58 @@ def test_rope_position_zero_long():
         base = run_rms(x, w)
         assert np.array_equal(run_rope(x, w, c0, s0, heads, d), base)
         assert np.array_equal(run_rope(x, w, c0, s0, heads, d, interleaved=True), base)
+
+
+@pytest.mark.parametrize("name", list(datagen.GENERAL_CONFIGS))
+def test_general_workload_full_size(name):
+    """The benchmark's shapes for the kernels of any row length, every
+    element, in the launch configuration the benchmark times."""
+    cfg = datagen.GENERAL_CONFIGS[name]
+    announce(f"general workload {name} rows={cfg.rows} hidden={cfg.hidden}")
+    inp = datagen.make_inputs(cfg)
+    if cfg.rope:
+        got, rep = check_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg.heads, cfg.head_dim,
+                              cfg.eps, label=name, interleaved=cfg.interleaved)
+        assert rep["n_floor_bound"] <= 1e-5 * rep["n"]
+    else:
+        got, rep = check_rms(inp["x"], inp["w"], cfg.eps, label=name)
+        assert rep["max_ulp"] <= 1.0
+    assert rep.get("n_bit_exact", rep.get("n_exact")) >= 0.99 * rep["n"]
+
+
+# heads packed into wavefronts: non-power-of-two heads whose halves are whole
+# vectors, and (16-bit types) halves of an odd number of 4-element groups
+PACKED = [(8, d) for d in (24, 40, 56, 72, 88, 104, 120, 136, 184, 248, 80, 96, 112, 160, 192,
+                           240)] + [(4, d) for d in (24, 40, 72, 120)]
+
+
+@pytest.mark.parametrize("epv,head_dim", PACKED)
+@pytest.mark.parametrize("heads", [1, 7, 33])
+@pytest.mark.parametrize("rows,seq_len", [(7, 3), (300, 4096)])
+def test_rope_packed_heads(epv, head_dim, heads, rows, seq_len):
+    dtypes = ["bf16", "f16"] if epv == 8 else ["f32"]
+    hidden = heads * head_dim
+    for dtype in dtypes:
+        announce(f"packed rope {dtype} {heads}x{head_dim} rows={rows}")
+        x = datagen.make_x(rows, hidden, seed=hidden + rows + 3, stream=1, dtype=dtype)
+        w = datagen.make_w(hidden, seed=hidden + rows + 3, stream=2, dtype=dtype)
+        c, s = datagen.rope_tables(seq_len, head_dim)
+        check_rope(x, w, c, s, heads, head_dim,
+                   label=f"packed rope {dtype} {rows}x{heads}x{head_dim}")
+
+
+@pytest.mark.parametrize("head_dim", [72, 80, 88])
+def test_rope_packed_invariants(head_dim):
+    """Position 0 is RMSNorm bit for bit; in place equals out of place."""
+    heads = 16
+    hidden = heads * head_dim
+    announce(f"packed rope invariants d={head_dim}")
+    x = datagen.make_x(100, hidden, seed=head_dim, stream=1)
+    w = datagen.make_w(hidden, seed=head_dim, stream=2)
+    c0, s0 = datagen.rope_tables(1, head_dim)
+    assert np.array_equal(run_rope(x, w, c0, s0, heads, head_dim), run_rms(x, w))
+    c, s = datagen.rope_tables(50, head_dim)
+    ref = run_rope(x, w, c, s, heads, head_dim)
+    xt = dev_bf16(x)
+    ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), heads, head_dim, 1e-6, out=xt)
+    assert np.array_equal(host_bits(xt), ref)
