@@ -17,10 +17,10 @@ the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
 scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
-"rms_f16" / "rms_f32", three shapes served by the kernels for rows of any
-length under "general" (hidden 3076, a 16 x 72 rotate-half head, rows of
-262144), and the CPU oracle timed on this host under "cpu_baseline".  Prints
-one JSON line.
+"rms_f16" / "rms_f32", three shapes outside the pages' set under "general"
+(hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
+rotate-half pairs; rows of 262144, beyond the register budget), and the CPU
+oracle timed on this host under "cpu_baseline".  Prints one JSON line.
 
 --probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|copy runs
 a few launches only, for rocprofv3 counter passes.
@@ -319,7 +319,7 @@ def main():
         line["general"] = {}
         for name, kernel, path in (
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
-                ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "general one-pass, LDS exchange"),
+                ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
                 ("rms_1x256x262144", "rmsnorm_long", "two-pass")):
             rc = datagen.GENERAL_CONFIGS[name]
             rw = Workload(rc, dev, stream)

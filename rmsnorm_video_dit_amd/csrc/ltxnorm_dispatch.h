@@ -137,6 +137,11 @@ inline int rows_per_block(int wpr) { return wpr == 1 ? 4 : (wpr <= 3 ? 2 : 1); }
 
 // Register budget of the one-pass kernels, in 16-byte vectors per row.
 constexpr int64_t kMaxRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMaxVecPerLane;
+// The general kernel also holds two weight chunks per vector: at most five
+// vectors per lane (more spill at 16 wavefronts); longer rows take the
+// two-pass kernel.
+constexpr int kMaxGeneralVecPerLane = 5;
+constexpr int64_t kMaxGeneralRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMaxGeneralVecPerLane;
 // Dynamic LDS the rotate-half general kernel may take per workgroup.
 constexpr size_t kMaxExchangeLds = 64 * 1024 - 256;
 
@@ -162,17 +167,18 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
     // up to two more than hidden / E)
     const int64_t touched = whole ? r.hidden / E : (r.hidden + 2 * E - 2) / E;
     const bool fits = touched <= kMaxRowVectors;
+    const bool gfits = touched <= kMaxGeneralRowVectors;
     const Plan gp = plan_for(touched, 4, 2);
     switch (op) {
         case Op::kRmsNorm:
             if (whole && fits)
                 return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(plan_for(a.nvec, 4, 2), a, stream);
-            if (fits) return by_plan<GeneralL<IO, GOp::kRms>, 4, 2, kMaxVecPerLane>(gp, a, stream);
+            if (gfits) return by_plan<GeneralL<IO, GOp::kRms>, 4, 2, kMaxGeneralVecPerLane>(gp, a, stream);
             return launch_long<IO, GOp::kRms>(a, stream);
         case Op::kAdaLN:
             if (whole && fits)
                 return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane>(plan_for(a.nvec, 4, 2), a, stream);
-            if (fits) return by_plan<GeneralL<IO, GOp::kAda>, 4, 2, kMaxVecPerLane>(gp, a, stream);
+            if (gfits) return by_plan<GeneralL<IO, GOp::kAda>, 4, 2, kMaxGeneralVecPerLane>(gp, a, stream);
             return launch_long<IO, GOp::kAda>(a, stream);
         case Op::kRopeRotateHalf: {
             const bool even = r.head_dim % (2 * E) == 0;    // half heads of whole vectors
@@ -198,8 +204,9 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
                 return by_plan<RopePairL<IO>, 2, 1, kMaxVecPerLane / 2>(plan_for(a.nunits, 2, 1), a,
                                                                         stream);
             const size_t lds_row = (size_t)r.hidden * sizeof(float);
-            if (fits && lds_row * rows_per_block(gp.wpr) <= kMaxExchangeLds)
-                return by_plan<GeneralL<IO, GOp::kRopeHalf>, 4, 2, kMaxVecPerLane>(gp, a, stream, lds_row);
+            if (gfits && lds_row * rows_per_block(gp.wpr) <= kMaxExchangeLds)
+                return by_plan<GeneralL<IO, GOp::kRopeHalf>, 4, 2, kMaxGeneralVecPerLane>(gp, a, stream,
+                                                                                         lds_row);
             return launch_long<IO, GOp::kRopeHalf>(a, stream);
         }
         case Op::kRopeInterleaved: {
@@ -210,7 +217,7 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
                     return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane>(p, a, stream);
                 return by_plan<RopeIlL<IO, false>, 4, 2, kMaxVecPerLane>(p, a, stream);
             }
-            if (fits) return by_plan<GeneralL<IO, GOp::kRopeIl>, 4, 2, kMaxVecPerLane>(gp, a, stream);
+            if (gfits) return by_plan<GeneralL<IO, GOp::kRopeIl>, 4, 2, kMaxGeneralVecPerLane>(gp, a, stream);
             return launch_long<IO, GOp::kRopeIl>(a, stream);
         }
     }

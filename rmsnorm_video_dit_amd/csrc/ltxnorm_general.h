@@ -133,17 +133,9 @@ __device__ __forceinline__ u32x4 load_window(const void* base, int64_t start, in
     return load_elems<IO>(base, start, 0, n);
 }
 
-// The row's vector q (row-relative elements j0 .. j0 + kEpv, j0 = q kEpv -
-// first): whole vectors with the streaming load, the row's end vectors
-// element by element (its own elements only).
-template <typename IO>
-__device__ __forceinline__ u32x4 load_row_vec(const void* x, int64_t s, int64_t g0, int q, int j0,
-                                              int hidden) {
-    constexpr int E = IO::kEpv;
-    if (j0 >= 0 && j0 + E <= hidden) return load_stream(static_cast<const u32x4*>(x) + g0 + q);
-    return load_elems<IO>(x, s + j0, s, s + hidden);
-}
-
+// Store a row's vector q (row-relative elements j0 .. j0 + kEpv): whole
+// vectors with the streaming store, the row's end vectors element by element
+// (its own elements only).
 template <typename IO>
 __device__ __forceinline__ void store_row_vec(void* out, int64_t s, int64_t g0, int q, int j0,
                                               int hidden, const u32x4 v) {
@@ -154,53 +146,79 @@ __device__ __forceinline__ void store_row_vec(void* out, int64_t s, int64_t g0, 
         store_elems<IO>(out, s + j0, v, s, s + hidden);
 }
 
-// Normalise one vector of the row in place: f = (x * rstd) * w, plus the
-// AdaLN modulation; fw (fm) = start of the weight (modulation) window mod
-// kEpv.  msample = element offset of the row's modulation row.
-template <typename IO, GOp OP>
-__device__ __forceinline__ void normalise_vec(const KArgs& a, const u32x4 xv, int j0, int fw,
-                                              int64_t msample, int fm, float rstd, float* f) {
-    constexpr int E = IO::kEpv;
-    float g[E];
-    IO::widen(xv, f);
-    const u32x4 wv = a.w ? load_window<IO>(a.w, j0, fw, a.hidden) : splat(IO::kOne);
-    IO::widen(wv, g);
+// Zero the elements of v outside positions [lo, hi) of the vector
+// (0 <= lo, hi <= kEpv): the parts of a row's end vectors that belong to the
+// neighbouring rows.
+template <typename IO>
+__device__ __forceinline__ u32x4 keep_range(u32x4 v, int lo, int hi) {
+    const uint32_t keep = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
-    if constexpr (OP == GOp::kAda) {
-        float sc[E], sh[E];
-        const u32x4 sv = a.scale ? load_window<IO>(a.scale, msample + j0, fm, a.mod_elems)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 hv = a.shift ? load_window<IO>(a.shift, msample + j0, fm, a.mod_elems)
-                                 : splat(IO::kNegZero);
-        IO::widen(sv, sc);
-        IO::widen(hv, sh);
-#pragma unroll
-        for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+    for (int m = 0; m < 4; ++m) {
+        uint32_t mk;
+        if constexpr (IO::kEpv == 8)
+            mk = ((keep >> (2 * m)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * m + 1)) & 1u ? 0xFFFF0000u : 0u);
+        else
+            mk = (keep >> m) & 1u ? 0xFFFFFFFFu : 0u;
+        v[m] &= mk;
     }
+    return v;
+}
+
+// Chunk c of the weight (elements c kEpv .. + kEpv), zero outside [0, H);
+// ones for a null weight.
+template <typename IO>
+__device__ __forceinline__ u32x4 weight_chunk(const void* w, int c, int hidden) {
+    constexpr int E = IO::kEpv;
+    if (w == nullptr) return splat(IO::kOne);
+    if (c < 0) return u32x4{0u, 0u, 0u, 0u};
+    if ((c + 1) * E <= hidden) return static_cast<const u32x4*>(w)[c];
+    return load_elems<IO>(w, (int64_t)c * E, 0, hidden);
+}
+
+// Chunk c of the weight when it is whole (ones for a null weight, zero
+// otherwise): a load on one side only, so it issues without waiting; the
+// weight's partial last chunk is fetched separately.
+template <typename IO>
+__device__ __forceinline__ u32x4 whole_weight_chunk(const void* w, int c, int hidden) {
+    constexpr int E = IO::kEpv;
+    if (w == nullptr) return splat(IO::kOne);
+    return (c >= 0 && (c + 1) * E <= hidden) ? static_cast<const u32x4*>(w)[c] : u32x4{0u, 0u, 0u, 0u};
+}
+
+// The weight window of a row's vector q from the lane's two resident chunks
+// q - 1 and q: f = window start mod kEpv, the same for the whole row.
+template <typename IO>
+__device__ __forceinline__ u32x4 weight_window(u32x4 lo, u32x4 hi, int f) {
+    if (f == 0) return hi;
+    keep_packed(lo);
+    keep_packed(hi);
+    const uint32_t W[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return take_at<IO>(W, f);
 }
 
 // Interleaved RoPE on one normalised vector: pairs (2i, 2i + 1) of a head
 // turn by table column i.  j0 is even (hidden even, rows start at even
-// element offsets), so pairs never straddle vectors or the row's ends.
+// element offsets), so pairs never straddle vectors or the row's ends.  The
+// column is computed for every pair, valid or not, so that all table reads
+// are in range and issue together.
 template <int E>
 __device__ __forceinline__ void rope_interleaved_vec(const KArgs& a, const float* crow,
                                                      const float* srow, int j0, const float* f,
                                                      float* o) {
     const int d = a.head_dim;
     int hd = ((j0 % d) + d) % d;  // position of element 0 in its head
+    float c[E / 2], sn[E / 2];
 #pragma unroll
-    for (int e = 0; e < E; e += 2) {
-        const int j = j0 + e;
-        if (j >= 0 && j < a.hidden) {
-            const float c = crow[hd / 2], sn = srow[hd / 2];
-            o[e] = f[e] * c - f[e + 1] * sn;
-            o[e + 1] = f[e + 1] * c + f[e] * sn;
-        } else {
-            o[e] = o[e + 1] = 0.0f;
-        }
+    for (int p = 0; p < E / 2; ++p) {
+        c[p] = crow[hd / 2];
+        sn[p] = srow[hd / 2];
         hd += 2;
         if (hd == d) hd = 0;
+    }
+#pragma unroll
+    for (int p = 0; p < E / 2; ++p) {
+        o[2 * p] = f[2 * p] * c[p] - f[2 * p + 1] * sn[p];
+        o[2 * p + 1] = f[2 * p + 1] * c[p] + f[2 * p] * sn[p];
     }
 }
 
@@ -208,6 +226,15 @@ __device__ __forceinline__ void rope_interleaved_vec(const KArgs& a, const float
 // One-pass kernel for any hidden size that fits the register budget.
 // VPL vectors per lane, WPR wavefronts per row, Layout<WPR> rows per block.
 // Rotate-half needs Layout<WPR>::kRowsPerBlock * hidden floats of dynamic LDS.
+//
+// Every lane issues all its row loads before using any: an if/else with a
+// load on each side makes the compiler wait for every outstanding load at the
+// join, which serialised the loads of a row (H = 3076 measured 41 % of peak
+// that way).  So whole vectors are loaded unconditionally, the tensor's final
+// partial vector (if any) is fetched afterwards under a uniform branch, and
+// the neighbouring rows' elements in a row's end vectors are zeroed in
+// registers.  The weight chunks around each lane's windows are loaded once
+// per workgroup.
 // ---------------------------------------------------------------------------
 template <typename IO, GOp OP, int VPL, int WPR>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
@@ -219,6 +246,17 @@ rmsnorm_general_kernel(const KArgs a) {
     extern __shared__ float ybuf[];
     const Lane<WPR> ln;
     const int H = a.hidden;
+    const int64_t total = a.rows * (int64_t)H;
+    const int64_t whole = total / E;  // whole vectors in x
+
+    // weight chunks q - 1 and q of every slot (window of vector q)
+    u32x4 wlo[VPL], whi[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int q = k * L + ln.t;
+        wlo[k] = weight_chunk<IO>(a.w, q - 1, H);
+        whi[k] = weight_chunk<IO>(a.w, q, H);
+    }
 
     int parity = 0;
     for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
@@ -237,10 +275,34 @@ rmsnorm_general_kernel(const KArgs a) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int q = k * L + ln.t;
-            xv[k] = q < nch ? load_row_vec<IO>(a.x, s, g0, q, q * E - first, H) : u32x4{0u, 0u, 0u, 0u};
+            const bool in = q < nch && g0 + q < whole;
+            xv[k] = in ? load_stream(static_cast<const u32x4*>(a.x) + g0 + q) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (active && s + H > whole * E) {  // the tensor's final, partial vector
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int q = k * L + ln.t;
+                if (q < nch && g0 + q >= whole) xv[k] = load_elems<IO>(a.x, (g0 + q) * E, s, s + H);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int j0 = (k * L + ln.t) * E - first;
+            const int lo = j0 < 0 ? -j0 : 0;
+            const int hi = H - j0 >= E ? E : (H - j0 > 0 ? H - j0 : 0);
+            xv[k] = keep_range<IO>(xv[k], lo, hi);
         }
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+
+        auto normalise = [&](int k, float* f) {
+            float g[E];
+            keep_packed(xv[k]);
+            IO::widen(xv[k], f);
+            IO::widen(weight_window<IO>(wlo[k], whi[k], fw), g);
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
+        };
 
         if constexpr (kExchange) {
             float* yrow = ybuf + ln.slot * H;
@@ -250,8 +312,7 @@ rmsnorm_general_kernel(const KArgs a) {
                 if (q < nch) {
                     const int j0 = q * E - first;
                     float f[E];
-                    keep_packed(xv[k]);
-                    normalise_vec<IO, OP>(a, xv[k], j0, fw, 0, 0, rstd, f);
+                    normalise(k, f);
 #pragma unroll
                     for (int e = 0; e < E; ++e)
                         if (j0 + e >= 0 && j0 + e < H) yrow[j0 + e] = f[e];
@@ -268,20 +329,25 @@ rmsnorm_general_kernel(const KArgs a) {
                 if (q < nch) {
                     const int j0 = q * E - first;
                     int hd = ((j0 % d) + d) % d;
+                    float c[E], sn[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {  // columns in range for every element
+                        const int col = hd < half ? hd : hd - half;
+                        c[e] = crow[col];
+                        sn[e] = hd < half ? -srow[col] : srow[col];
+                        if (++hd == d) hd = 0;
+                    }
+                    hd = ((j0 % d) + d) % d;
                     float o[E];
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
+                        // first half: a c - b s; second half: b c + a s
                         const int j = j0 + e;
-                        if (j >= 0 && j < H) {
-                            // first half: a c - b s; second half: b c + a s
-                            const bool lo = hd < half;
-                            const int col = lo ? hd : hd - half;
-                            const float c = crow[col], sn = srow[col];
-                            const float par = yrow[lo ? j + half : j - half];
-                            o[e] = yrow[j] * c + par * (lo ? -sn : sn);
-                        } else {
-                            o[e] = 0.0f;
-                        }
+                        const bool valid = j >= 0 && j < H;
+                        // indices clamped into the row: every LDS read is in range
+                        const int jj = valid ? j : 0;
+                        const int pj = valid ? (hd < half ? j + half : j - half) : 0;
+                        o[e] = yrow[jj] * c[e] + yrow[pj] * sn[e];
                         if (++hd == d) hd = 0;
                     }
                     store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(o));
@@ -304,8 +370,18 @@ rmsnorm_general_kernel(const KArgs a) {
                 if (q < nch) {
                     const int j0 = q * E - first;
                     float f[E];
-                    keep_packed(xv[k]);
-                    normalise_vec<IO, OP>(a, xv[k], j0, fw, msample, fm, rstd, f);
+                    normalise(k, f);
+                    if constexpr (OP == GOp::kAda) {
+                        float sc[E], sh[E];
+                        const u32x4 sv = a.scale ? load_window<IO>(a.scale, msample + j0, fm, a.mod_elems)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+                        const u32x4 hv = a.shift ? load_window<IO>(a.shift, msample + j0, fm, a.mod_elems)
+                                                 : splat(IO::kNegZero);
+                        IO::widen(sv, sc);
+                        IO::widen(hv, sh);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+                    }
                     if constexpr (OP == GOp::kRopeIl) {
                         float o[E];
                         rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
@@ -335,6 +411,7 @@ rmsnorm_long_kernel(const KArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int H = a.hidden;
+    const int64_t whole = a.rows * (int64_t)H / E;  // whole vectors in x
 
     int parity = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
@@ -344,21 +421,39 @@ rmsnorm_long_kernel(const KArgs a) {
         const int nch = (first + H + E - 1) / E;
         const int fw = (-first) & (E - 1);
 
+        // U row vectors from q0, loads issued before any use (the pattern of
+        // the one-pass kernel): whole vectors, then the tensor's final
+        // partial vector under a uniform branch, then the neighbouring rows'
+        // elements zeroed.
+        auto load_vecs = [&](int q0, u32x4* v, bool stream) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = q0 + u * T + tid;
+                const bool in = q < nch && g0 + q < whole;
+                const u32x4* p = static_cast<const u32x4*>(a.x) + g0 + q;
+                v[u] = in ? (stream ? load_stream(p) : *p) : u32x4{0u, 0u, 0u, 0u};
+            }
+            if (s + H > whole * E) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int q = q0 + u * T + tid;
+                    if (q < nch && g0 + q >= whole) v[u] = load_elems<IO>(a.x, (g0 + q) * E, s, s + H);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j0 = (q0 + u * T + tid) * E - first;
+                const int lo = j0 < 0 ? -j0 : 0;
+                const int hi = H - j0 >= E ? E : (H - j0 > 0 ? H - j0 : 0);
+                v[u] = keep_range<IO>(v[u], lo, hi);
+            }
+        };
+
         // pass 1: sum of squares, U vectors in flight per thread
         float part = 0.0f;
         for (int q0 = 0; q0 < nch; q0 += T * U) {
             u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = q0 + u * T + tid;
-                const int j0 = q * E - first;
-                if (q >= nch)
-                    v[u] = u32x4{0u, 0u, 0u, 0u};
-                else if (j0 >= 0 && j0 + E <= H)
-                    v[u] = static_cast<const u32x4*>(a.x)[g0 + q];
-                else
-                    v[u] = load_elems<IO>(a.x, s + j0, s, s + H);
-            }
+            load_vecs(q0, v, false);
             part += sum_squares<IO, U>(v);
         }
         float sum = wave_sum(part);
@@ -381,20 +476,46 @@ rmsnorm_long_kernel(const KArgs a) {
             // pass 2: vectors in the row's vector grid
             const int64_t msample = OP == GOp::kAda ? (row / a.rows_per_sample) * H : 0;
             const int fm = (int)((msample - first) & (E - 1));
+            const int wfull = H / E;  // whole weight chunks
             for (int q0 = 0; q0 < nch; q0 += T * U) {
-                u32x4 v[U];
+                u32x4 v[U], wl[U], wh[U];
+                load_vecs(q0, v, true);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int q = q0 + u * T + tid;
-                    v[u] = q < nch ? load_row_vec<IO>(a.x, s, g0, q, q * E - first, H) : u32x4{0u, 0u, 0u, 0u};
+                    wl[u] = whole_weight_chunk<IO>(a.w, q - 1, H);
+                    wh[u] = whole_weight_chunk<IO>(a.w, q, H);
+                }
+                if (a.w != nullptr && wfull * E != H && q0 + T * U > wfull) {
+                    // windows reaching the weight's partial last chunk
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int q = q0 + u * T + tid;
+                        if (q - 1 == wfull) wl[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
+                        if (q == wfull) wh[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int q = q0 + u * T + tid;
                     if (q < nch) {
                         const int j0 = q * E - first;
-                        float f[E];
-                        normalise_vec<IO, OP>(a, v[u], j0, fw, msample, fm, rstd, f);
+                        float f[E], g[E];
+                        IO::widen(v[u], f);
+                        IO::widen(weight_window<IO>(wl[u], wh[u], fw), g);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
+                        if constexpr (OP == GOp::kAda) {
+                            float sc[E], sh[E];
+                            const u32x4 sv = a.scale ? load_window<IO>(a.scale, msample + j0, fm, a.mod_elems)
+                                                     : u32x4{0u, 0u, 0u, 0u};
+                            const u32x4 hv = a.shift ? load_window<IO>(a.shift, msample + j0, fm, a.mod_elems)
+                                                     : splat(IO::kNegZero);
+                            IO::widen(sv, sc);
+                            IO::widen(hv, sh);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+                        }
                         if constexpr (OP == GOp::kRopeIl) {
                             float o[E];
                             rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
