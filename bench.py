@@ -165,6 +165,25 @@ class Workload:
         return t0.elapsed_time(t1) * 1e-3 / steps
 
 
+def launch_floor_us(stream, launches: int = 1000) -> float:
+    """Per-launch time of a back-to-back empty kernel on the same stream
+    (torch's sleep kernel with zero cycles): the part of every step that no
+    kernel design removes."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            torch.cuda._sleep(0)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(launches):
+            torch.cuda._sleep(0)
+        t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / launches
+
+
 def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict:
     """The CPU oracle (double arithmetic, one rounding) on this host's cores,
     rows split into contiguous blocks across a thread pool; repeated over the
@@ -292,6 +311,11 @@ def main():
     }
     if traffic is not None:
         line["roofline"]["traffic_bytes_per_launch"] = int(traffic)
+    floor = launch_floor_us(stream)
+    line["launch_floor_us"] = round(floor, 3)
+    line["launch_floor_note"] = ("per-launch time of an empty kernel launched back to back on the "
+                                 "same stream; each step pays it, so small workloads cannot reach "
+                                 "the HBM rate (context, not subtracted from value)")
     host = wl.host
     del wl
     torch.cuda.empty_cache()
