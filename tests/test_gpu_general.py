@@ -16,7 +16,8 @@ import torch
 
 import datagen
 import rmsnorm_video_dit_amd as ltx
-from test_gpu_parity import (DEV, announce, check_adaln, check_rms, check_rope, dev_bf16,
+from parity import compare
+from test_gpu_parity import (DEV, ORC, announce, check_adaln, check_rms, check_rope, dev_bf16,
                              dev_f32, host_bits, run_adaln, run_rms, run_rope)
 
 pytestmark = pytest.mark.gpu
@@ -247,3 +248,73 @@ def test_rope_packed_invariants(head_dim):
     xt = dev_bf16(x)
     ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), heads, head_dim, 1e-6, out=xt)
     assert np.array_equal(host_bits(xt), ref)
+
+
+# ---------------------------------------------------------------------------
+# Element offsets past 2^31: 64-bit row addressing on every path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("op,hidden,d", [("rms", 2048, 0), ("rms", 3076, 0), ("half", 2048, 64),
+                                         ("il", 2048, 64), ("half", 1152, 72), ("adaln", 2048, 0)])
+def test_offsets_past_2_31(op, hidden, d):
+    """A tensor of more than 2^31 elements built on the device by repeating
+    one seeded 4096-row block; the last rows (element offsets past 2^31) and
+    the first rows are compared with the oracle's result for that block."""
+    block_rows = 4096
+    reps = (1 << 31) // (block_rows * hidden) + 2
+    rows = reps * block_rows
+    assert rows * hidden > (1 << 31)
+    announce(f"offsets past 2^31 {op} hidden={hidden} rows={rows}")
+    xb = datagen.make_x(block_rows, hidden, seed=hidden + d, stream=1)
+    w = datagen.make_w(hidden, seed=hidden + d, stream=2)
+    xt = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
+    xt.view(reps, block_rows, hidden).copy_(dev_bf16(xb).unsqueeze(0).expand(reps, block_rows, hidden))
+    wt = dev_bf16(w)
+    c = s = None
+    if op in ("half", "il"):
+        # one table row per block row, so every block repeat sees the same positions
+        c, s = datagen.rope_tables(block_rows, d)
+        y = ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s), hidden // d, d, 1e-6,
+                             interleaved=(op == "il"))
+        ref_y, mag = ORC.rmsnorm_rope(xb, w, c, s, hidden // d, d, 1e-6, with_mag=True,
+                                      interleaved=(op == "il"))
+    elif op == "adaln":
+        sc = datagen.make_x(1, hidden, seed=7, stream=4, sigma=0.25)
+        sh = datagen.make_x(1, hidden, seed=7, stream=5, sigma=0.25)
+        y = ltx.rmsnorm_adaln(xt, wt, dev_bf16(sc), dev_bf16(sh), 1e-6, rows_per_sample=rows)
+        ref_y, mag = ORC.rmsnorm_adaln(xb, w, sc, sh, block_rows, 1e-6, with_mag=True)
+    else:
+        y = ltx.rmsnorm(xt, wt, 1e-6)
+        ref_y, mag = ORC.rmsnorm(xb, w, 1e-6), None
+    ref32, ref = ORC.round(ref_y)
+    for name, sl in (("first block", slice(0, block_rows)), ("last block", slice(rows - block_rows, rows))):
+        got = host_bits(y[sl])
+        rep = compare(got, ref, mag, ref32)
+        assert rep["pass"], (op, hidden, name, rep)
+    del xt, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("op,dtype", [("rms", "bf16"), ("rms", "f32"), ("half", "bf16"),
+                                      ("il", "bf16"), ("adaln", "bf16")])
+def test_max_hidden(op, dtype):
+    """One row of LTXNORM_MAX_HIDDEN (2^24) elements: the two-pass kernel at
+    the largest accepted row; one beyond it is refused."""
+    hidden = ltx.MAX_HIDDEN
+    announce(f"max hidden {op} {dtype}")
+    x = datagen.make_x(1, hidden, seed=99, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=99, stream=2, dtype=dtype)
+    if op in ("half", "il"):
+        d = 4096
+        c, s = datagen.rope_tables(1, d)
+        check_rope(x, w, c, s, hidden // d, d, interleaved=(op == "il"), label=f"max hidden {op}")
+    elif op == "adaln":
+        sc = datagen.make_x(1, hidden, seed=98, stream=4, sigma=0.25, dtype=dtype)
+        sh = datagen.make_x(1, hidden, seed=98, stream=5, sigma=0.25, dtype=dtype)
+        check_adaln(x, w, sc, sh, 1, label="max hidden adaln")
+    else:
+        check_rms(x, w, label=f"max hidden rms {dtype}")
+    xt = dev_bf16(x)
+    st = ltx.ltxnorm_rmsnorm_fwd_dt_status(xt, xt, None, 1, hidden + 1, 1e-6,
+                                           {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype], None)
+    assert st == ltx.ERR_UNSUPPORTED
