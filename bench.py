@@ -33,6 +33,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,11 +70,17 @@ def pct_of_peak(gb_s: float, peak_gbps: float) -> float:
     return 100.0 * gb_s / peak_gbps
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and blank space removed), so
+    that stored counter figures stay valid across comment-only edits."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            code = _COMMENT.sub("", f.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,12 +10,14 @@
 // a 16-byte vector.  The lanes therefore walk the row in the global vector
 // grid: lane t of the row takes vectors k * L + t counted from the vector that
 // holds the row's first element, so every access inside the row is still an
-// aligned 16-byte vector and only the row's first and last vectors, shared
-// with the neighbouring rows, are read and written element by element (and
-// only the row's own elements).  The weight (and the modulation rows) are then
-// misaligned by a row-dependent number of elements: a lane reads the two
-// aligned vectors that straddle its window and funnel-shifts them, or element
-// by element at the ends of the array.
+// aligned 16-byte vector.  The row's first and last vectors are shared with
+// the neighbouring rows: they are loaded whole and the other rows' elements
+// zeroed in registers, and stored element by element (the row's own elements
+// only).  The weight (and the modulation rows) are then misaligned by a
+// row-dependent number of elements: a lane funnel-shifts the two aligned
+// vectors that straddle its window (held in registers for the weight, loaded
+// per row for the modulation), reading element by element only at the ends
+// of an array.
 //
 //  * rmsnorm_general_kernel: one pass, the row in registers (as the vector
 //    kernels): RMSNorm, AdaLN, and interleaved RoPE, whose pairs
