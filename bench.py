@@ -8,7 +8,13 @@ seeded synthetic tensors (x ~ N(0,1), weight ~ U(0.5,1.5)), resident in HBM
 before timing starts.  Consecutive steps cycle through enough copies of the
 input and output buffers (>= 1 GiB in total) that the 256 MB memory-side
 Infinity Cache cannot serve a step from the previous one.  Timing uses HIP
-events recorded on the stream the kernels are launched on.
+events recorded on the stream the kernels are launched on.  The K timed
+launches are issued one by one on the stream; `--launch graph` captures them
+into one HIP graph and replays it once instead (the library only enqueues
+kernels, so the launches capture as they are).  The line reports the
+headline in the other mode too ("graph_launch" / "stream_launch"); at these
+sizes the two agree, since the host-side cost of issuing a launch is hidden
+behind the previous kernel.
 
 value = algorithmic bytes per step (read x + write y + read weight once,
 201,332,736 B) / seconds per step, in GB/s (10^9 B/s); it is compared with
@@ -155,20 +161,36 @@ class Workload:
             self.ltx.ltxnorm_rmsnorm_fwd_dt(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
                                             self.code, self.stream)
 
-    def time_steps(self, steps: int, warmup: int):
-        """Warm up, then time exactly `steps` launches with HIP events on
-        the launch stream; returns seconds per step."""
+    def time_steps(self, steps: int, warmup: int, graph: bool = True):
+        """Warm up, then time exactly `steps` launches with HIP events on the
+        launch stream; returns seconds per step.  With `graph`, the `steps`
+        launches are captured into one HIP graph first (they only enqueue
+        kernels) and the timed region is one replay of it: every launch still
+        runs in full, without the host-side cost of issuing it."""
         import torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(self.stream)
-        for i in range(steps):
-            self.step(i)
-        t1.record(self.stream)
-        torch.cuda.synchronize()
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(steps):
+                    self.step(warmup + i)
+            torch.cuda.synchronize()
+            t0.record(self.stream)
+            with torch.cuda.stream(self.stream):
+                g.replay()
+            t1.record(self.stream)
+            torch.cuda.synchronize()
+            del g
+        else:
+            t0.record(self.stream)
+            for i in range(steps):
+                self.step(i)
+            t1.record(self.stream)
+            torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e-3 / steps
 
 
@@ -263,6 +285,9 @@ def main():
                     help="skip the RoPE and AdaLN line items (headline only)")
     ap.add_argument("--probe", choices=sorted(PROBES) + ["copy"])
     ap.add_argument("--launches", type=int, default=10)
+    ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
+                    help="issue the timed launches one by one on the stream (default) or as one "
+                         "captured HIP graph")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -286,8 +311,10 @@ def main():
 
     cfg = datagen.CONFIGS[datagen.HEADLINE]
     wl = Workload(cfg, dev, stream)
-    sec = wl.time_steps(args.steps, args.warmup)
+    graph = args.launch == "graph"
+    sec = wl.time_steps(args.steps, args.warmup, graph)
     value = gbps(cfg.algorithmic_bytes(), sec)
+    sec_other = wl.time_steps(args.steps, args.warmup, not graph)  # the other launch mode
     traffic = read_traffic("rmsnorm", cfg.name)
     line = {
         "metric": METRIC,
@@ -318,6 +345,12 @@ def main():
     }
     if traffic is not None:
         line["roofline"]["traffic_bytes_per_launch"] = int(traffic)
+    line["launch"] = ("one HIP graph of the K launches, replayed once in the timed region"
+                      if graph else "K launches issued one by one on the stream")
+    line["graph_launch" if not graph else "stream_launch"] = {
+        "value": round(gbps(cfg.algorithmic_bytes(), sec_other), 2), "unit": "GB/s",
+        "ms_per_step": round(sec_other * 1e3, 6),
+        "frac": round(gbps(cfg.algorithmic_bytes(), sec_other) / HBM_PEAK_GBPS, 4)}
     floor = launch_floor_us(stream)
     line["launch_floor_us"] = round(floor, 3)
     line["launch_floor_note"] = ("per-launch time of an empty kernel launched back to back on the "
@@ -336,7 +369,7 @@ def main():
                 ("rms_f32", datagen.HEADLINE, "rmsnorm_f32", "f32")):
             rc = datagen.CONFIGS[name]
             rw = Workload(rc, dev, stream, dtype=dtype)
-            rsec = rw.time_steps(args.steps, args.warmup)
+            rsec = rw.time_steps(args.steps, args.warmup, graph)
             rv = gbps(rw.nbytes, rsec)
             rtraffic = read_traffic(kernel, rc.name)
             line[key] = {"workload": rc.name, "io_dtype": dtype, "value": round(rv, 2),
@@ -354,7 +387,7 @@ def main():
                 ("rms_1x256x262144", "rmsnorm_long", "two-pass")):
             rc = datagen.GENERAL_CONFIGS[name]
             rw = Workload(rc, dev, stream)
-            rsec = rw.time_steps(args.steps, args.warmup)
+            rsec = rw.time_steps(args.steps, args.warmup, graph)
             rv = gbps(rw.nbytes, rsec)
             rtraffic = read_traffic(kernel, rc.name)
             line["general"][name] = {

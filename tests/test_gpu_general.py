@@ -318,3 +318,67 @@ def test_max_hidden(op, dtype):
     st = ltx.ltxnorm_rmsnorm_fwd_dt_status(xt, xt, None, 1, hidden + 1, 1e-6,
                                            {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype], None)
     assert st == ltx.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: the entry points enqueue kernels only (no memset, no
+# allocation), so a captured sequence replays like the eager calls
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replays():
+    """Capture one call of each operation (vector, head-packed, general and
+    two-pass kernels) into a graph; replay it three times with new inputs
+    written eagerly between replays; every replay equals the eager result."""
+    announce("graph capture")
+    shapes = [("rms", 512, 2048, 0), ("adaln", 512, 2048, 0), ("half", 512, 2048, 64),
+              ("il", 512, 2048, 64), ("half", 512, 1152, 72), ("rms", 256, 3076, 0),
+              ("rms", 2, 70001, 0)]
+    s = torch.cuda.Stream()
+    bufs = []
+    for op, rows, hidden, d in shapes:
+        xt = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
+        yt = torch.empty_like(xt)
+        wt = dev_bf16(datagen.make_w(hidden, seed=hidden, stream=2))
+        extra = {}
+        if d:
+            c, sn = datagen.rope_tables(rows, d)
+            extra = dict(c=dev_f32(c), s=dev_f32(sn))
+        if op == "adaln":
+            extra = dict(sc=dev_bf16(datagen.make_x(2, hidden, seed=4, stream=4, sigma=0.25)),
+                         sh=dev_bf16(datagen.make_x(2, hidden, seed=4, stream=5, sigma=0.25)))
+        bufs.append((op, rows, hidden, d, xt, yt, wt, extra))
+
+    def enqueue():
+        for op, rows, hidden, d, xt, yt, wt, e in bufs:
+            if op == "rms":
+                ltx.rmsnorm(xt, wt, 1e-6, out=yt)
+            elif op == "adaln":
+                ltx.rmsnorm_adaln(xt, wt, e["sc"], e["sh"], 1e-6, out=yt, rows_per_sample=rows // 2)
+            else:
+                ltx.rmsnorm_rope(xt, wt, e["c"], e["s"], hidden // d, d, 1e-6, out=yt,
+                                 interleaved=(op == "il"))
+
+    def fill(seed):
+        for i, (op, rows, hidden, d, xt, yt, wt, e) in enumerate(bufs):
+            xt.copy_(dev_bf16(datagen.make_x(rows, hidden, seed=seed * 100 + i, stream=1)))
+
+    fill(1)
+    with torch.cuda.stream(s):
+        enqueue()  # warm up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        enqueue()
+    torch.cuda.synchronize()
+    for seed in (2, 3, 4):
+        fill(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = [host_bits(b[5]).copy() for b in bufs]
+        for b in bufs:
+            b[5].zero_()
+        enqueue()  # eager, on the current stream
+        torch.cuda.synchronize()
+        for b, r in zip(bufs, replayed):
+            assert np.array_equal(host_bits(b[5]), r), (seed, b[:4])
