@@ -194,6 +194,15 @@ class Workload:
         return t0.elapsed_time(t1) * 1e-3 / steps
 
 
+def describe(cfg: datagen.Config, dtype: str = "bf16") -> str:
+    """The kernel and launch shape the library picks for a workload."""
+    import rmsnorm_video_dit_amd as ltx
+    op = (ltx.OP_ADALN if cfg.adaln else ltx.OP_ROPE_INTERLEAVED if cfg.interleaved
+          else ltx.OP_ROPE if cfg.rope else ltx.OP_RMSNORM)
+    return ltx.ltxnorm_describe_launch(op, cfg.rows, cfg.hidden, cfg.heads, cfg.head_dim,
+                                       DTYPE_CODE[dtype])
+
+
 def launch_floor_us(stream, launches: int = 1000) -> float:
     """Per-launch time of a back-to-back empty kernel on the same stream
     (torch's sleep kernel with zero cycles): the part of every step that no
@@ -339,6 +348,7 @@ def main():
                      "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / sec / 1e9, 2),
                      "kernel": "rmsnorm_kernel",
+                     "launch_shape": describe(cfg),
                      "kernel_us": round(sec * 1e6, 3)},
         "baseline_note": "vs_baseline divides by the H100 figure for this shape on the "
                          "pages (0.157 ms = 1282.4 GB/s); another GPU, context only",
@@ -372,7 +382,8 @@ def main():
             rsec = rw.time_steps(args.steps, args.warmup, graph)
             rv = gbps(rw.nbytes, rsec)
             rtraffic = read_traffic(kernel, rc.name)
-            line[key] = {"workload": rc.name, "io_dtype": dtype, "value": round(rv, 2),
+            line[key] = {"workload": rc.name, "io_dtype": dtype, "kernel": describe(rc, dtype),
+                         "value": round(rv, 2),
                          "unit": "GB/s", "ms_per_step": round(rsec * 1e3, 6),
                          "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
                          "frac": round(rv / HBM_PEAK_GBPS, 4),
@@ -391,7 +402,7 @@ def main():
             rv = gbps(rw.nbytes, rsec)
             rtraffic = read_traffic(kernel, rc.name)
             line["general"][name] = {
-                "path": path, "value": round(rv, 2), "unit": "GB/s",
+                "path": path, "kernel": describe(rc), "value": round(rv, 2), "unit": "GB/s",
                 "ms_per_step": round(rsec * 1e3, 6), "bytes_per_step": rw.nbytes,
                 "rotating_sets": rw.nsets, "frac": round(rv / HBM_PEAK_GBPS, 4),
                 "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}

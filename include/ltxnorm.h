@@ -204,6 +204,33 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd_dt(void *out, const void *x
                                                         float eps, ltxnorm_dtype dtype,
                                                         hipStream_t stream);
 
+/* The operations, for ltxnorm_describe_launch. */
+typedef enum ltxnorm_op {
+    LTXNORM_OP_RMSNORM = 0,           /* ltxnorm_rmsnorm_fwd                   */
+    LTXNORM_OP_ROPE = 1,              /* ltxnorm_rmsnorm_rope_fwd (rotate-half) */
+    LTXNORM_OP_ROPE_INTERLEAVED = 2,  /* ltxnorm_rmsnorm_rope_interleaved_fwd  */
+    LTXNORM_OP_ADALN = 3              /* ltxnorm_rmsnorm_adaln_fwd             */
+} ltxnorm_op;
+
+/*
+ * Which kernel, and which launch shape, a call of operation `op` with these
+ * shapes would use.  It is written as one NUL-terminated line of text into
+ * buf, truncated to len bytes, for example
+ *     "rmsnorm_kernel wavefronts_per_row=3 vectors_per_lane=2 rows_per_block=2
+ *      threads=384 lds_bytes=0"
+ * (the kernel names are those a profiler shows).  heads and head_dim are
+ * read for the RoPE operations only.
+ *
+ * Shapes are validated as the entry point validates them.  No pointer
+ * other than buf is involved: the call enqueues nothing and needs no GPU.
+ * Returns the status the entry point would return for the shapes,
+ * LTXNORM_ERR_NULL for a NULL buf with len > 0, or LTXNORM_ERR_UNSUPPORTED
+ * for an unknown op.  rows == 0 describes as "none".
+ */
+LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, int64_t hidden,
+                                                   int32_t heads, int32_t head_dim,
+                                                   ltxnorm_dtype dtype, char *buf, size_t len);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 LTXNORM_API const char *ltxnorm_status_str(ltxnorm_status s);
 

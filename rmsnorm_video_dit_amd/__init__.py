@@ -34,6 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libltxnorm.
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_ALIAS, ERR_VALUE, ERR_HIP = range(8)
 BF16, F16, F32 = 0, 1, 2
+OP_RMSNORM, OP_ROPE, OP_ROPE_INTERLEAVED, OP_ADALN = 0, 1, 2, 3
 MAX_HIDDEN = 1 << 24
 
 _lib = None
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.ltxnorm_status_str.restype = ctypes.c_char_p
         L.ltxnorm_version.argtypes = []
         L.ltxnorm_version.restype = ctypes.c_int
+        L.ltxnorm_describe_launch.argtypes = [c_int, i64, i64, i32, i32, c_int, ctypes.c_char_p,
+                                              ctypes.c_size_t]
+        L.ltxnorm_describe_launch.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -102,6 +106,17 @@ def ltxnorm_status_str(status: int) -> str:
 
 def ltxnorm_version() -> int:
     return lib().ltxnorm_version()
+
+
+def ltxnorm_describe_launch(op: int, rows: int, hidden: int, heads: int = 0, head_dim: int = 0,
+                            dtype: int = BF16) -> str:
+    """The kernel and launch shape a call would use (no GPU needed); raises
+    LtxnormError with the status the entry point would return for bad shapes."""
+    buf = ctypes.create_string_buffer(256)
+    st = lib().ltxnorm_describe_launch(int(op), int(rows), int(hidden), int(heads), int(head_dim),
+                                       int(dtype), buf, len(buf))
+    _raise_if(st, "ltxnorm_describe_launch")
+    return buf.value.decode()
 
 
 def ltxnorm_rmsnorm_fwd_status(out, x, weight, rows, hidden, eps, stream) -> int:

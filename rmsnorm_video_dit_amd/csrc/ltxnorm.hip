@@ -15,6 +15,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "ltxnorm.h"
 #include "ltxnorm_launch.h"
@@ -32,19 +33,37 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
     return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
+// Shape checks shared by every entry point, in order: dtype, shape, scalar
+// value.
+ltxnorm_status check_shape(int64_t rows, int64_t hidden, float eps, ltxnorm_dtype dtype) {
+    if (ltxnorm_detail::elems_per_vec(dtype) == 0) return LTXNORM_ERR_UNSUPPORTED;
+    const int eb = ltxnorm_detail::elem_bytes(dtype);
+    if (rows < 0 || hidden <= 0) return LTXNORM_ERR_SHAPE;
+    if (hidden > LTXNORM_MAX_HIDDEN) return LTXNORM_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / (hidden * eb)) return LTXNORM_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return LTXNORM_ERR_VALUE;
+    return LTXNORM_OK;
+}
+
+// The RoPE entry points' extra shape checks: rotation pairs need an even
+// head_dim, and the heads must tile the row.
+ltxnorm_status check_rope_shape(int64_t hidden, int32_t heads, int32_t head_dim, int64_t seq_len) {
+    if (heads < 1 || head_dim < 2 || head_dim % 2 != 0 || seq_len < 1 ||
+        (int64_t)heads * head_dim != hidden)
+        return LTXNORM_ERR_SHAPE;
+    if (seq_len > INT64_MAX / ((int64_t)head_dim * 4)) return LTXNORM_ERR_SHAPE;
+    return LTXNORM_OK;
+}
+
 // Checks shared by every entry point, in order: dtype, shape, scalar value,
 // empty, pointers, alignment, aliasing.  Returns OK with *empty set when
 // there is nothing to launch.
 ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_t rows,
                             int64_t hidden, float eps, ltxnorm_dtype dtype, bool* empty) {
     *empty = false;
-    const int epv = ltxnorm_detail::elems_per_vec(dtype);
-    if (epv == 0) return LTXNORM_ERR_UNSUPPORTED;
+    const ltxnorm_status st = check_shape(rows, hidden, eps, dtype);
+    if (st != LTXNORM_OK) return st;
     const int eb = ltxnorm_detail::elem_bytes(dtype);
-    if (rows < 0 || hidden <= 0) return LTXNORM_ERR_SHAPE;
-    if (hidden > LTXNORM_MAX_HIDDEN) return LTXNORM_ERR_UNSUPPORTED;
-    if (rows > INT64_MAX / (hidden * eb)) return LTXNORM_ERR_SHAPE;
-    if (!std::isfinite(eps) || eps < 0.0f) return LTXNORM_ERR_VALUE;
     if (rows == 0) {
         *empty = true;
         return LTXNORM_OK;
@@ -57,18 +76,15 @@ ltxnorm_status check_common(void* out, const void* x, const void* weight, int64_
     return LTXNORM_OK;
 }
 
-// Validation shared by the RoPE entry points: rotation pairs need an even
-// head_dim, and the heads must tile the row.
+// Validation shared by the RoPE entry points.
 ltxnorm_status check_rope(void* out, const void* x, const void* weight, const float* cos_tab,
                           const float* sin_tab, int64_t rows, int64_t hidden, int32_t heads,
                           int32_t head_dim, int64_t seq_len, float eps, ltxnorm_dtype dtype,
                           bool* empty) {
     if (ltxnorm_detail::elems_per_vec(dtype) == 0) return LTXNORM_ERR_UNSUPPORTED;
-    if (heads < 1 || head_dim < 2 || head_dim % 2 != 0 || seq_len < 1 ||
-        (int64_t)heads * head_dim != hidden)
-        return LTXNORM_ERR_SHAPE;
-    if (seq_len > INT64_MAX / ((int64_t)head_dim * 4)) return LTXNORM_ERR_SHAPE;
-    ltxnorm_status st = check_common(out, x, weight, rows, hidden, eps, dtype, empty);
+    ltxnorm_status st = check_rope_shape(hidden, heads, head_dim, seq_len);
+    if (st != LTXNORM_OK) return st;
+    st = check_common(out, x, weight, rows, hidden, eps, dtype, empty);
     if (st != LTXNORM_OK || *empty) return st;
     if (cos_tab == nullptr || sin_tab == nullptr) return LTXNORM_ERR_NULL;
     if (misaligned(cos_tab) || misaligned(sin_tab)) return LTXNORM_ERR_ALIGN;
@@ -184,6 +200,46 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void* out, const void* x, c
                                                      hipStream_t stream) {
     return ltxnorm_rmsnorm_adaln_fwd_dt(out, x, weight, scale, shift, rows, hidden,
                                         rows_per_sample, eps, LTXNORM_BF16, stream);
+}
+
+LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, int64_t hidden,
+                                                   int32_t heads, int32_t head_dim,
+                                                   ltxnorm_dtype dtype, char* buf, size_t len) {
+    if (buf == nullptr && len > 0) return LTXNORM_ERR_NULL;
+    const int epv = ltxnorm_detail::elems_per_vec(dtype);
+    if (epv == 0) return LTXNORM_ERR_UNSUPPORTED;
+    Op kop;
+    switch (op) {
+        case LTXNORM_OP_RMSNORM: kop = Op::kRmsNorm; break;
+        case LTXNORM_OP_ROPE: kop = Op::kRopeRotateHalf; break;
+        case LTXNORM_OP_ROPE_INTERLEAVED: kop = Op::kRopeInterleaved; break;
+        case LTXNORM_OP_ADALN: kop = Op::kAdaLN; break;
+        default: return LTXNORM_ERR_UNSUPPORTED;
+    }
+    // the entry points' shape checks (in their order)
+    const bool rope = kop == Op::kRopeRotateHalf || kop == Op::kRopeInterleaved;
+    ltxnorm_status st = rope ? check_rope_shape(hidden, heads, head_dim, 1) : LTXNORM_OK;
+    if (st == LTXNORM_OK) st = check_shape(rows, hidden, 1e-6f, dtype);
+    if (st != LTXNORM_OK) return st;
+    const Request r{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, rows,
+                    hidden, 1, 1, rope ? head_dim : 0, 1e-6f};
+    const ltxnorm_detail::Choice c = ltxnorm_detail::choose(kop, r, epv);
+    using ltxnorm_detail::Kernel;
+    const char* name = ltxnorm_detail::kernel_name(c.kernel);
+    if (len == 0) return LTXNORM_OK;
+    if (c.kernel == Kernel::kNone) {
+        std::snprintf(buf, len, "none");
+    } else if (c.kernel == Kernel::kLong) {
+        std::snprintf(buf, len, "%s passes=2 rows_per_block=1 threads=%d lds_bytes=0", name,
+                      ltxnorm_detail::kLongThreads);
+    } else {
+        const int rpb = ltxnorm_detail::rows_per_block(c.plan.wpr);
+        std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld",
+                      name, c.plan.wpr, c.kernel == Kernel::kRopePair ? "pairs_per_lane" : "vectors_per_lane",
+                      c.plan.per, rpb, ltxnorm_detail::kWave * c.plan.wpr * rpb,
+                      (long long)(c.lds_per_row * rpb));
+    }
+    return LTXNORM_OK;
 }
 
 LTXNORM_API const char* ltxnorm_status_str(ltxnorm_status s) {

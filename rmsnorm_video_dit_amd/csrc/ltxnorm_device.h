@@ -61,10 +61,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
-constexpr int kMaxVecPerLane = 8;     // register budget for one row slice
-constexpr int kMaxWavesPerRow = 16;   // 1024-thread workgroup
-constexpr int64_t kMaxGrid = 1 << 30; // rows beyond grid * rows-per-block loop
 
 // ---------------------------------------------------------------------------
 // I/O element types.  kEpv values per 16-byte vector; kOne and kNegZero are
@@ -201,7 +197,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // 2-3 wavefronts, one row of 4-16 wavefronts (256-1024 threads).
 template <int WPR>
 struct Layout {
-    static constexpr int kRowsPerBlock = WPR == 1 ? 4 : (WPR <= 3 ? 2 : 1);
+    static constexpr int kRowsPerBlock = rows_per_block(WPR);
     static constexpr int kThreads = kWave * WPR * kRowsPerBlock;
     static constexpr int kLanesPerRow = kWave * WPR;
 };

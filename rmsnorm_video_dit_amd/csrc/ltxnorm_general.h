@@ -40,8 +40,7 @@ namespace {
 // Operation of a general kernel.
 enum class GOp { kRms, kAda, kRopeHalf, kRopeIl };
 
-constexpr int kLongThreads = 1024;                  // one row per workgroup
-constexpr int kLongWaves = kLongThreads / kWave;
+constexpr int kLongWaves = kLongThreads / kWave;     // one row per workgroup
 // vectors in flight per thread (fp32 rows keep two: four spill at 1024 threads)
 template <typename IO>
 constexpr int kLongUnroll = IO::kEpv == 8 ? 4 : 2;

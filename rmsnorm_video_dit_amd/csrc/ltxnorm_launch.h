@@ -35,6 +35,153 @@ struct Request {
     float eps;
 };
 
+// Launch geometry shared by the host-side choice below and the kernels.
+constexpr int kWave = 64;                 // lanes per wavefront
+constexpr int kMaxVecPerLane = 8;         // register budget for one row slice
+constexpr int kMaxWavesPerRow = 16;       // 1024-thread workgroup
+constexpr int64_t kMaxGrid = 1 << 30;     // rows beyond grid * rows-per-block loop
+// Register budget of the one-pass kernels, in 16-byte vectors per row.
+constexpr int64_t kMaxRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMaxVecPerLane;
+// The general kernel also holds two weight chunks per vector: at most five
+// vectors per lane (more spill at 16 wavefronts); longer rows take the
+// two-pass kernel.
+constexpr int kMaxGeneralVecPerLane = 5;
+constexpr int64_t kMaxGeneralRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMaxGeneralVecPerLane;
+// Dynamic LDS the rotate-half general kernel may take per workgroup.
+constexpr int64_t kMaxExchangeLds = 64 * 1024 - 256;
+constexpr int kLongThreads = 1024;        // two-pass kernel: one row per workgroup
+
+// How a row is split over lanes.
+struct Plan {
+    int wpr;    // wavefronts per row
+    int per;    // vectors (or pair units) per lane
+    bool full;  // no masking needed
+};
+
+// How a row is split.  `items` are 16-byte vectors, or pair units of two
+// vectors.  A single wavefront takes the row while each lane holds at most
+// `one_wave_max` items; longer rows are spread over enough wavefronts (up to
+// 16) that each lane holds about `spread` items, and past 16 wavefronts the
+// lanes take more, up to the register budget.  Measured at [16384 x 3072]
+// bf16 (384 vectors per row): 3 wavefronts x 2 vectors reached 6.08 TB/s,
+// 2 x 3 6.02, 1 x 6 5.98, 6 x 1 5.46; at hidden 2048 one wavefront x 4
+// vectors was best (6.11 TB/s) and 4 x 1 the worst.
+inline Plan plan_for(int64_t items, int one_wave_max, int spread) {
+    int wpr = 1;
+    if (items > (int64_t)kWave * one_wave_max) {
+        const int64_t w = (items + (int64_t)kWave * spread - 1) / ((int64_t)kWave * spread);
+        wpr = (int)(w < kMaxWavesPerRow ? w : kMaxWavesPerRow);
+    }
+    const int64_t lanes = (int64_t)kWave * wpr;
+    const int per = (int)((items + lanes - 1) / lanes);
+    return Plan{wpr, per, items == (int64_t)per * lanes};
+}
+
+// Rows per workgroup: four single-wavefront rows, two rows of 2-3
+// wavefronts, one row of 4-16 wavefronts.
+constexpr int rows_per_block(int wpr) { return wpr == 1 ? 4 : (wpr <= 3 ? 2 : 1); }
+
+// The kernel that serves a request.
+enum class Kernel {
+    kNone,                   // nothing to launch (no rows)
+    kRmsNorm,                // rmsnorm_kernel
+    kAdaLN,                  // rmsnorm_adaln_kernel
+    kRopeXor,                // rmsnorm_rope_xor_kernel (power-of-two half heads)
+    kRopePacked,             // rmsnorm_rope_packed_kernel, half heads of whole vectors
+    kRopePackedOdd,          // rmsnorm_rope_packed_kernel, half heads of odd 4-element groups
+    kRopePair,               // rmsnorm_rope_pair_kernel
+    kRopeInterleaved,        // rmsnorm_rope_interleaved_kernel, table slice per slot
+    kRopeInterleavedShared,  // rmsnorm_rope_interleaved_kernel, one table slice per row
+    kGeneral,                // rmsnorm_general_kernel (any row length)
+    kLong,                   // rmsnorm_long_kernel (two passes)
+};
+
+struct Choice {
+    Kernel kernel;
+    Plan plan;            // one-pass kernels: row split
+    int64_t lds_per_row;  // dynamic LDS bytes per row slot (general rotate-half)
+};
+
+// The kernel and row split for a validated request with E elements per
+// 16-byte vector.  Rows of whole vectors within the register budget take
+// the vector kernels (and heads those kernels can pair); other rows that fit
+// take the general one-pass kernel; longer rows the two-pass kernel.
+inline Choice choose(Op op, const Request& r, int E) {
+    const int64_t H = r.hidden;
+    if (r.rows == 0) return Choice{Kernel::kNone, Plan{0, 0, false}, 0};
+    const bool whole = H % E == 0;
+    // most vectors one row touches (a row that starts inside a vector
+    // touches up to two more than H / E)
+    const int64_t touched = whole ? H / E : (H + 2 * E - 2) / E;
+    const bool fits = touched <= kMaxRowVectors;
+    const bool gfits = touched <= kMaxGeneralRowVectors;
+    const Plan gp = plan_for(touched, 4, 2);
+    const Choice general{Kernel::kGeneral, gp, 0};
+    const Choice two_pass{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0};
+    const int64_t nvec = H / E;
+    switch (op) {
+        case Op::kRmsNorm:
+            if (whole && fits) return Choice{Kernel::kRmsNorm, plan_for(nvec, 4, 2), 0};
+            return gfits ? general : two_pass;
+        case Op::kAdaLN:
+            if (whole && fits) return Choice{Kernel::kAdaLN, plan_for(nvec, 4, 2), 0};
+            return gfits ? general : two_pass;
+        case Op::kRopeRotateHalf: {
+            const int d = r.head_dim;
+            const bool even = d % (2 * E) == 0;                 // half heads of whole vectors
+            const bool odd = E == 8 && d % E == 0 && !even;     // ... of 4-element groups
+            if (whole && fits && even) {
+                const int P = d / (2 * E);
+                if ((P & (P - 1)) == 0 && P <= kWave / 2)  // partner lanes within one wavefront
+                    return Choice{Kernel::kRopeXor, plan_for(nvec, 4, 2), 0};
+            }
+            const int vph = d / E;
+            if (whole && fits && (even || odd) && vph <= kWave / 2) {
+                // heads packed into wavefronts (lw of 64 lanes used)
+                const int lw = kWave - kWave % vph;
+                Plan p = plan_for((nvec * kWave + lw - 1) / lw, 4, 2);
+                p.per = (int)((nvec + (int64_t)lw * p.wpr - 1) / ((int64_t)lw * p.wpr));
+                p.full = false;
+                if (p.per <= kMaxVecPerLane)
+                    return Choice{odd ? Kernel::kRopePackedOdd : Kernel::kRopePacked, p, 0};
+            }
+            if (whole && fits && even) return Choice{Kernel::kRopePair, plan_for(H / (2 * E), 2, 1), 0};
+            const int64_t lds_row = H * (int64_t)sizeof(float);
+            if (gfits && lds_row * rows_per_block(gp.wpr) <= kMaxExchangeLds)
+                return Choice{Kernel::kGeneral, gp, lds_row};
+            return two_pass;
+        }
+        case Op::kRopeInterleaved: {
+            if (whole && fits && r.head_dim % E == 0) {
+                const Plan p = plan_for(nvec, 4, 2);
+                const int vph = r.head_dim / E;
+                return Choice{(kWave * p.wpr) % vph == 0 ? Kernel::kRopeInterleavedShared
+                                                         : Kernel::kRopeInterleaved,
+                              p, 0};
+            }
+            return gfits ? general : two_pass;
+        }
+    }
+    return Choice{Kernel::kNone, Plan{0, 0, false}, 0};
+}
+
+inline const char* kernel_name(Kernel k) {
+    switch (k) {
+        case Kernel::kNone: return "none";
+        case Kernel::kRmsNorm: return "rmsnorm_kernel";
+        case Kernel::kAdaLN: return "rmsnorm_adaln_kernel";
+        case Kernel::kRopeXor: return "rmsnorm_rope_xor_kernel";
+        case Kernel::kRopePacked: return "rmsnorm_rope_packed_kernel";
+        case Kernel::kRopePackedOdd: return "rmsnorm_rope_packed_kernel(odd)";
+        case Kernel::kRopePair: return "rmsnorm_rope_pair_kernel";
+        case Kernel::kRopeInterleaved: return "rmsnorm_rope_interleaved_kernel";
+        case Kernel::kRopeInterleavedShared: return "rmsnorm_rope_interleaved_kernel(shared)";
+        case Kernel::kGeneral: return "rmsnorm_general_kernel";
+        case Kernel::kLong: return "rmsnorm_long_kernel";
+    }
+    return "?";
+}
+
 // Elements per 16-byte vector for an I/O dtype (8 for 16-bit types, 4 for
 // binary32), or 0 for an unknown dtype.
 inline int elems_per_vec(ltxnorm_dtype d) {

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     ops = ["ltxnorm_rmsnorm_adaln_fwd", "ltxnorm_rmsnorm_fwd", "ltxnorm_rmsnorm_rope_fwd",
            "ltxnorm_rmsnorm_rope_interleaved_fwd"]
     assert declared_functions() == sorted(ops + [o + "_dt" for o in ops] +
-                                          ["ltxnorm_status_str", "ltxnorm_version"])
+                                          ["ltxnorm_describe_launch", "ltxnorm_status_str",
+                                           "ltxnorm_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -235,3 +236,95 @@ def test_error_raises_with_status():
     with pytest.raises(ltx.LtxnormError) as e:
         ltx.ltxnorm_rmsnorm_fwd(A, A + 64 * MB, None, 4, (1 << 24) + 1, 1e-6, 0)
     assert e.value.status == ltx.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Kernel choice (host logic): which kernel and row split serve a shape
+# ---------------------------------------------------------------------------
+
+def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
+    d = ltx.ltxnorm_describe_launch(op, rows, hidden, heads, head_dim, dtype)
+    name, *fields = d.split()
+    return name, dict(f.split("=") for f in fields)
+
+
+@pytest.mark.parametrize("op,hidden,heads,head_dim,dtype,kernel,wpr,per", [
+    # the measured plans: one wavefront x 4 vectors at 2048, 3 x 2 at 3072
+    (ltx.OP_RMSNORM, 2048, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 4),
+    (ltx.OP_RMSNORM, 3072, 0, 0, ltx.BF16, "rmsnorm_kernel", 3, 2),
+    (ltx.OP_RMSNORM, 3072, 0, 0, ltx.F16, "rmsnorm_kernel", 3, 2),
+    (ltx.OP_RMSNORM, 3072, 0, 0, ltx.F32, "rmsnorm_kernel", 6, 2),
+    (ltx.OP_RMSNORM, 65536, 0, 0, ltx.BF16, "rmsnorm_kernel", 16, 8),
+    (ltx.OP_ADALN, 2048, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 1, 4),
+    # rows that are not whole vectors, and rows past the register budget
+    (ltx.OP_RMSNORM, 3076, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 4, 2),
+    (ltx.OP_RMSNORM, 1, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
+    (ltx.OP_ADALN, 3070, 0, 0, ltx.F32, "rmsnorm_general_kernel", 7, 2),
+    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
+    (ltx.OP_RMSNORM, 65529, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
+    (ltx.OP_RMSNORM, 32772, 0, 0, ltx.F32, "rmsnorm_long_kernel", None, None),
+    # rotate-half: power-of-two half heads, head-packed lanes, pairs in a lane,
+    # LDS exchange, two passes
+    (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_xor_kernel", 1, 4),
+    (ltx.OP_ROPE, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 2),
+    (ltx.OP_ROPE, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 3),
+    (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 3, 2),
+    (ltx.OP_ROPE, 960, 24, 40, ltx.F32, "rmsnorm_rope_packed_kernel", 1, 4),
+    (ltx.OP_ROPE, 3072, 3, 1024, ltx.BF16, "rmsnorm_rope_pair_kernel", 3, 1),
+    (ltx.OP_ROPE, 1040, 20, 52, ltx.BF16, "rmsnorm_general_kernel", 1, 3),
+    (ltx.OP_ROPE, 17544, 129, 136, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 16, 3),
+    (ltx.OP_ROPE, 80000, 2, 40000, ltx.BF16, "rmsnorm_long_kernel", None, None),
+    (ltx.OP_ROPE, 65790, 255, 258, ltx.BF16, "rmsnorm_long_kernel", None, None),
+    # interleaved: one table slice per row when a head's vectors divide the lanes
+    (ltx.OP_ROPE_INTERLEAVED, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 1, 4),
+    (ltx.OP_ROPE_INTERLEAVED, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 3),
+    (ltx.OP_ROPE_INTERLEAVED, 70, 7, 10, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
+])
+def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
+    name, f = _describe(op, hidden, heads, head_dim, dtype)
+    assert name == kernel, (name, f)
+    if wpr is not None:
+        assert int(f["wavefronts_per_row"]) == wpr
+        per_key = "pairs_per_lane" if "pair" in name else "vectors_per_lane"
+        assert int(f[per_key]) == per
+        assert int(f["threads"]) == 64 * wpr * int(f["rows_per_block"])
+    else:
+        assert f["passes"] == "2" and f["threads"] == "1024"
+
+
+def test_kernel_choice_lds_and_limits():
+    """The LDS exchange takes one binary32 row per row slot; shapes that the
+    entry points refuse are refused with the same status; no rows, no launch."""
+    name, f = _describe(ltx.OP_ROPE, 1040, 20, 52)
+    assert int(f["lds_bytes"]) == 1040 * 4 * int(f["rows_per_block"])
+    assert ltx.ltxnorm_describe_launch(ltx.OP_RMSNORM, 0, 2048) == "none"
+    for args, status in (((ltx.OP_ROPE, 16, 2048, 16, 64), ltx.ERR_SHAPE),
+                         ((ltx.OP_ROPE, 16, 96, 32, 3), ltx.ERR_SHAPE),
+                         ((ltx.OP_RMSNORM, 16, (1 << 24) + 1, 0, 0), ltx.ERR_UNSUPPORTED),
+                         ((ltx.OP_RMSNORM, -1, 2048, 0, 0), ltx.ERR_SHAPE),
+                         ((7, 16, 2048, 0, 0), ltx.ERR_UNSUPPORTED)):
+        with pytest.raises(ltx.LtxnormError) as e:
+            ltx.ltxnorm_describe_launch(*args)
+        assert e.value.status == status, args
+    lib = ltx.lib()
+    assert lib.ltxnorm_describe_launch(0, 16, 2048, 0, 0, 0, None, 0) == ltx.OK
+    assert lib.ltxnorm_describe_launch(0, 16, 2048, 0, 0, 0, None, 8) == ltx.ERR_NULL
+    buf = ctypes.create_string_buffer(8)
+    assert lib.ltxnorm_describe_launch(0, 16, 3072, 0, 0, 0, buf, 8) == ltx.OK
+    assert buf.value == b"rmsnorm"  # truncated, NUL-terminated
+
+
+def test_kernel_choice_covers_the_benchmark_workloads():
+    """Every benchmark workload maps to the kernel its profile names."""
+    import datagen
+    expect = {"rms_4x4096x3072": "rmsnorm_kernel", "rope_2x4096x2048_h32d64": "rmsnorm_rope_xor_kernel",
+              "ropei_2x4096x2048_h32d64": "rmsnorm_rope_interleaved_kernel(shared)",
+              "adaln_2x4096x2048": "rmsnorm_adaln_kernel", "rms_4x4096x3076": "rmsnorm_general_kernel",
+              "rope_2x4096x1152_h16d72": "rmsnorm_rope_packed_kernel(odd)",
+              "rms_1x256x262144": "rmsnorm_long_kernel"}
+    for name, kernel in expect.items():
+        cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[name]
+        op = (ltx.OP_ADALN if cfg.adaln else ltx.OP_ROPE_INTERLEAVED if cfg.interleaved
+              else ltx.OP_ROPE if cfg.rope else ltx.OP_RMSNORM)
+        got = ltx.ltxnorm_describe_launch(op, cfg.rows, cfg.hidden, cfg.heads, cfg.head_dim)
+        assert got.split()[0] == kernel, (name, got)

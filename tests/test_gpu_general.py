@@ -81,7 +81,8 @@ def test_long_rows(dtype, hidden, rows):
 
 
 # (heads, head_dim): head sizes the vector kernels cannot pair, rows that are
-# not whole vectors, and rows beyond the LDS exchange (two-pass)
+# not whole vectors; LONG_ROPE: long rows (head-packed for 129 x 136, the
+# two-pass kernel for the rest)
 ROPE_SHAPES = [(1, 2), (33, 2), (5, 6), (7, 10), (4, 24), (16, 72), (32, 40), (3, 130),
                (2, 136), (24, 88), (13, 14), (1, 1000), (9, 18), (20, 52)]
 LONG_ROPE = [(129, 136), (2, 40000), (1, 70002), (255, 258), (64, 1026)]
