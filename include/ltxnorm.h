@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LTXNORM_ABI_VERSION 3
+#define LTXNORM_ABI_VERSION 4
 
 #define LTXNORM_API __attribute__((visibility("default")))
 

@@ -52,7 +52,7 @@ def test_library_targets_gfx950_only():
 
 
 def test_version_and_status_strings():
-    assert ltx.ltxnorm_version() == 3
+    assert ltx.ltxnorm_version() == 4
     seen = set()
     for code in range(8):
         s = ltx.ltxnorm_status_str(code)
