@@ -58,8 +58,7 @@ H100_GBPS_4x4096x3072 = 201_332_736 / 0.157e-3 / 1e9
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 KERNEL_SOURCES = (sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.hip")))
-                  + sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.h")))
-                  + [os.path.join(ROOT, "include", "ltxnorm.h")])
+                  + sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.h"))))
 DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
 PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datagen.HEADLINE,
           "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
