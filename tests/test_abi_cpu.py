@@ -9,6 +9,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import rmsnorm_video_dit_amd as ltx
@@ -328,3 +329,68 @@ def test_kernel_choice_covers_the_benchmark_workloads():
               else ltx.OP_ROPE if cfg.rope else ltx.OP_RMSNORM)
         got = ltx.ltxnorm_describe_launch(op, cfg.rows, cfg.hidden, cfg.heads, cfg.head_dim)
         assert got.split()[0] == kernel, (name, got)
+
+
+def test_kernel_choice_always_covers_the_row():
+    """For seeded random shapes in every dtype and operation, the plan the
+    library picks covers every vector (or pair unit) of the row with its
+    lanes, within the kernel's limits: the property every launch relies on."""
+    rng = np.random.default_rng(20261202)
+    epv = {ltx.BF16: 8, ltx.F16: 8, ltx.F32: 4}
+    seen = set()
+    for _ in range(1500):
+        dtype = int(rng.choice([ltx.BF16, ltx.F16, ltx.F32]))
+        E = epv[dtype]
+        op = int(rng.integers(0, 4))
+        if op in (ltx.OP_ROPE, ltx.OP_ROPE_INTERLEAVED):
+            d = 2 * int(rng.choice([rng.integers(1, 40), rng.integers(1, 600), 32, 36, 64]))
+            heads = int(rng.integers(1, max(2, min(200, 70000 // d))))
+            H = heads * d
+        else:
+            d = heads = 0
+            H = int(rng.choice([rng.integers(1, 9000), rng.integers(1, 80000), 8 * rng.integers(1, 9000)]))
+        rows = int(rng.integers(1, 5000))
+        desc = ltx.ltxnorm_describe_launch(op, rows, H, heads, d, dtype)
+        name, *fields = desc.split()
+        f = dict(x.split("=") for x in fields)
+        seen.add(name)
+        whole = H % E == 0
+        touched = H // E if whole else (H + 2 * E - 2) // E
+        if name == "rmsnorm_long_kernel":
+            assert f["threads"] == "1024"
+            continue
+        wpr, rpb, threads = int(f["wavefronts_per_row"]), int(f["rows_per_block"]), int(f["threads"])
+        assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024 and wpr != 2
+        assert rpb == (4 if wpr == 1 else 2 if wpr <= 3 else 1)
+        if name == "rmsnorm_rope_pair_kernel":
+            per = int(f["pairs_per_lane"])
+            assert whole and d % (2 * E) == 0 and 64 * wpr * per >= H // (2 * E) and per <= 4
+            continue
+        per = int(f["vectors_per_lane"])
+        if name == "rmsnorm_general_kernel":
+            assert 64 * wpr * per >= touched and per <= 5
+            if op == ltx.OP_ROPE:
+                assert int(f["lds_bytes"]) == 4 * H * rpb <= 64 * 1024 - 256
+            continue
+        assert whole and int(f["lds_bytes"]) == 0 and per <= 8
+        nvec = H // E
+        if name.startswith("rmsnorm_rope_packed_kernel"):
+            vph = d // E
+            lw = 64 - 64 % vph
+            assert vph <= 32 and lw * wpr * per >= nvec
+            assert (d % (2 * E) == 0) != name.endswith("(odd)")
+            continue
+        assert 64 * wpr * per >= nvec
+        if name == "rmsnorm_rope_xor_kernel":
+            P = d // (2 * E)
+            assert d % (2 * E) == 0 and P & (P - 1) == 0 and P <= 32
+        elif name.startswith("rmsnorm_rope_interleaved_kernel"):
+            assert d % E == 0
+            assert name.endswith("(shared)") == ((64 * wpr) % (d // E) == 0)
+        else:
+            assert name in ("rmsnorm_kernel", "rmsnorm_adaln_kernel"), desc
+    # the sample reaches every kernel family
+    assert {"rmsnorm_kernel", "rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel",
+            "rmsnorm_rope_packed_kernel", "rmsnorm_rope_packed_kernel(odd)", "rmsnorm_rope_pair_kernel",
+            "rmsnorm_rope_interleaved_kernel", "rmsnorm_rope_interleaved_kernel(shared)",
+            "rmsnorm_general_kernel", "rmsnorm_long_kernel"} <= seen, seen
