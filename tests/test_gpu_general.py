@@ -383,3 +383,45 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         for b, r in zip(bufs, replayed):
             assert np.array_equal(host_bits(b[5]), r), (seed, b[:4])
+
+
+def _random_cases(n=96, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+        op = ["rms", "adaln", "half", "il"][int(rng.integers(0, 4))]
+        if op in ("half", "il"):
+            d = 2 * int(rng.choice([rng.integers(1, 40), rng.integers(1, 300), 32, 36, 64]))
+            heads = int(rng.integers(1, max(2, min(64, 40000 // d))))
+            hidden = heads * d
+        else:
+            d = heads = 0
+            hidden = int(rng.choice([rng.integers(1, 5000), rng.integers(1, 70000), 8 * rng.integers(1, 3000)]))
+        rows = int(rng.integers(1, max(2, min(64, 400000 // hidden))))
+        cases.append((i, dtype, op, rows, hidden, heads, d))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}x{c[4]}")
+def test_random_shapes(case):
+    """Seeded random shapes across operations and dtypes (whichever kernel
+    the library picks for each) against the oracle."""
+    i, dtype, op, rows, hidden, heads, d = case
+    announce(f"random shape {case} -> "
+             + ltx.ltxnorm_describe_launch({"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "half": ltx.OP_ROPE,
+                                            "il": ltx.OP_ROPE_INTERLEAVED}[op], rows, hidden, heads, d,
+                                           {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]))
+    x = datagen.make_x(rows, hidden, seed=1000 + i, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=1000 + i, stream=2, dtype=dtype)
+    if op in ("half", "il"):
+        c, s = datagen.rope_tables(int(1 + i % 7), d)
+        check_rope(x, w, c, s, heads, d, interleaved=(op == "il"), label=str(case))
+    elif op == "adaln":
+        rps = max(1, rows // 2)
+        samples = -(-rows // rps)
+        sc = datagen.make_x(samples, hidden, seed=2000 + i, stream=4, sigma=0.25, dtype=dtype)
+        sh = datagen.make_x(samples, hidden, seed=2000 + i, stream=5, sigma=0.25, dtype=dtype)
+        check_adaln(x, w, sc, sh, rps, label=str(case))
+    else:
+        check_rms(x, w, label=str(case))
