@@ -176,7 +176,7 @@ def pin_brute_force_exact(o):
     reference within one binary32 ulp of the exact value."""
     rng = np.random.default_rng(23)
     rows = []
-    for hidden in (1, 2, 8, 16, 64):
+    for hidden in (1, 2, 3, 7, 8, 16, 64):
         rows.append(_rand_bf16(rng, (hidden,)))
         rows.append(_rand_bf16(rng, (hidden,), scale=1e-5))
         mixed = rng.standard_normal(hidden) * np.where(rng.random(hidden) < 0.2, 300.0, 1e-3)
@@ -338,6 +338,28 @@ def pin_rope_il_complex_rotation(o):
                 rot = complex(a, b) * complex(float(c[r, i]), float(s[r, i]))
                 got = complex(y[r, h * d + 2 * i], y[r, h * d + 2 * i + 1])
                 assert cmath.isclose(got, rot, rel_tol=1e-14, abs_tol=1e-300), (r, h, i)
+
+
+def pin_rope_small_and_odd_halves(o):
+    """Heads of 2, 6 and 10 elements (half heads of 1, 3 and 5 pairs; rows
+    that are not whole 16-byte vectors), both pairings: every pair is the
+    complex product of its normalised values and the phasor c + is."""
+    rng = np.random.default_rng(61)
+    for d, heads in ((2, 5), (6, 3), (10, 7)):
+        seq = 3
+        x = _rand_bf16(rng, (seq, heads * d))
+        w = datagen.to_bf16_bits(rng.uniform(0.5, 1.5, heads * d))
+        c, s = _tables(np.arange(seq) * 5 + 2, d)
+        z = o.rmsnorm(x, w, 1e-6)
+        for interleaved in (False, True):
+            y = o.rmsnorm_rope(x, w, c, s, heads, d, 1e-6, interleaved=interleaved)
+            for r in range(seq):
+                for h in range(heads):
+                    for i in range(d // 2):
+                        ia, ib = (h * d + 2 * i, h * d + 2 * i + 1) if interleaved else (h * d + i, h * d + i + d // 2)
+                        rot = complex(z[r, ia], z[r, ib]) * complex(float(c[r, i]), float(s[r, i]))
+                        got = complex(y[r, ia], y[r, ib])
+                        assert cmath.isclose(got, rot, rel_tol=1e-14, abs_tol=1e-300), (d, interleaved, r, h, i)
 
 
 def pin_rope_il_matches_rotate_half_after_reorder(o):
@@ -645,7 +667,7 @@ PINS = [
     pin_rope_position_zero_is_rmsnorm, pin_rope_complex_rotation, pin_rope_pair_norm,
     pin_rope_constant_row, pin_rope_row_position, pin_rope_mag,
     pin_rope_il_position_zero_is_rmsnorm, pin_rope_il_complex_rotation,
-    pin_rope_il_matches_rotate_half_after_reorder, pin_rope_il_constant_row, pin_rope_il_mag,
+    pin_rope_small_and_odd_halves, pin_rope_il_matches_rotate_half_after_reorder, pin_rope_il_constant_row, pin_rope_il_mag,
     pin_adaln_zero_modulation_is_rmsnorm, pin_adaln_scale_minus_one_gives_shift,
     pin_adaln_exact_closed_form, pin_adaln_sample_rows, pin_adaln_brute_force, pin_adaln_mag,
     pin_bf16_rounding, pin_round_twice,
