@@ -106,6 +106,10 @@ __device__ __forceinline__ u32x4 take(const uint32_t* W) {
     return r;
 }
 
+// The same for a shift f known only at run time but uniform across the
+// wavefront: a chain of uniform branches, each with compile-time indices (a
+// select over the words instead was turned into a runtime-indexed array in
+// private memory and measured 12 points of peak slower).
 template <typename IO, int F = 1>
 __device__ __forceinline__ u32x4 take_at(const uint32_t* W, int f) {
     if constexpr (F >= IO::kEpv) {
