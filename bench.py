@@ -249,11 +249,32 @@ def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict
             if el >= budget_s:
                 break
     per_pass = el / passes
+
+    # one thread on a 2048-row slice of the batch, for about 3 s
+    sub = np.arange(min(2048, cfg.rows))
+    sub_bytes = 4 * len(sub) * cfg.hidden + 2 * cfg.hidden
+    n1 = 0
+    t1 = time.perf_counter()
+    while True:
+        work(sub)
+        n1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= budget_s * 0.3:
+            break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(gbps(cfg.algorithmic_bytes(), per_pass), 3), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": f"full {cfg.name} batch ({cfg.rows} rows x {cfg.hidden}), {passes} passes "
                       f"in {el:.1f} s; double arithmetic + rounding to bf16; "
-                      f"{per_pass * 1e3:.1f} ms per pass"}
+                      f"{per_pass * 1e3:.1f} ms per pass",
+            "single_thread": {"value": round(gbps(sub_bytes, el1 / n1), 3), "unit": "GB/s",
+                              "sample": f"{len(sub)} rows x {cfg.hidden}, {n1} passes in {el1:.1f} s"},
+            "cpu_model": model}
 
 
 def probe(kind: str, launches: int):
