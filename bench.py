@@ -25,11 +25,12 @@ cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
 "rms_f16" / "rms_f32", three shapes outside the pages' set under "general"
 (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
-rotate-half pairs; rows of 262144, beyond the register budget), and the CPU
-oracle timed on this host under "cpu_baseline".  Prints one JSON line.
+rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
+of 128), and the CPU oracle timed on this host under "cpu_baseline".  Prints
+one JSON line.
 
---probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|copy runs
-a few launches only, for rocprofv3 counter passes.
+--probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|rms_short|copy
+runs a few launches only, for rocprofv3 counter passes.
 """
 from __future__ import annotations
 
@@ -63,7 +64,7 @@ DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
 PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datagen.HEADLINE,
           "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
           "rms_odd": "rms_4x4096x3076", "rope_d72": "rope_2x4096x1152_h16d72",
-          "rms_long": "rms_1x256x262144"}
+          "rms_long": "rms_1x256x262144", "rms_short": "rms_2x4096x24_d128"}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
@@ -415,7 +416,8 @@ def main():
         for name, kernel, path in (
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
                 ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
-                ("rms_1x256x262144", "rmsnorm_long", "two-pass")):
+                ("rms_1x256x262144", "rmsnorm_long", "two-pass"),
+                ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, 4 per wavefront")):
             rc = datagen.GENERAL_CONFIGS[name]
             rw = Workload(rc, dev, stream)
             rsec = rw.time_steps(args.steps, args.warmup, graph)

@@ -222,12 +222,16 @@ CONFIGS = {
 # Shapes outside the pages' set that exercise the kernels for rows of any
 # length, with the same value recipe: a hidden size that is not a whole number
 # of 16-byte vectors, a head size the vector kernels cannot pair (16 heads x
-# 72, rotate-half), and rows longer than the register budget.
+# 72, rotate-half), rows longer than the register budget, and rows of one
+# head (per-head normalisation).
 GENERAL_CONFIGS = {
     "rms_4x4096x3076": Config("rms_4x4096x3076", 9, 4, 4096, 3076),
     "rope_2x4096x1152_h16d72": Config("rope_2x4096x1152_h16d72", 10, 2, 4096, 1152,
                                       heads=16, head_dim=72, theta=10000.0),
     "rms_1x256x262144": Config("rms_1x256x262144", 11, 1, 256, 262144),
+    # per-head normalisation (query/key norm): rows of one 128-element head,
+    # [2 x 4096 x 24 heads] of them
+    "rms_2x4096x24_d128": Config("rms_2x4096x24_d128", 12, 2, 4096 * 24, 128),
 }
 HEADLINE = "rms_4x4096x3072"
 ROPE = "rope_2x4096x2048_h32d64"

@@ -134,6 +134,10 @@ struct IoF32 {
     }
 };
 
+// Operation of a kernel that serves several: RMSNorm, AdaLN, rotate-half
+// RoPE, interleaved RoPE.
+enum class GOp { kRms, kAda, kRopeHalf, kRopeIl };
+
 __device__ __forceinline__ u32x4 splat(uint32_t w) { return u32x4{w, w, w, w}; }
 
 // Keep a packed register value opaque to the optimiser, so that it is

@@ -113,6 +113,22 @@ ltxnorm_status launch_long(const KArgs& a, hipStream_t stream) {
     return launch((const void*)&rmsnorm_long_kernel<IO, OP>, kLongThreads, 1, a, 0, stream);
 }
 
+// Short rows: the instance for the lanes per row.
+template <typename IO, GOp OP>
+ltxnorm_status launch_short(int lanes, const KArgs& a, hipStream_t stream) {
+    const void* fn = nullptr;
+    switch (lanes) {
+        case 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 1>; break;
+        case 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 2>; break;
+        case 4: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 4>; break;
+        case 8: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 8>; break;
+        case 16: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16>; break;
+        case 32: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32>; break;
+        default: return LTXNORM_ERR_UNSUPPORTED;
+    }
+    return launch(fn, kWave * kShortWavesPerBlock, kShortWavesPerBlock * (kWave / lanes), a, 0, stream);
+}
+
 template <typename IO, GOp OP>
 ltxnorm_status launch_general(const Choice& c, const KArgs& a, hipStream_t stream) {
     if (c.kernel == Kernel::kLong) return launch_long<IO, OP>(a, stream);
@@ -147,6 +163,14 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
             return by_plan<RopeIlL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kRopeInterleavedShared:
             return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+        case Kernel::kShort:
+            switch (op) {
+                case Op::kRmsNorm: return launch_short<IO, GOp::kRms>(c.lanes_per_row, a, stream);
+                case Op::kAdaLN: return launch_short<IO, GOp::kAda>(c.lanes_per_row, a, stream);
+                case Op::kRopeRotateHalf: return launch_short<IO, GOp::kRopeHalf>(c.lanes_per_row, a, stream);
+                case Op::kRopeInterleaved: return launch_short<IO, GOp::kRopeIl>(c.lanes_per_row, a, stream);
+            }
+            return LTXNORM_ERR_UNSUPPORTED;
         case Kernel::kGeneral:
         case Kernel::kLong:
             switch (op) {

@@ -37,9 +37,6 @@
 namespace ltxnorm_detail {
 namespace {
 
-// Operation of a general kernel.
-enum class GOp { kRms, kAda, kRopeHalf, kRopeIl };
-
 constexpr int kLongWaves = kLongThreads / kWave;     // one row per workgroup
 // vectors in flight per thread (fp32 rows keep two: four spill at 1024 threads)
 template <typename IO>

@@ -54,6 +54,122 @@ rmsnorm_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Short rows (at most 32 vectors: H <= 256 bf16/fp16 or 128 fp32, as in
+// per-head normalisation).  S lanes per row, S the power of two at or above
+// the row's vector count, one vector per lane, 64 / S rows per wavefront and
+// four wavefronts per workgroup: a load instruction covers 64 / S
+// consecutive rows, where one wavefront per row would leave most lanes idle
+// (H = 128 measured 28 % of peak that way).  The sum of squares is reduced
+// inside each S-lane segment by the first log2 S steps of the wavefront
+// reduction (and an xor-16 exchange for S = 32), so every lane of a row ends
+// with the same bits.  RMSNorm, AdaLN, and RoPE whose partners stay inside a
+// row's lanes: rotate-half with power-of-two half heads (partner lane
+// l ^ P) and interleaved pairs.
+// ---------------------------------------------------------------------------
+template <int S>
+__device__ __forceinline__ float segment_sum(float v) {
+    if constexpr (S >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: xor 1
+    if constexpr (S >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: xor 2
+    if constexpr (S >= 8) v += dpp<0x141>(v);   // row_half_mirror: 8 lanes
+    if constexpr (S >= 16) v += dpp<0x140>(v);  // row_mirror: 16 lanes
+    if constexpr (S >= 32) {                    // the other 16 lanes
+        const int src = (((int)threadIdx.x & (kWave - 1)) ^ 16) << 2;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+    }
+    return v;
+}
+
+
+template <typename IO, GOp OP, int S>
+__global__ void __launch_bounds__(kWave * kShortWavesPerBlock)
+rmsnorm_short_kernel(const KArgs a) {
+    constexpr int E = IO::kEpv;
+    constexpr int G = kWave / S;           // rows per wavefront
+    constexpr int RPB = kShortWavesPerBlock * G;   // rows per workgroup
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int l = lane % S;                // vector within the row
+    const int seg = lane / S;              // row within the wavefront
+    const bool lin = l < a.nvec;
+    u32x4 wv = (a.w != nullptr && lin) ? reinterpret_cast<const u32x4*>(a.w)[l] : splat(IO::kOne);
+
+    // rotation constants of this lane (the xor layout of the power-of-two
+    // kernel, within the row's lanes; or the interleaved table columns)
+    int src = 0, toff = 0;
+    float sgn = 1.0f;
+    if constexpr (OP == GOp::kRopeHalf) {
+        const int P = a.vec_per_half;
+        src = (lane ^ P) << 2;
+        sgn = (l & P) ? 1.0f : -1.0f;
+        toff = (l & (P - 1)) * E;
+    } else if constexpr (OP == GOp::kRopeIl) {
+        toff = (l % a.vec_per_head) * (E / 2);
+    }
+
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows; base += (int64_t)gridDim.x * RPB) {
+        const int64_t row = base + wave * G + seg;
+        const bool in = lin && row < a.rows;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+        u32x4 xv = in ? load_stream(xr + l) : u32x4{0u, 0u, 0u, 0u};
+
+        // per-row side inputs, fetched together with x
+        u32x4 sv = {0u, 0u, 0u, 0u}, hv = splat(IO::kNegZero);
+        float c[E], sn[E];
+        if constexpr (OP == GOp::kAda) {
+            const int64_t sample = in ? row / a.rows_per_sample : 0;
+            if (a.scale != nullptr && in) sv = reinterpret_cast<const u32x4*>(a.scale)[sample * a.nvec + l];
+            if (a.shift != nullptr && in) hv = reinterpret_cast<const u32x4*>(a.shift)[sample * a.nvec + l];
+        } else if constexpr (OP == GOp::kRopeHalf) {
+            const int64_t pos = in ? row % a.seq_len : 0;
+            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
+            load_floats<E>(a.sin_tab + pos * a.half + toff, sn);
+        } else if constexpr (OP == GOp::kRopeIl) {
+            const int64_t pos = in ? row % a.seq_len : 0;
+            load_floats<E / 2>(a.cos_tab + pos * a.half + toff, c);
+            load_floats<E / 2>(a.sin_tab + pos * a.half + toff, sn);
+        }
+
+        float f[E], g[E];
+        IO::widen(xv, f);
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) part = fmaf(f[e], f[e], part);
+        const float rstd = rstd_of(segment_sum<S>(part), a.hidden_f, a.eps);
+        keep_packed(wv);
+        IO::widen(wv, g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
+
+        float o[E];
+        if constexpr (OP == GOp::kAda) {
+            float sc[E], sh[E];
+            IO::widen(sv, sc);
+            IO::widen(hv, sh);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = f[e] * (1.0f + sc[e]) + sh[e];
+        } else if constexpr (OP == GOp::kRopeHalf) {
+            // the partner lane's normalised values; -sin in the first half
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float par = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, f[e])));
+                o[e] = f[e] * c[e] + par * (sn[e] * sgn);
+            }
+        } else if constexpr (OP == GOp::kRopeIl) {
+#pragma unroll
+            for (int j = 0; j < E / 2; ++j) {
+                o[2 * j] = f[2 * j] * c[j] - f[2 * j + 1] * sn[j];
+                o[2 * j + 1] = f[2 * j + 1] * c[j] + f[2 * j] * sn[j];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = f[e];
+        }
+        if (in) store_stream(yr + l, IO::narrow(o));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // RMSNorm + rotate-half RoPE with the RMSNorm lane layout, when the number
 // of vectors per half head P = head_dim / (2 kEpv) is a power of two up to
 // 32.  Lane t holds vectors k*L + t (full 1 KiB lines per load

@@ -92,15 +92,29 @@ enum class Kernel {
     kRopePair,               // rmsnorm_rope_pair_kernel
     kRopeInterleaved,        // rmsnorm_rope_interleaved_kernel, table slice per slot
     kRopeInterleavedShared,  // rmsnorm_rope_interleaved_kernel, one table slice per row
+    kShort,                  // rmsnorm_short_kernel (rows of at most 32 vectors)
     kGeneral,                // rmsnorm_general_kernel (any row length)
     kLong,                   // rmsnorm_long_kernel (two passes)
 };
+
+// Short rows: lanes per row is the power of two at or above the row's
+// vectors (one vector per lane), 64 / lanes rows per wavefront, four
+// wavefronts per workgroup.
+constexpr int kMaxShortVectors = 32;
+constexpr int kShortWavesPerBlock = 4;
 
 struct Choice {
     Kernel kernel;
     Plan plan;            // one-pass kernels: row split
     int64_t lds_per_row;  // dynamic LDS bytes per row slot (general rotate-half)
+    int lanes_per_row;    // short rows: lanes per row (a power of two <= 32)
 };
+
+inline int pow2_at_least(int64_t n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
 
 // The kernel and row split for a validated request with E elements per
 // 16-byte vector.  Rows of whole vectors within the register budget take
@@ -108,7 +122,7 @@ struct Choice {
 // take the general one-pass kernel; longer rows the two-pass kernel.
 inline Choice choose(Op op, const Request& r, int E) {
     const int64_t H = r.hidden;
-    if (r.rows == 0) return Choice{Kernel::kNone, Plan{0, 0, false}, 0};
+    if (r.rows == 0) return Choice{Kernel::kNone, Plan{0, 0, false}, 0, 0};
     const bool whole = H % E == 0;
     // most vectors one row touches (a row that starts inside a vector
     // touches up to two more than H / E)
@@ -116,15 +130,19 @@ inline Choice choose(Op op, const Request& r, int E) {
     const bool fits = touched <= kMaxRowVectors;
     const bool gfits = touched <= kMaxGeneralRowVectors;
     const Plan gp = plan_for(touched, 4, 2);
-    const Choice general{Kernel::kGeneral, gp, 0};
-    const Choice two_pass{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0};
+    const Choice general{Kernel::kGeneral, gp, 0, 0};
+    const Choice two_pass{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0, 0};
     const int64_t nvec = H / E;
+    const bool short_row = whole && nvec <= kMaxShortVectors;
+    const Choice short_rows{Kernel::kShort, Plan{1, 1, false}, 0, short_row ? pow2_at_least(nvec) : 0};
     switch (op) {
         case Op::kRmsNorm:
-            if (whole && fits) return Choice{Kernel::kRmsNorm, plan_for(nvec, 4, 2), 0};
+            if (short_row) return short_rows;
+            if (whole && fits) return Choice{Kernel::kRmsNorm, plan_for(nvec, 4, 2), 0, 0};
             return gfits ? general : two_pass;
         case Op::kAdaLN:
-            if (whole && fits) return Choice{Kernel::kAdaLN, plan_for(nvec, 4, 2), 0};
+            if (short_row) return short_rows;
+            if (whole && fits) return Choice{Kernel::kAdaLN, plan_for(nvec, 4, 2), 0, 0};
             return gfits ? general : two_pass;
         case Op::kRopeRotateHalf: {
             const int d = r.head_dim;
@@ -132,8 +150,10 @@ inline Choice choose(Op op, const Request& r, int E) {
             const bool odd = E == 8 && d % E == 0 && !even;     // ... of 4-element groups
             if (whole && fits && even) {
                 const int P = d / (2 * E);
-                if ((P & (P - 1)) == 0 && P <= kWave / 2)  // partner lanes within one wavefront
-                    return Choice{Kernel::kRopeXor, plan_for(nvec, 4, 2), 0};
+                if ((P & (P - 1)) == 0 && P <= kWave / 2) {  // partner lanes within one wavefront
+                    if (short_row) return short_rows;     // partner l ^ P inside the row's lanes
+                    return Choice{Kernel::kRopeXor, plan_for(nvec, 4, 2), 0, 0};
+                }
             }
             const int vph = d / E;
             if (whole && fits && (even || odd) && vph <= kWave / 2) {
@@ -143,26 +163,27 @@ inline Choice choose(Op op, const Request& r, int E) {
                 p.per = (int)((nvec + (int64_t)lw * p.wpr - 1) / ((int64_t)lw * p.wpr));
                 p.full = false;
                 if (p.per <= kMaxVecPerLane)
-                    return Choice{odd ? Kernel::kRopePackedOdd : Kernel::kRopePacked, p, 0};
+                    return Choice{odd ? Kernel::kRopePackedOdd : Kernel::kRopePacked, p, 0, 0};
             }
-            if (whole && fits && even) return Choice{Kernel::kRopePair, plan_for(H / (2 * E), 2, 1), 0};
+            if (whole && fits && even) return Choice{Kernel::kRopePair, plan_for(H / (2 * E), 2, 1), 0, 0};
             const int64_t lds_row = H * (int64_t)sizeof(float);
             if (gfits && lds_row * rows_per_block(gp.wpr) <= kMaxExchangeLds)
-                return Choice{Kernel::kGeneral, gp, lds_row};
+                return Choice{Kernel::kGeneral, gp, lds_row, 0};
             return two_pass;
         }
         case Op::kRopeInterleaved: {
             if (whole && fits && r.head_dim % E == 0) {
+                if (short_row) return short_rows;
                 const Plan p = plan_for(nvec, 4, 2);
                 const int vph = r.head_dim / E;
                 return Choice{(kWave * p.wpr) % vph == 0 ? Kernel::kRopeInterleavedShared
                                                          : Kernel::kRopeInterleaved,
-                              p, 0};
+                              p, 0, 0};
             }
             return gfits ? general : two_pass;
         }
     }
-    return Choice{Kernel::kNone, Plan{0, 0, false}, 0};
+    return Choice{Kernel::kNone, Plan{0, 0, false}, 0, 0};
 }
 
 inline const char* kernel_name(Kernel k) {
@@ -176,6 +197,7 @@ inline const char* kernel_name(Kernel k) {
         case Kernel::kRopePair: return "rmsnorm_rope_pair_kernel";
         case Kernel::kRopeInterleaved: return "rmsnorm_rope_interleaved_kernel";
         case Kernel::kRopeInterleavedShared: return "rmsnorm_rope_interleaved_kernel(shared)";
+        case Kernel::kShort: return "rmsnorm_short_kernel";
         case Kernel::kGeneral: return "rmsnorm_general_kernel";
         case Kernel::kLong: return "rmsnorm_long_kernel";
     }

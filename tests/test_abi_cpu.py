@@ -280,11 +280,26 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE_INTERLEAVED, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 1, 4),
     (ltx.OP_ROPE_INTERLEAVED, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 3),
     (ltx.OP_ROPE_INTERLEAVED, 70, 7, 10, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
+    # short rows (at most 32 vectors): lanes per row given in the wpr column
+    (ltx.OP_RMSNORM, 128, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, None),
+    (ltx.OP_RMSNORM, 8, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 1, None),
+    (ltx.OP_RMSNORM, 96, 0, 0, ltx.F16, "rmsnorm_short_kernel", 16, None),
+    (ltx.OP_RMSNORM, 128, 0, 0, ltx.F32, "rmsnorm_short_kernel", 32, None),
+    (ltx.OP_ADALN, 256, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 32, None),
+    (ltx.OP_ROPE, 64, 1, 64, ltx.BF16, "rmsnorm_short_kernel", 8, None),
+    (ltx.OP_ROPE, 256, 2, 128, ltx.BF16, "rmsnorm_short_kernel", 32, None),
+    (ltx.OP_ROPE_INTERLEAVED, 128, 2, 64, ltx.BF16, "rmsnorm_short_kernel", 16, None),
+    (ltx.OP_ROPE, 144, 2, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 1),   # not a power of two
+    (ltx.OP_RMSNORM, 264, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 1),                   # 33 vectors
 ])
 def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
     name, f = _describe(op, hidden, heads, head_dim, dtype)
     assert name == kernel, (name, f)
-    if wpr is not None:
+    if name == "rmsnorm_short_kernel":
+        lanes = int(f["lanes_per_row"])
+        assert lanes == wpr and int(f["rows_per_wavefront"]) == 64 // lanes
+        assert int(f["rows_per_block"]) == 4 * (64 // lanes) and f["threads"] == "256"
+    elif wpr is not None:
         assert int(f["wavefronts_per_row"]) == wpr
         per_key = "pairs_per_lane" if "pair" in name else "vectors_per_lane"
         assert int(f[per_key]) == per
@@ -359,6 +374,17 @@ def test_kernel_choice_always_covers_the_row():
         if name == "rmsnorm_long_kernel":
             assert f["threads"] == "1024"
             continue
+        if name == "rmsnorm_short_kernel":
+            lanes = int(f["lanes_per_row"])
+            assert whole and H // E <= 32 and lanes <= 32 and lanes & (lanes - 1) == 0
+            assert lanes >= H // E and (lanes == 1 or lanes // 2 < H // E)
+            assert int(f["rows_per_wavefront"]) * lanes == 64
+            if op == ltx.OP_ROPE:
+                P = d // (2 * E)
+                assert d % (2 * E) == 0 and P & (P - 1) == 0
+            if op == ltx.OP_ROPE_INTERLEAVED:
+                assert d % E == 0
+            continue
         wpr, rpb, threads = int(f["wavefronts_per_row"]), int(f["rows_per_block"]), int(f["threads"])
         assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024 and wpr != 2
         assert rpb == (4 if wpr == 1 else 2 if wpr <= 3 else 1)
@@ -393,4 +419,4 @@ def test_kernel_choice_always_covers_the_row():
     assert {"rmsnorm_kernel", "rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel",
             "rmsnorm_rope_packed_kernel", "rmsnorm_rope_packed_kernel(odd)", "rmsnorm_rope_pair_kernel",
             "rmsnorm_rope_interleaved_kernel", "rmsnorm_rope_interleaved_kernel(shared)",
-            "rmsnorm_general_kernel", "rmsnorm_long_kernel"} <= seen, seen
+            "rmsnorm_general_kernel", "rmsnorm_long_kernel", "rmsnorm_short_kernel"} <= seen, seen

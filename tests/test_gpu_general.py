@@ -425,3 +425,62 @@ def test_random_shapes(case):
         check_adaln(x, w, sc, sh, rps, label=str(case))
     else:
         check_rms(x, w, label=str(case))
+
+
+# ---------------------------------------------------------------------------
+# Short rows (at most 32 vectors): several rows per wavefront
+# ---------------------------------------------------------------------------
+
+SHORT = {"bf16": [8, 16, 24, 40, 64, 96, 128, 192, 256], "f16": [8, 64, 128, 256],
+         "f32": [4, 8, 12, 20, 32, 64, 96, 128]}
+
+
+@pytest.mark.parametrize("dtype,hidden", [(dt, h) for dt, hs in SHORT.items() for h in hs])
+@pytest.mark.parametrize("rows", [1, 5, 63, 1000, 4097])
+def test_short_rows(dtype, hidden, rows):
+    announce(f"short rows {dtype} rows={rows} hidden={hidden}")
+    seed = 7 * hidden + rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    got, rep = check_rms(x, w, label=f"short rms {dtype} {rows}x{hidden}")
+    if dtype != "f32":
+        assert rep["max_ulp"] <= 1.0
+    rps = max(1, rows // 3)
+    samples = -(-rows // rps)
+    sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    check_adaln(x, w, sc, sh, rps, label=f"short adaln {dtype} {rows}x{hidden}")
+    E = 4 if dtype == "f32" else 8
+    # RoPE with one or two heads per row (per-head rows), both pairings
+    for heads in (1, 2):
+        d = hidden // heads
+        if hidden % heads or d % 2:
+            continue
+        c, s_ = datagen.rope_tables(int(1 + rows % 11), d)
+        P = d // (2 * E) if d % (2 * E) == 0 else 0
+        check_rope(x, w, c, s_, heads, d, label=f"short rope {dtype} {rows}x{heads}x{d}")
+        check_rope(x, w, c, s_, heads, d, interleaved=True, label=f"short rope-il {dtype} {rows}x{heads}x{d}")
+
+
+def test_short_rows_invariants():
+    """Per-head rows: NULL weight = ones, in place = out of place, run to run
+    identical, position 0 = RMSNorm, NULL modulation = RMSNorm."""
+    announce("short rows invariants")
+    x = datagen.make_x(3000, 128, seed=5, stream=1)
+    w = datagen.make_w(128, seed=5, stream=2)
+    base = run_rms(x, w)
+    assert np.array_equal(base, run_rms(x, w))
+    assert np.array_equal(run_rms(x, None), run_rms(x, np.full(128, 0x3F80, dtype=np.uint16)))
+    xt = dev_bf16(x)
+    ltx.rmsnorm(xt, dev_bf16(w), 1e-6, out=xt)
+    assert np.array_equal(host_bits(xt), base)
+    c0, s0 = datagen.rope_tables(1, 128)
+    assert np.array_equal(run_rope(x, w, c0, s0, 1, 128), base)
+    assert np.array_equal(run_rope(x, w, c0, s0, 1, 128, interleaved=True), base)
+    assert np.array_equal(run_adaln(x, w, None, None, 1000), base)
+    # in place with rotation (partners exchanged between lanes)
+    c, s = datagen.rope_tables(17, 128)
+    ref = run_rope(x, w, c, s, 1, 128)
+    xt = dev_bf16(x)
+    ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), 1, 128, 1e-6, out=xt)
+    assert np.array_equal(host_bits(xt), ref)
