@@ -23,7 +23,8 @@ the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
 scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
-"rms_f16" / "rms_f32", three shapes outside the pages' set under "general"
+"rms_f16" / "rms_f32" (and the RoPE / AdaLN workloads in fp16 or fp32 under
+"rope_f16", "rope_f32", "adaln_f32"), three shapes outside the pages' set under "general"
 (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
 rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
 of 128), and the CPU oracle timed on this host under "cpu_baseline".  Prints
@@ -397,7 +398,10 @@ def main():
                 ("rope_interleaved", datagen.ROPE_INTERLEAVED, "rmsnorm_rope_interleaved", "bf16"),
                 ("adaln", datagen.ADALN, "rmsnorm_adaln", "bf16"),
                 ("rms_f16", datagen.HEADLINE, "rmsnorm_f16", "f16"),
-                ("rms_f32", datagen.HEADLINE, "rmsnorm_f32", "f32")):
+                ("rms_f32", datagen.HEADLINE, "rmsnorm_f32", "f32"),
+                ("rope_f16", datagen.ROPE, "rmsnorm_rope_f16", "f16"),
+                ("rope_f32", datagen.ROPE, "rmsnorm_rope_f32", "f32"),
+                ("adaln_f32", datagen.ADALN, "rmsnorm_adaln_f32", "f32")):
             rc = datagen.CONFIGS[name]
             rw = Workload(rc, dev, stream, dtype=dtype)
             rsec = rw.time_steps(args.steps, args.warmup, graph)
