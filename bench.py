@@ -24,11 +24,12 @@ cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
 scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
 "rms_f16" / "rms_f32" (and the RoPE / AdaLN workloads in fp16 or fp32 under
-"rope_f16", "rope_f32", "adaln_f32"), three shapes outside the pages' set under "general"
+"rope_f16", "rope_f32", "adaln_f32"), four shapes outside the pages' set under "general"
 (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
 rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
-of 128), and the CPU oracle timed on this host under "cpu_baseline".  Prints
-one JSON line.
+of 128), and the CPU oracle timed on this host under "cpu_baseline".  The
+same CPU leg compares every timed workload's output, element by element over
+the whole batch, with the oracle's result ("parity").  Prints one JSON line.
 
 --probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|rms_short|copy
 runs a few launches only, for rocprofv3 counter passes.
@@ -118,6 +119,16 @@ def to_device(a, dev):
     return torch.from_numpy(a).to(dev)
 
 
+def to_host(t) -> np.ndarray:
+    """A device output as the oracle compares it: bf16 as uint16 bit
+    patterns, fp16 and fp32 as numpy arrays of that type."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
 class Workload:
     """Rotating device buffers for one config, and the launch of one step."""
 
@@ -161,6 +172,11 @@ class Workload:
         else:
             self.ltx.ltxnorm_rmsnorm_fwd_dt(self.y[k], self.x[k], self.w, c.rows, c.hidden, c.eps,
                                             self.code, self.stream)
+
+    def output(self) -> np.ndarray:
+        """The output of the last timed launches (every rotating set holds the
+        same input, so any set's output is the timed kernel's result)."""
+        return to_host(self.y[0])
 
     def time_steps(self, steps: int, warmup: int, graph: bool = True):
         """Warm up, then time exactly `steps` launches with HIP events on the
@@ -279,6 +295,46 @@ def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict
             "cpu_model": model}
 
 
+def oracle_parity(checks: list, workers: int = 4) -> dict:
+    """Element-by-element check of every timed kernel's output against the
+    CPU oracle on the whole batch, with the pass rule of the parity tests
+    (one output ulp; for rotated and modulated outputs a floor scaled by the
+    magnitude of the two cancelling terms).  `checks` holds (key, config,
+    io dtype, host inputs, device output copied to the host)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import parity
+    o = oracle.Oracle()
+
+    def one(item):
+        key, cfg, dtype, inp, got = item
+        x = inp["x"].reshape(-1, cfg.hidden)
+        mag = None
+        if cfg.adaln:
+            y, mag = o.rmsnorm_adaln(x, inp["w"], inp["scale"], inp["shift"], cfg.seq, cfg.eps,
+                                     with_mag=True)
+        elif cfg.rope:
+            y, mag = o.rmsnorm_rope(x, inp["w"], inp["cos"], inp["sin"], cfg.heads,
+                                    cfg.head_dim, cfg.eps, with_mag=True,
+                                    interleaved=cfg.interleaved)
+        else:
+            y = o.rmsnorm(x, inp["w"], cfg.eps)
+        ref32, ref = o.round(y, dtype)
+        del y
+        rep = parity.compare(got.reshape(-1), ref.reshape(-1), mag, ref32)
+        rep.update(workload=cfg.name, io_dtype=dtype)
+        return key, rep
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(workers) as ex:
+        reps = dict(ex.map(one, checks))
+    return {"all_pass": all(r["pass"] for r in reps.values()),
+            "rule": "|gpu - oracle| <= 1 ulp of the output type (bf16/fp16), or 2^-18 (|ref| + m) "
+                    "for fp32; a 2^-16 m floor where RoPE / AdaLN terms of magnitude m cancel",
+            "seconds": round(time.perf_counter() - t0, 1),
+            "workloads": reps}
+
+
 def probe(kind: str, launches: int):
     """A handful of launches for counter collection (rocprofv3 --pmc)."""
     import torch
@@ -346,6 +402,7 @@ def main():
     sec = wl.time_steps(args.steps, args.warmup, graph)
     value = gbps(cfg.algorithmic_bytes(), sec)
     sec_other = wl.time_steps(args.steps, args.warmup, not graph)  # the other launch mode
+    checks = [("headline", cfg, "bf16", wl.host, wl.output())]
     traffic = read_traffic("rmsnorm", cfg.name)
     line = {
         "metric": METRIC,
@@ -413,6 +470,7 @@ def main():
                          "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
                          "frac": round(rv / HBM_PEAK_GBPS, 4),
                          "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+            checks.append((key, rc, dtype, rw.host, rw.output()))
             del rw
             torch.cuda.empty_cache()
         # shapes served by the kernels for rows of any length
@@ -432,11 +490,13 @@ def main():
                 "ms_per_step": round(rsec * 1e3, 6), "bytes_per_step": rw.nbytes,
                 "rotating_sets": rw.nsets, "frac": round(rv / HBM_PEAK_GBPS, 4),
                 "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+            checks.append((name, rc, "bf16", rw.host, rw.output()))
             del rw
             torch.cuda.empty_cache()
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, host)
+        line["parity"] = oracle_parity(checks)
     print(json.dumps(line), flush=True)
 
 

@@ -1,6 +1,11 @@
 """Element-wise comparison of kernel output with the oracle, for bf16, fp16
 and fp32 outputs.
 
+Each report gives the largest error in output ulps over all elements
+("max_ulp") and over those the floor does not cover ("max_ulp_outside_floor"),
+and the largest ratio of error to tolerance ("max_tol_ratio", at most 1 for a
+pass).
+
 Rule, per element: |gpu - ref16| <= max(ulp16(ref16), 2^-16 * m), where
 ref16 is the oracle's binary32 result rounded to bf16 (nearest-even),
 ulp16(v) = 2^(floor(log2|v|) - 7) is the bf16 spacing at v's binade (the
@@ -69,10 +74,13 @@ def compare(got, ref, mag=None, ref32=None) -> dict:
     bad = (diff > tol) | (gnan != rnan)
     # elements that pass only thanks to the magnitude term m
     own = u if ref.dtype == np.float16 else 2.0 ** -18 * np.abs(np.where(both, r, 0.0))
+    floor_bound = (diff > own) & (diff <= tol)
     rep = {"n": int(g.size), "pass": bool(not bad.any()), "n_bad": int(bad.sum()),
            "n_exact": int((g == r).sum() + (gnan & rnan).sum()),
            "max_ulp": float((diff / u).max()) if diff.size else 0.0,
-           "n_floor_bound": int(((diff > own) & (diff <= tol)).sum())}
+           "max_ulp_outside_floor": float(np.where(floor_bound, 0.0, diff / u).max()) if diff.size else 0.0,
+           "max_tol_ratio": float((diff / tol).max()) if diff.size else 0.0,
+           "n_floor_bound": int(floor_bound.sum())}
     if ref32 is not None:
         r32 = np.asarray(ref32, dtype=np.float32).reshape(-1).astype(np.float64)
         ok = both & ~np.isnan(r32) & np.isfinite(g)
@@ -107,6 +115,8 @@ def compare_bf16(got_bits, ref16, mag=None, ref32=None) -> dict:
         "n_bad": int(bad.sum()),
         "n_bit_exact": int((got_bits == ref16).sum()),
         "max_ulp": float((diff / u).max()) if diff.size else 0.0,
+        "max_ulp_outside_floor": float(np.where(floor_bound, 0.0, diff / u).max()) if diff.size else 0.0,
+        "max_tol_ratio": float((diff / tol).max()) if diff.size else 0.0,
         "n_floor_bound": int(floor_bound.sum()),
     }
     if ref32 is not None:
