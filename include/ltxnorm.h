@@ -218,7 +218,10 @@ typedef enum ltxnorm_op {
  * buf, truncated to len bytes, for example
  *     "rmsnorm_kernel wavefronts_per_row=3 vectors_per_lane=2 rows_per_block=2
  *      threads=384 lds_bytes=0"
- * (the kernel names are those a profiler shows).  heads and head_dim are
+ * (the kernel names are those a profiler shows).  The general kernel's line
+ * ends in "grid=resident": its grid is capped at the number of workgroups
+ * the device holds at once, each workgroup looping over rows; every other
+ * kernel takes one workgroup per group of rows.  heads and head_dim are
  * read for the RoPE operations only.
  *
  * Shapes are validated as the entry point validates them.  No pointer

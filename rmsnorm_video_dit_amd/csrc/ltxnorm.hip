@@ -239,10 +239,10 @@ LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, 
                       ltxnorm_detail::kLongThreads);
     } else {
         const int rpb = ltxnorm_detail::rows_per_block(c.plan.wpr);
-        std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld",
+        std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld%s",
                       name, c.plan.wpr, c.kernel == Kernel::kRopePair ? "pairs_per_lane" : "vectors_per_lane",
                       c.plan.per, rpb, ltxnorm_detail::kWave * c.plan.wpr * rpb,
-                      (long long)(c.lds_per_row * rpb));
+                      (long long)(c.lds_per_row * rpb), c.kernel == Kernel::kGeneral ? " grid=resident" : "");
     }
     return LTXNORM_OK;
 }

@@ -3,6 +3,8 @@
 // Included once per I/O dtype; not a public header.
 #pragma once
 
+#include <mutex>
+
 #include "ltxnorm_kernels.h"
 #include "ltxnorm_general.h"
 
@@ -13,13 +15,56 @@ namespace {
 // Host side: per-plan instance, launch.
 // ---------------------------------------------------------------------------
 
+// Workgroups of `fn` (at this size and dynamic LDS) that the stream's device
+// holds at once: workgroups per CU times the CU count, or 0 where HIP cannot
+// say.  The figure depends only on the device and the kernel instance, so it
+// is kept in a small table guarded by a mutex (entries are never removed;
+// once the table is full, later instances are queried on every launch).
+inline int64_t resident_workgroups(const void* fn, int threads, size_t lds_bytes,
+                                   hipStream_t stream) {
+    struct Entry {
+        const void* fn;
+        size_t lds;
+        int device;
+        int64_t n;
+    };
+    static std::mutex mu;
+    static Entry table[128];
+    static int used = 0;
+    int dev = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (table[i].fn == fn && table[i].lds == lds_bytes && table[i].device == dev) return table[i].n;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds_bytes) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int64_t n = (int64_t)(per_cu > 0 ? per_cu : 0) * (cus > 0 ? cus : 0);
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < (int)(sizeof(table) / sizeof(table[0]))) table[used++] = Entry{fn, lds_bytes, dev, n};
+    return n;
+}
+
+// Launch with one workgroup per group of rows.  Most kernels take the full
+// grid: a grid-stride loop capped at the resident capacity measured 3-4%
+// slower than letting the dispatcher stream fresh workgroups, which keeps
+// every CU busy to the last rows.  `resident` caps the grid at the resident
+// capacity instead, for kernels that load per-workgroup data worth reusing
+// across rows (the general kernel's weight chunks: at hidden 3076, 42.5 ->
+// 57.9 % of peak; the cap measured best at one resident wave of workgroups,
+// against two, three or four).
 inline ltxnorm_status launch(const void* fn, int threads, int rpb, const KArgs& args,
-                             size_t lds_bytes, hipStream_t stream) {
-    // One workgroup per group of rows: a grid-stride loop capped at the
-    // resident capacity measured 3-4% slower than letting the dispatcher
-    // stream fresh workgroups, which keeps every CU busy to the last rows.
+                             size_t lds_bytes, hipStream_t stream, bool resident = false) {
     const int64_t need = (args.rows + rpb - 1) / rpb;
-    const unsigned grid = (unsigned)(need < kMaxGrid ? need : kMaxGrid);
+    int64_t grid_rows = need < kMaxGrid ? need : kMaxGrid;
+    if (resident) {
+        const int64_t cap = resident_workgroups(fn, threads, lds_bytes, stream);
+        if (cap > 0 && cap < grid_rows) grid_rows = cap;
+    }
+    const unsigned grid = (unsigned)grid_rows;
     KArgs copy = args;
     void* params[] = {&copy};
     const hipError_t e =
@@ -27,24 +72,29 @@ inline ltxnorm_status launch(const void* fn, int threads, int rpb, const KArgs& 
     return e == hipSuccess ? LTXNORM_OK : LTXNORM_ERR_HIP;
 }
 
-// One launcher per kernel family: fn<WPR, PER, FULL>() picks the instance.
+// One launcher per kernel family: fn<WPR, PER, FULL>() picks the instance;
+// kResident asks for the grid capped at the resident capacity.
 template <typename IO>
 struct RmsL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO>
 struct RopeXorL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO>
 struct RopePairL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_rope_pair_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO, bool SHARED>
 struct RopeIlL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() {
         return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED>;
@@ -52,17 +102,20 @@ struct RopeIlL {
 };
 template <typename IO>
 struct AdaL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO, bool ODD>
 struct RopePackedL {
+    static constexpr bool kResident = false;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD>; }
 };
 // The general kernel masks every row itself: FULL does not select anything.
 template <typename IO, GOp OP>
 struct GeneralL {
+    static constexpr bool kResident = true;
     template <int WPR, int PER, bool FULL>
     static const void* fn() { return (const void*)&rmsnorm_general_kernel<IO, OP, PER, WPR>; }
 };
@@ -75,7 +128,7 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
         if (p.per == LO) {
             const void* fn = p.full ? LN::template fn<WPR, LO, true>() : LN::template fn<WPR, LO, false>();
             return launch(fn, Layout<WPR>::kThreads, Layout<WPR>::kRowsPerBlock, a,
-                          lds_per_row * Layout<WPR>::kRowsPerBlock, s);
+                          lds_per_row * Layout<WPR>::kRowsPerBlock, s, LN::kResident);
         }
         return by_per<LN, WPR, LO + 1, HI>(p, a, lds_per_row, s);
     }

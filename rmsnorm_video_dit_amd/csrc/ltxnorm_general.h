@@ -135,17 +135,69 @@ __device__ __forceinline__ u32x4 load_window(const void* base, int64_t start, in
     return load_elems<IO>(base, start, 0, n);
 }
 
-// Store a row's vector q (row-relative elements j0 .. j0 + kEpv): whole
-// vectors with the streaming store, the row's end vectors element by element
-// (its own elements only).
+// Store elements lo .. hi - 1 (0 <= lo < hi <= kEpv) of the aligned vector
+// at p as naturally aligned pieces: up from byte lo * size in pieces of 2, 4
+// and 8 bytes while the start is misaligned, then down in pieces of 8, 4 and
+// 2 bytes (at most four stores).  Where a row boundary falls on a 4-byte
+// boundary, no store is narrower than 4 bytes: a 2-byte store leaves a
+// partially written 4-byte word in the cache, and rows of hidden 3076 took
+// 41 % of peak with one 2-byte store per element at their end vectors.
 template <typename IO>
-__device__ __forceinline__ void store_row_vec(void* out, int64_t s, int64_t g0, int q, int j0,
-                                              int hidden, const u32x4 v) {
+__device__ __forceinline__ void store_vec_range(u32x4* p, const u32x4 v, int lo, int hi) {
+    constexpr int ES = 16 / IO::kEpv;  // bytes per element
+    char* base = reinterpret_cast<char*>(p);
+    int b0 = lo * ES;
+    const int b1 = hi * ES;
+    // word i of v for a lane-varying i, as selects (no indexed array)
+    auto word = [&](int i) { return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3])); };
+    auto put2 = [&](int b) {
+        __builtin_nontemporal_store((uint16_t)(word(b >> 2) >> (8 * (b & 3))),
+                                    reinterpret_cast<uint16_t*>(base + b));
+    };
+    auto put4 = [&](int b) { __builtin_nontemporal_store(word(b >> 2), reinterpret_cast<uint32_t*>(base + b)); };
+    if (b1 - b0 == 16) {
+        store_stream(p, v);
+        return;
+    }
+    if constexpr (ES == 2) {
+        if ((b0 & 2) && b0 + 2 <= b1) {
+            put2(b0);
+            b0 += 2;
+        }
+    }
+    if ((b0 & 4) && b0 + 4 <= b1) {
+        put4(b0);
+        b0 += 4;
+    }
+    if ((b0 & 8) && b0 + 8 <= b1) {  // bytes 8 .. 15
+        __builtin_nontemporal_store(u32x2{v[2], v[3]}, reinterpret_cast<u32x2*>(base + 8));
+        b0 += 8;
+    }
+    if (b1 - b0 >= 8) {  // bytes 0 .. 7 (b0 is 0 here)
+        __builtin_nontemporal_store(u32x2{v[0], v[1]}, reinterpret_cast<u32x2*>(base));
+        b0 += 8;
+    }
+    if (b1 - b0 >= 4) {
+        put4(b0);
+        b0 += 4;
+    }
+    if constexpr (ES == 2) {
+        if (b1 - b0 >= 2) put2(b0);
+    }
+}
+
+// Store a row's vector q (row-relative elements j0 .. j0 + kEpv): whole
+// vectors with the streaming store, the row's end vectors as aligned pieces
+// holding the row's own elements only.
+template <typename IO>
+__device__ __forceinline__ void store_row_vec(void* out, int64_t g0, int q, int j0, int hidden,
+                                              const u32x4 v) {
     constexpr int E = IO::kEpv;
+    u32x4* p = static_cast<u32x4*>(out) + g0 + q;
     if (j0 >= 0 && j0 + E <= hidden)
-        store_stream(static_cast<u32x4*>(out) + g0 + q, v);
+        store_stream(p, v);
     else
-        store_elems<IO>(out, s + j0, v, s, s + hidden);
+        store_vec_range<IO>(p, v, j0 < 0 ? -j0 : 0, hidden - j0 < E ? hidden - j0 : E);
 }
 
 // Zero the elements of v outside positions [lo, hi) of the vector
@@ -352,7 +404,7 @@ rmsnorm_general_kernel(const KArgs a) {
                         o[e] = yrow[jj] * c[e] + yrow[pj] * sn[e];
                         if (++hd == d) hd = 0;
                     }
-                    store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(o));
+                    store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(o));
                 }
             }
             __syncthreads();  // the next row reuses the LDS row
@@ -387,9 +439,9 @@ rmsnorm_general_kernel(const KArgs a) {
                     if constexpr (OP == GOp::kRopeIl) {
                         float o[E];
                         rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
-                        store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(o));
+                        store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(o));
                     } else {
-                        store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(f));
+                        store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(f));
                     }
                 }
             }
@@ -521,9 +573,9 @@ rmsnorm_long_kernel(const KArgs a) {
                         if constexpr (OP == GOp::kRopeIl) {
                             float o[E];
                             rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
-                            store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(o));
+                            store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(o));
                         } else {
-                            store_row_vec<IO>(a.out, s, g0, q, j0, H, IO::narrow(f));
+                            store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(f));
                         }
                     }
                 }

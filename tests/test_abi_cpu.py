@@ -304,6 +304,7 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
         per_key = "pairs_per_lane" if "pair" in name else "vectors_per_lane"
         assert int(f[per_key]) == per
         assert int(f["threads"]) == 64 * wpr * int(f["rows_per_block"])
+        assert (f.get("grid") == "resident") == (name == "rmsnorm_general_kernel"), f
     else:
         assert f["passes"] == "2" and f["threads"] == "1024"
 
