@@ -239,10 +239,12 @@ def launch_floor_us(stream, launches: int = 1000) -> float:
     return t0.elapsed_time(t1) * 1e3 / launches
 
 
-def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict:
+def cpu_baseline(cfg: datagen.Config, inp: dict, checks: list, budget_s: float = 10.0) -> dict:
     """The CPU oracle (double arithmetic, one rounding) on this host's cores,
     rows split into contiguous blocks across a thread pool; repeated over the
-    full batch until `budget_s` has passed."""
+    full batch until `budget_s` has passed.  The same leg then checks every
+    timed kernel's output against the oracle (`checks`, see oracle_parity) and
+    returns that report under "parity"."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     o = oracle.Oracle()
@@ -292,12 +294,13 @@ def cpu_baseline(cfg: datagen.Config, inp: dict, budget_s: float = 10.0) -> dict
                       f"{per_pass * 1e3:.1f} ms per pass",
             "single_thread": {"value": round(gbps(sub_bytes, el1 / n1), 3), "unit": "GB/s",
                               "sample": f"{len(sub)} rows x {cfg.hidden}, {n1} passes in {el1:.1f} s"},
-            "cpu_model": model}
+            "cpu_model": model,
+            "parity": oracle_parity(checks)}
 
 
 def oracle_parity(checks: list, workers: int = 4) -> dict:
-    """Element-by-element check of every timed kernel's output against the
-    CPU oracle on the whole batch, with the pass rule of the parity tests
+    """Part of the CPU-baseline leg: element-by-element check of every timed
+    kernel's output against the CPU oracle on the whole batch, with the pass rule of the parity tests
     (one output ulp; for rotated and modulated outputs a floor scaled by the
     magnitude of the two cancelling terms).  `checks` holds (key, config,
     io dtype, host inputs, device output copied to the host)."""
@@ -495,8 +498,9 @@ def main():
             torch.cuda.empty_cache()
 
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, host)
-        line["parity"] = oracle_parity(checks)
+        cb = cpu_baseline(cfg, host, checks)
+        line["parity"] = cb.pop("parity")
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

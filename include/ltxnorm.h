@@ -36,7 +36,10 @@
  *   - The destination comes first, as in an out-variant op.
  *   - Arguments are validated on the host before any HIP call; a rejected
  *     call enqueues nothing.  No C++ exception crosses this boundary.
- *   - Calls are thread-safe and reentrant; the library keeps no state.
+ *   - Calls are thread-safe and reentrant.  The only state the library keeps
+ *     is a mutex-guarded table of how many workgroups of a kernel instance
+ *     the device holds at once (queried from HIP on first use and never
+ *     changed), which sizes the grid of the kernel for rows of any length.
  *   - Each operation has a bf16 entry point and a `_dt` twin taking the I/O
  *     dtype (the skill page, "Supported Data Types", lists FP16, BF16 and
  *     FP32); x, out, weight, scale and shift all use that dtype, the
