@@ -428,6 +428,101 @@ def test_random_shapes(case):
 
 
 # ---------------------------------------------------------------------------
+# The general kernel's grid holds only the workgroups the device keeps
+# resident at once, and each workgroup loops over rows.  Row counts several
+# times that capacity exercise the loop: weight chunks reused across rows,
+# the rotate-half LDS row reused, cross-wavefront partial sums alternating
+# between their two buffers.
+# ---------------------------------------------------------------------------
+
+RESIDENT = [  # dtype, op, rows, hidden, head_dim
+    ("bf16", "rms", 20000, 1028, 0),     # one wavefront per row, four rows per workgroup
+    ("f16", "adaln", 9000, 3076, 0),     # four wavefronts per row, nine samples
+    ("bf16", "half", 20000, 1040, 52),   # rotate-half through LDS, four rows per workgroup
+    ("f32", "half", 6000, 4100, 82),     # rotate-half through LDS, nine wavefronts per row
+    ("bf16", "il", 20000, 1000, 10),     # interleaved pairs, two vectors per lane
+    ("f32", "rms", 12000, 1027, 0),      # three wavefronts per row, two rows per workgroup
+]
+_OPS = {"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "half": ltx.OP_ROPE, "il": ltx.OP_ROPE_INTERLEAVED}
+_DT = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}
+
+
+@pytest.mark.parametrize("dtype,op,rows,hidden,d", RESIDENT)
+def test_resident_grid_many_rows(dtype, op, rows, hidden, d):
+    heads = hidden // d if d else 0
+    desc = ltx.ltxnorm_describe_launch(_OPS[op], rows, hidden, heads, d, _DT[dtype])
+    announce(f"resident grid {dtype} {op} rows={rows} hidden={hidden} d={d} -> {desc}")
+    assert desc.startswith("rmsnorm_general_kernel ") and desc.endswith(" grid=resident"), desc
+    seed = rows + hidden
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    if op == "rms":
+        check_rms(x, w, label=f"resident rms {dtype} {rows}x{hidden}")
+    elif op == "adaln":
+        rps = 1000
+        samples = -(-rows // rps)
+        sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+        sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+        check_adaln(x, w, sc, sh, rps, label=f"resident adaln {dtype} {rows}x{hidden}")
+    else:
+        c, s_ = datagen.rope_tables(4096, d)
+        check_rope(x, w, c, s_, heads, d, interleaved=(op == "il"),
+                   label=f"resident rope {op} {dtype} {rows}x{heads}x{d}")
+
+
+def test_resident_grid_threads():
+    """Eight host threads launch at once, each on its own stream.  Each uses
+    rotate-half shapes whose LDS size is new to the process, so the threads
+    add to the library's occupancy table concurrently.  Every result matches
+    the oracle, and repeats are bit-identical."""
+    import threading
+    # (heads, head_dim): head sizes only the general kernel pairs (LDS row
+    # exchange), a distinct hidden size per thread
+    shapes = [(37, 14), (23, 22), (19, 26), (17, 30), (13, 34), (11, 38), (29, 42), (7, 46)]
+    rows = 4099
+    announce(f"resident grid, {len(shapes)} threads")
+    inputs = []
+    for heads, d in shapes:
+        hidden = heads * d
+        x = datagen.make_x(rows, hidden, seed=hidden, stream=1)
+        w = datagen.make_w(hidden, seed=hidden, stream=2)
+        c, s_ = datagen.rope_tables(97, d)
+        inputs.append((heads, d, x, w, c, s_))
+    results = [None] * len(shapes)
+    errors = []
+    barrier = threading.Barrier(len(shapes))
+
+    def work(i):
+        try:
+            heads, d, x, w, c, s_ = inputs[i]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                xt, wt, ct, st = dev_bf16(x), dev_bf16(w), dev_f32(c), dev_f32(s_)
+                stream.synchronize()
+                barrier.wait()
+                outs = [ltx.rmsnorm_rope(xt, wt, ct, st, heads, d, 1e-6) for _ in range(3)]
+                stream.synchronize()
+            results[i] = [host_bits(o) for o in outs]
+        except Exception as e:  # reported below, in the test's thread
+            errors.append((i, repr(e)))
+            barrier.abort()
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert all(not t.is_alive() for t in threads)
+    for (heads, d, x, w, c, s_), outs in zip(inputs, results):
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+        y, mag = ORC.rmsnorm_rope(x, w, c, s_, heads, d, 1e-6, with_mag=True)
+        ref32, ref = ORC.round(y, "bf16")
+        rep = compare(outs[0], ref, mag, ref32)
+        assert rep["pass"], (heads, d, rep)
+
+
+# ---------------------------------------------------------------------------
 # Short rows (at most 32 vectors): several rows per wavefront
 # ---------------------------------------------------------------------------
 
