@@ -470,6 +470,32 @@ def test_resident_grid_many_rows(dtype, op, rows, hidden, d):
                    label=f"resident rope {op} {dtype} {rows}x{heads}x{d}")
 
 
+def test_graph_capture_first_general_launch():
+    """The general kernel's first launch at a new size and LDS footprint
+    happens inside graph capture, so its occupancy query runs during capture
+    too; the captured graph replays to the eager result."""
+    heads, d, rows = 7, 38, 9000           # hidden 266: rotate-half through LDS
+    hidden = heads * d
+    announce("graph capture, first general launch")
+    x = dev_bf16(datagen.make_x(rows, hidden, seed=266, stream=1))
+    w = dev_bf16(datagen.make_w(hidden, seed=266, stream=2))
+    c, sn = datagen.rope_tables(333, d)
+    ct, st = dev_f32(c), dev_f32(sn)
+    y = torch.empty_like(x)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ltx.rmsnorm_rope(x, w, ct, st, heads, d, 1e-6, out=y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), host_bits(ltx.rmsnorm_rope(x, w, ct, st, heads, d, 1e-6)))
+
+
 def test_resident_grid_threads():
     """Eight host threads launch at once, each on its own stream.  Each uses
     rotate-half shapes whose LDS size is new to the process, so the threads
