@@ -22,10 +22,11 @@ MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
 the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
 cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
 (adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
-scale/shift) under "adaln", the headline RMSNorm with fp16 and fp32 I/O under
-"rms_f16" / "rms_f32" (and the RoPE / AdaLN workloads in fp16 or fp32 under
-"rope_f16", "rope_f32", "adaln_f32"), four shapes outside the pages' set under "general"
-(hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
+scale/shift) under "adaln", the other four shapes of the pages' RMSNorm
+micro-benchmark under "pages_shapes" (with the page's H100 ms as context),
+the headline RMSNorm with fp16 and fp32 I/O under "rms_f16" / "rms_f32" (and
+the RoPE / AdaLN workloads in fp16 or fp32 under "rope_f16", "rope_f32",
+"adaln_f32"), four shapes outside the pages' set under "general" (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
 rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
 of 128), and the CPU oracle timed on this host under "cpu_baseline".  The
 same CPU leg compares every timed workload's output, element by element over
@@ -58,6 +59,10 @@ METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, RMSNorm 
 # H100 figure for the same shape and byte convention: 201,332,736 B in 0.157 ms
 # (Hugging Face cuda-kernels skill page, "RMSNorm Micro-benchmarks"); context only.
 H100_GBPS_4x4096x3072 = 201_332_736 / 0.157e-3 / 1e9
+# The custom kernel's ms for every shape of that table (same page and
+# section), quoted beside the MI355X figures for the same shapes; context only.
+H100_MS = {"rms_1x1024x2048": 0.019, "rms_2x1024x2048": 0.024, "rms_4x1024x2048": 0.036,
+           "rms_2x4096x3072_outliers": 0.087, "rms_4x4096x3072": 0.157}
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 KERNEL_SOURCES = (sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.hip")))
@@ -372,7 +377,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-rope", action="store_true",
-                    help="skip the RoPE and AdaLN line items (headline only)")
+                    help="skip the RoPE, AdaLN, other-dtype and general line items (the "
+                         "headline and the pages' other RMSNorm shapes only)")
     ap.add_argument("--probe", choices=sorted(PROBES) + ["copy"])
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
@@ -451,6 +457,28 @@ def main():
     host = wl.host
     del wl
     torch.cuda.empty_cache()
+
+    # the other shapes of the pages' micro-benchmark table, in both launch modes
+    line["pages_shapes"] = {}
+    for name in ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
+                 "rms_2x4096x3072_outliers"):
+        rc = datagen.CONFIGS[name]
+        rw = Workload(rc, dev, stream)
+        rsec = rw.time_steps(args.steps, args.warmup, graph)
+        gsec = rw.time_steps(args.steps, args.warmup, not graph)
+        rv = gbps(rw.nbytes, rsec)
+        line["pages_shapes"][name] = {
+            "kernel": describe(rc), "ms_per_step": round(rsec * 1e3, 6),
+            ("graph" if not graph else "stream") + "_ms_per_step": round(gsec * 1e3, 6),
+            "value": round(rv, 2), "unit": "GB/s", "frac": round(rv / HBM_PEAK_GBPS, 4),
+            "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
+            "h100_ms_on_the_pages": H100_MS[name]}
+        checks.append((name, rc, "bf16", rw.host, rw.output()))
+        del rw
+        torch.cuda.empty_cache()
+    line["pages_shapes"]["note"] = ("the smaller shapes take a few microseconds per launch, most of "
+                                    "it the launch itself (launch_floor_us); graph replay removes the "
+                                    "host-side issue cost")
 
     if not args.no_rope:
         for key, name, kernel, dtype in (
