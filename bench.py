@@ -26,13 +26,16 @@ scale/shift) under "adaln", the other four shapes of the pages' RMSNorm
 micro-benchmark under "pages_shapes" (with the page's H100 ms as context),
 the headline RMSNorm with fp16 and fp32 I/O under "rms_f16" / "rms_f32" (and
 the RoPE / AdaLN workloads in fp16 or fp32 under "rope_f16", "rope_f32",
-"adaln_f32"), four shapes outside the pages' set under "general" (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
+"adaln_f32"), RoPE (24 heads x 128, both pairings) and AdaLN at the
+headline's size under "rope_large", "rope_interleaved_large" and
+"adaln_large", four shapes outside the pages' set under "general" (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
 rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
 of 128), and the CPU oracle timed on this host under "cpu_baseline".  The
 same CPU leg compares every timed workload's output, element by element over
 the whole batch, with the oracle's result ("parity").  Prints one JSON line.
 
---probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|rms_short|copy
+--probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|rms_short|rope_large|
+ropei_large|adaln_large|copy
 runs a few launches only, for rocprofv3 counter passes.
 """
 from __future__ import annotations
@@ -71,7 +74,9 @@ DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
 PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datagen.HEADLINE,
           "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
           "rms_odd": "rms_4x4096x3076", "rope_d72": "rope_2x4096x1152_h16d72",
-          "rms_long": "rms_1x256x262144", "rms_short": "rms_2x4096x24_d128"}
+          "rms_long": "rms_1x256x262144", "rms_short": "rms_2x4096x24_d128",
+          "rope_large": "rope_4x4096x3072_h24d128", "ropei_large": "ropei_4x4096x3072_h24d128",
+          "adaln_large": "adaln_4x4096x3072"}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
@@ -360,7 +365,7 @@ def probe(kind: str, launches: int):
         print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[PROBES[kind]]
+    cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS, **datagen.LARGE_CONFIGS}[PROBES[kind]]
     dtype = kind[4:] if kind in ("rms_f16", "rms_f32") else "bf16"
     wl = Workload(cfg, dev, s, max_sets=2, dtype=dtype)
     for i in range(launches):
@@ -489,8 +494,11 @@ def main():
                 ("rms_f32", datagen.HEADLINE, "rmsnorm_f32", "f32"),
                 ("rope_f16", datagen.ROPE, "rmsnorm_rope_f16", "f16"),
                 ("rope_f32", datagen.ROPE, "rmsnorm_rope_f32", "f32"),
-                ("adaln_f32", datagen.ADALN, "rmsnorm_adaln_f32", "f32")):
-            rc = datagen.CONFIGS[name]
+                ("adaln_f32", datagen.ADALN, "rmsnorm_adaln_f32", "f32"),
+                ("rope_large", "rope_4x4096x3072_h24d128", "rmsnorm_rope_large", "bf16"),
+                ("rope_interleaved_large", "ropei_4x4096x3072_h24d128", "rmsnorm_rope_il_large", "bf16"),
+                ("adaln_large", "adaln_4x4096x3072", "rmsnorm_adaln_large", "bf16")):
+            rc = {**datagen.CONFIGS, **datagen.LARGE_CONFIGS}[name]
             rw = Workload(rc, dev, stream, dtype=dtype)
             rsec = rw.time_steps(args.steps, args.warmup, graph)
             rv = gbps(rw.nbytes, rsec)

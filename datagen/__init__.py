@@ -233,6 +233,16 @@ GENERAL_CONFIGS = {
     # [2 x 4096 x 24 heads] of them
     "rms_2x4096x24_d128": Config("rms_2x4096x24_d128", 12, 2, 4096 * 24, 128),
 }
+# The fused operations at the headline's size ([4 x 4096 x 3072]), large
+# enough that the launch floor no longer sets their rate: RoPE with 24 heads
+# of 128 in both pairings, and AdaLN with per-sample rows [4 x 3072].
+LARGE_CONFIGS = {
+    "rope_4x4096x3072_h24d128": Config("rope_4x4096x3072_h24d128", 13, 4, 4096, 3072,
+                                       heads=24, head_dim=128, theta=10000.0),
+    "ropei_4x4096x3072_h24d128": Config("ropei_4x4096x3072_h24d128", 14, 4, 4096, 3072,
+                                        heads=24, head_dim=128, theta=10000.0, interleaved=True),
+    "adaln_4x4096x3072": Config("adaln_4x4096x3072", 15, 4, 4096, 3072, adaln_sigma=0.25),
+}
 HEADLINE = "rms_4x4096x3072"
 ROPE = "rope_2x4096x2048_h32d64"
 ROPE_INTERLEAVED = "ropei_2x4096x2048_h32d64"

@@ -129,6 +129,22 @@ def test_workload_full_size(name):
     assert rep.get("n_bit_exact", rep.get("n_exact")) >= 0.99 * rep["n"]
 
 
+@pytest.mark.parametrize("name", list(datagen.LARGE_CONFIGS))
+def test_large_workload_full_size(name):
+    """The fused operations at the headline's size, every element."""
+    cfg = datagen.LARGE_CONFIGS[name]
+    announce(f"large workload {name} rows={cfg.rows} hidden={cfg.hidden}")
+    inp = datagen.make_inputs(cfg)
+    if cfg.rope:
+        got, rep = check_rope(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg.heads, cfg.head_dim,
+                              cfg.eps, label=name, interleaved=cfg.interleaved)
+    else:
+        got, rep = check_adaln(inp["x"], inp["w"], inp["scale"], inp["shift"],
+                               inp["rows_per_sample"], cfg.eps, label=name)
+    assert rep["n_floor_bound"] <= 1e-5 * rep["n"]
+    assert rep["n_bit_exact"] >= 0.99 * rep["n"]
+
+
 # ---------------------------------------------------------------------------
 # fp16 and fp32 I/O: every operation at the workloads' full size
 # ---------------------------------------------------------------------------
