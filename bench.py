@@ -384,6 +384,9 @@ def main():
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the RoPE, AdaLN, other-dtype and general line items (the "
                          "headline and the pages' other RMSNorm shapes only)")
+    ap.add_argument("--no-pages", action="store_true",
+                    help="skip the pages' other RMSNorm shapes (one of them runs the headline's "
+                         "kernel instance, which would merge the two in a per-kernel trace)")
     ap.add_argument("--probe", choices=sorted(PROBES) + ["copy"])
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
@@ -465,8 +468,8 @@ def main():
 
     # the other shapes of the pages' micro-benchmark table, in both launch modes
     line["pages_shapes"] = {}
-    for name in ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
-                 "rms_2x4096x3072_outliers"):
+    for name in () if args.no_pages else ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
+                                          "rms_2x4096x3072_outliers"):
         rc = datagen.CONFIGS[name]
         rw = Workload(rc, dev, stream)
         rsec = rw.time_steps(args.steps, args.warmup, graph)
@@ -481,9 +484,10 @@ def main():
         checks.append((name, rc, "bf16", rw.host, rw.output()))
         del rw
         torch.cuda.empty_cache()
-    line["pages_shapes"]["note"] = ("the smaller shapes take a few microseconds per launch, most of "
-                                    "it the launch itself (launch_floor_us); graph replay removes the "
-                                    "host-side issue cost")
+    if not args.no_pages:
+        line["pages_shapes"]["note"] = ("the smaller shapes take a few microseconds per launch, most "
+                                        "of it the launch itself (launch_floor_us); graph replay "
+                                        "removes the host-side issue cost")
 
     if not args.no_rope:
         for key, name, kernel, dtype in (
