@@ -61,7 +61,10 @@ inline ltxnorm_status launch(const void* fn, int threads, int rpb, const KArgs& 
     const int64_t need = (args.rows + rpb - 1) / rpb;
     int64_t grid_rows = need < kMaxGrid ? need : kMaxGrid;
     if (resident) {
-        const int64_t cap = resident_workgroups(fn, threads, lds_bytes, stream);
+        // a multiple of 8 workgroups whenever they loop: the rows a workgroup
+        // slot visits then all start at the same offset into a 16-byte vector
+        // (the general kernel builds its weight windows once on that basis)
+        const int64_t cap = resident_workgroups(fn, threads, lds_bytes, stream) & ~(int64_t)7;
         if (cap > 0 && cap < grid_rows) grid_rows = cap;
     }
     const unsigned grid = (unsigned)grid_rows;

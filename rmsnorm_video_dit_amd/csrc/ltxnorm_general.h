@@ -287,8 +287,9 @@ __device__ __forceinline__ void rope_interleaved_vec(const KArgs& a, const float
 // that way).  So whole vectors are loaded unconditionally, the tensor's final
 // partial vector (if any) is fetched afterwards under a uniform branch, and
 // the neighbouring rows' elements in a row's end vectors are zeroed in
-// registers.  The weight chunks around each lane's windows are loaded once
-// per workgroup.
+// registers.  Each lane's weight windows are built once per workgroup: the
+// launch keeps every row of a workgroup slot at the same offset into its
+// first vector.
 // ---------------------------------------------------------------------------
 template <typename IO, GOp OP, int VPL, int WPR>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
@@ -303,13 +304,20 @@ rmsnorm_general_kernel(const KArgs a) {
     const int64_t total = a.rows * (int64_t)H;
     const int64_t whole = total / E;  // whole vectors in x
 
-    // weight chunks q - 1 and q of every slot (window of vector q)
-    u32x4 wlo[VPL], whi[VPL];
+    // The weight window of every slot, built once.  A row starts
+    // (row * H) mod E elements into its first vector; the launch makes the
+    // grid-stride step (gridDim.x * RPB rows) a multiple of 8 whenever a
+    // workgroup loops, so every row this slot visits has its first row's
+    // offset and the same window (from chunks q - 1 and q).
+    u32x4 wwin[VPL];
+    {
+        const int64_t row0 = (int64_t)blockIdx.x * RPB + ln.slot;
+        const int fw0 = (int)((-(row0 * (int64_t)H)) & (E - 1));
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int q = k * L + ln.t;
-        wlo[k] = weight_chunk<IO>(a.w, q - 1, H);
-        whi[k] = weight_chunk<IO>(a.w, q, H);
+        for (int k = 0; k < VPL; ++k) {
+            const int q = k * L + ln.t;
+            wwin[k] = weight_window<IO>(weight_chunk<IO>(a.w, q - 1, H), weight_chunk<IO>(a.w, q, H), fw0);
+        }
     }
 
     int parity = 0;
@@ -323,7 +331,6 @@ rmsnorm_general_kernel(const KArgs a) {
         const int first = (int)(s & (E - 1));        // its place in its vector
         const int64_t g0 = s / E;                    // that vector
         const int nch = active ? (first + H + E - 1) / E : 0;  // vectors the row touches
-        const int fw = (-first) & (E - 1);           // weight window offset mod E
 
         u32x4 xv[VPL];
 #pragma unroll
@@ -353,7 +360,8 @@ rmsnorm_general_kernel(const KArgs a) {
             float g[E];
             keep_packed(xv[k]);
             IO::widen(xv[k], f);
-            IO::widen(weight_window<IO>(wlo[k], whi[k], fw), g);
+            keep_packed(wwin[k]);
+            IO::widen(wwin[k], g);
 #pragma unroll
             for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
         };
