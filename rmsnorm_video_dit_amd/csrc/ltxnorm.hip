@@ -183,7 +183,7 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd_dt(void* out, const void* x
     if (st != LTXNORM_OK || empty) return st;
     if ((scale && misaligned(scale)) || (shift && misaligned(shift))) return LTXNORM_ERR_ALIGN;
     const int eb = ltxnorm_detail::elem_bytes(dtype);
-    const int64_t samples = (rows + rows_per_sample - 1) / rows_per_sample;
+    const int64_t samples = ltxnorm_detail::sample_count(rows, rows_per_sample);
     const int64_t nbytes = rows * hidden * eb;
     const int64_t mbytes = samples * hidden * eb;
     if ((scale && overlap(out, nbytes, scale, mbytes)) || (shift && overlap(out, nbytes, shift, mbytes)))

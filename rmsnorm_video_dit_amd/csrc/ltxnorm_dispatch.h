@@ -198,7 +198,7 @@ template <typename IO>
 ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
     constexpr int E = IO::kEpv;
     const Choice c = choose(op, r, E);
-    const int64_t samples = (r.rows + r.rows_per_sample - 1) / r.rows_per_sample;
+    const int64_t samples = sample_count(r.rows, r.rows_per_sample);
     KArgs a{r.out, r.x, r.w, r.cos_tab, r.sin_tab, r.scale, r.shift, r.rows, r.seq_len,
             r.rows_per_sample, (int32_t)(r.hidden / E), (int32_t)(r.hidden / (2 * E)),
             r.head_dim / (2 * E), r.head_dim / E, r.head_dim / 2, (int32_t)r.hidden, r.head_dim,

@@ -51,6 +51,14 @@ constexpr int64_t kMaxGeneralRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMa
 constexpr int64_t kMaxExchangeLds = 64 * 1024 - 256;
 constexpr int kLongThreads = 1024;        // two-pass kernel: one row per workgroup
 
+// Samples (modulation rows) for `rows` rows of `rows_per_sample` each, the
+// last possibly partial: ceil(rows / rows_per_sample) without overflow for
+// any rows >= 0 and rows_per_sample >= 1 (a caller may pass a huge
+// rows_per_sample to mean one sample).
+inline int64_t sample_count(int64_t rows, int64_t rows_per_sample) {
+    return rows / rows_per_sample + (rows % rows_per_sample != 0 ? 1 : 0);
+}
+
 // How a row is split over lanes.
 struct Plan {
     int wpr;    // wavefronts per row

@@ -162,6 +162,10 @@ def test_rope_interleaved_validation(kw, status):
     (dict(scale=A + 1024), ltx.ERR_ALIAS),
     (dict(shift=A - 64), ltx.ERR_ALIAS),
     (dict(rows=0, out=None, x=None), ltx.OK),
+    # a huge rows_per_sample means one sample: its row overlaps out's last
+    # 16 bytes (the sample count must not overflow on the way)
+    (dict(rows_per_sample=(1 << 63) - 1, scale=A + 8 * 2048 * 2 - 16), ltx.ERR_ALIAS),
+    (dict(rows_per_sample=(1 << 63) - 1, shift=A + 8 * 2048 * 2 - 16), ltx.ERR_ALIAS),
 ])
 def test_adaln_validation(kw, status):
     args = dict(out=A, x=A + 64 * MB, w=None, scale=A + 200 * MB, shift=A + 201 * MB, rows=8,

@@ -184,6 +184,22 @@ def test_adaln_null_modulation_any_hidden():
         assert np.array_equal(run_adaln(x, w, None, None, 2), run_rms(x, w))
 
 
+@pytest.mark.parametrize("hidden", [3076, 2048, 70001])
+def test_adaln_huge_rows_per_sample(hidden):
+    """rows_per_sample far beyond rows (here 2^63 - 1) means one sample: the
+    result equals rows_per_sample = rows, on the general, vector and two-pass
+    kernels (the sample count is computed without overflow)."""
+    rows = 6
+    announce(f"adaln rows_per_sample 2^63-1 hidden={hidden}")
+    x = datagen.make_x(rows, hidden, seed=hidden, stream=1)
+    w = datagen.make_w(hidden, seed=hidden, stream=2)
+    sc = datagen.make_x(1, hidden, seed=hidden, stream=4, sigma=0.25)
+    sh = datagen.make_x(1, hidden, seed=hidden, stream=5, sigma=0.25)
+    got = run_adaln(x, w, sc, sh, (1 << 63) - 1)
+    assert np.array_equal(got, run_adaln(x, w, sc, sh, rows))
+    check_adaln(x, w, sc, sh, rows, label=f"adaln one sample {hidden}")
+
+
 def test_rope_position_zero_long():
     announce("rope position zero, two-pass and LDS exchange")
     for heads, d in ((16, 72), (129, 136)):
