@@ -511,25 +511,39 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         const float* crow = a.cos_tab + pos * a.half;
         const float* srow = a.sin_tab + pos * a.half;
-        float c[NP], sn[NP];
-        if constexpr (WPR > 1) {  // with x, as in the rotate-half kernels
-            load_floats<NP>(crow + toff[0], c);
-            load_floats<NP>(srow + toff[0], sn);
-        }
+        // Up to four slots, every slot's slice is fetched at once (one L2
+        // round trip per row, not one per slot: d = 72 and 24 at
+        // [43690 x 1152], 64.4 -> 67.2 % and 65.1 -> 67.4 % of peak): with x
+        // for several wavefronts per row, as in the rotate-half kernels;
+        // after the reduction for one, which measured 0.8 points better than
+        // with x.  More slots would spill registers, so there slots 1.. load
+        // their slices in turn.
+        constexpr bool kAll = !SHARED && VPL <= 4;
+        constexpr int NT = kAll ? VPL : 1;  // table slices held at once
+        float c[NT][NP], sn[NT][NP];
+        auto load_tables = [&]() {
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                load_floats<NP>(crow + toff[k], c[k]);
+                load_floats<NP>(srow + toff[k], sn[k]);
+            }
+        };
+        if constexpr (WPR > 1) load_tables();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-        if constexpr (WPR == 1) {
-            load_floats<NP>(crow + toff[0], c);
-            load_floats<NP>(srow + toff[0], sn);
-        }
+        if constexpr (WPR == 1) load_tables();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = k * L + ln.t;
             const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
-            if (!SHARED && k > 0) {
-                load_floats<NP>(crow + toff[k], c);
-                load_floats<NP>(srow + toff[k], sn);
+            if constexpr (!SHARED && !kAll) {
+                if (k > 0) {
+                    load_floats<NP>(crow + toff[k], c[0]);
+                    load_floats<NP>(srow + toff[k], sn[0]);
+                }
             }
+            const float* ck = c[kAll ? k : 0];
+            const float* sk = sn[kAll ? k : 0];
             keep_packed(xv[k]);
             keep_packed(wv[k]);
             float y[E], g[E], o[E];
@@ -539,8 +553,8 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
             for (int e = 0; e < E; ++e) y[e] = (y[e] * rstd) * g[e];
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                o[2 * j] = y[2 * j] * c[j] - y[2 * j + 1] * sn[j];
-                o[2 * j + 1] = y[2 * j + 1] * c[j] + y[2 * j] * sn[j];
+                o[2 * j] = y[2 * j] * ck[j] - y[2 * j + 1] * sk[j];
+                o[2 * j + 1] = y[2 * j + 1] * ck[j] + y[2 * j] * sk[j];
             }
             if (in) store_stream(yr + v, IO::narrow(o));
         }
