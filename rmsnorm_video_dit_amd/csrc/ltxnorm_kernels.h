@@ -264,8 +264,9 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 //    groups, so group 0's partner is group 1 of some lane and group 1's
 //    partner is group 0 of another: two ds_bpermute sources, each fetching a
 //    fixed register.
-// The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot
-// and is read once per row, as in the power-of-two kernel.
+// The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot;
+// the wavefront reads the position's table rows once and the lanes take
+// their slices from each other (TableChunks).
 // ---------------------------------------------------------------------------
 template <typename IO, int VPL, int WPR, bool ODD>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
@@ -330,17 +331,15 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
             const bool in = l < lw && v < a.nvec && (WPR == 1 || active);
             xv[k] = in ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
         }
+        // the position's table rows, fetched with x by the first vph lanes
+        // (vph chunks of G floats per table) and handed out after the
+        // reduction: lane l needs the chunks at columns col0 and col1
         float c[E], ss[E];
-        auto load_tables = [&]() {
-            load_floats<G>(a.cos_tab + pos * a.half + col0, c);
-            load_floats<G>(a.cos_tab + pos * a.half + col1, c + G);
-            load_floats<G>(a.sin_tab + pos * a.half + col0, ss);
-            load_floats<G>(a.sin_tab + pos * a.half + col1, ss + G);
-        };
-        if constexpr (WPR > 1) load_tables();  // with x, as in the power-of-two kernel
+        TableChunks<G> tabs;
+        tabs.fetch(a.cos_tab + pos * a.half, a.sin_tab + pos * a.half, l, a.half / G);
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-        if constexpr (WPR == 1) load_tables();
+        tabs.gather(col0, col1, c, ss);
 #pragma unroll
         for (int e = 0; e < G; ++e) {
             ss[e] *= sg0;
@@ -511,35 +510,55 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         const float* crow = a.cos_tab + pos * a.half;
         const float* srow = a.sin_tab + pos * a.half;
-        // Up to four slots, every slot's slice is fetched at once (one L2
-        // round trip per row, not one per slot: d = 72 and 24 at
-        // [43690 x 1152], 64.4 -> 67.2 % and 65.1 -> 67.4 % of peak): with x
-        // for several wavefronts per row, as in the rotate-half kernels;
-        // after the reduction for one, which measured 0.8 points better than
-        // with x.  More slots would spill registers, so there slots 1.. load
-        // their slices in turn.
+        // Per-slot slices, one wavefront per row, heads of at most 64
+        // vectors: the wavefront fetches the position's table rows once, with
+        // x (vph chunks of NP floats), and after the reduction each slot takes
+        // its slice from the lane holding it (d = 72, 24, 40 at about 200 MB:
+        // 66.8 -> 68.8 %, 67.1 -> 68.8 %, 67.3 -> 73.1 % of peak; with one
+        // slice per row this measured slower on the [8192 x 2048] workload,
+        // and with 16 wavefronts per row it spills registers).  Otherwise, up to four slots fetch their slices at once
+        // (one L2 round trip per row, not one per slot: d = 72 and 24 at
+        // [43690 x 1152], 64.4 -> 67.2 % and 65.1 -> 67.4 %), with x for
+        // several wavefronts per row and after the reduction for one; more
+        // slots would spill registers, so there slots 1.. load in turn.
         constexpr bool kAll = !SHARED && VPL <= 4;
         constexpr int NT = kAll ? VPL : 1;  // table slices held at once
         float c[NT][NP], sn[NT][NP];
+        constexpr bool kGather = !SHARED && WPR == 1;
+        const bool gathered = kGather && vph <= kWave;
+        TableChunks<NP> tabs;
+        if constexpr (kGather) {
+            if (gathered) tabs.fetch(crow, srow, ln.lane, vph);
+        }
         auto load_tables = [&]() {
 #pragma unroll
             for (int k = 0; k < NT; ++k) {
-                load_floats<NP>(crow + toff[k], c[k]);
-                load_floats<NP>(srow + toff[k], sn[k]);
+                if (gathered) {
+                    tabs.gather1(toff[k], c[k], sn[k]);
+                } else {
+                    load_floats<NP>(crow + toff[k], c[k]);
+                    load_floats<NP>(srow + toff[k], sn[k]);
+                }
             }
         };
-        if constexpr (WPR > 1) load_tables();
+        if constexpr (WPR > 1) {
+            if (!gathered) load_tables();
+        }
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-        if constexpr (WPR == 1) load_tables();
+        if (WPR == 1 || gathered) load_tables();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = k * L + ln.t;
             const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
             if constexpr (!SHARED && !kAll) {
                 if (k > 0) {
-                    load_floats<NP>(crow + toff[k], c[0]);
-                    load_floats<NP>(srow + toff[k], sn[0]);
+                    if (gathered) {
+                        tabs.gather1(toff[k], c[0], sn[0]);
+                    } else {
+                        load_floats<NP>(crow + toff[k], c[0]);
+                        load_floats<NP>(srow + toff[k], sn[0]);
+                    }
                 }
             }
             const float* ck = c[kAll ? k : 0];
