@@ -186,9 +186,9 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd_dt(
  *
  *   out, x, weight, rows, hidden, eps, stream   as for ltxnorm_rmsnorm_fwd.
  *   scale, shift  bf16 [ceil(rows / rows_per_sample), hidden], row-major,
- *           read; NULL means zeros.  With both NULL the result equals
- *           ltxnorm_rmsnorm_fwd bit for bit.  16-byte aligned; must not
- *           overlap out.
+ *           read; NULL means zeros.  With both NULL the call runs
+ *           ltxnorm_rmsnorm_fwd's kernel and row split, and the result
+ *           equals it bit for bit.  16-byte aligned; must not overlap out.
  *   rows_per_sample  rows sharing one modulation row (S for [B, S, H] x);
  *           >= 1, else LTXNORM_ERR_SHAPE.
  */
@@ -225,7 +225,14 @@ typedef enum ltxnorm_op {
  * ends in "grid=resident": its grid is capped at the number of workgroups
  * the device holds at once, each workgroup looping over rows; every other
  * kernel takes one workgroup per group of rows.  heads and head_dim are
- * read for the RoPE operations only.
+ * read for the RoPE operations only.  LTXNORM_OP_ADALN describes a call
+ * with modulation rows (one with neither runs LTXNORM_OP_RMSNORM's kernel).
+ *
+ * The row split fixes the order in which a row's squares are added, so two
+ * operations give bit-identical normalised values only when they take the
+ * same split: RoPE at position 0 (cos 1, sin 0) equals RMSNorm bit for bit
+ * where both take the same split, and within the rounding of the sum
+ * elsewhere.
  *
  * Shapes are validated as the entry point validates them.  No pointer
  * other than buf is involved: the call enqueues nothing and needs no GPU.

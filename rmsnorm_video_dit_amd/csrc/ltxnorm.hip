@@ -190,7 +190,12 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd_dt(void* out, const void* x
         return LTXNORM_ERR_ALIAS;
     const Request r{out, x, weight, nullptr, nullptr, scale, shift, rows, hidden, 1,
                     rows_per_sample, 0, eps};
-    return dispatch(Op::kAdaLN, r, dtype, stream);
+    // Without modulation rows the operation is RMSNorm.  RMSNorm's kernel and
+    // row split then serve it: the split fixes the order in which a row's
+    // squares are added, so the result equals ltxnorm_rmsnorm_fwd bit for
+    // bit, and the modulation arithmetic is skipped.
+    return dispatch(scale == nullptr && shift == nullptr ? Op::kRmsNorm : Op::kAdaLN, r, dtype,
+                    stream);
 }
 
 LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_adaln_fwd(void* out, const void* x, const void* weight,

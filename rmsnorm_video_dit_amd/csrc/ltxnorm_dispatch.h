@@ -140,13 +140,19 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
 // Plans that plan_for can produce: one wavefront with 1..ONE items per lane;
 // 3..15 wavefronts with exactly SPREAD items per lane (2 wavefronts never
 // occur: a row too long for one wavefront needs more than 2 * ONE / SPREAD);
-// 16 wavefronts with SPREAD..MAXP items per lane.  lds_per_row: dynamic LDS
-// bytes per row slot of the block.
-template <typename LN, int ONE, int SPREAD, int MAXP>
+// 16 wavefronts with SPREAD..MAXP items per lane.  WIDE adds plan_wide's
+// plans: two or three wavefronts with 3..4 items per lane.  lds_per_row:
+// dynamic LDS bytes per row slot of the block.
+template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false>
 ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_per_row = 0) {
     switch (p.wpr) {
         case 1: return by_per<LN, 1, 1, ONE>(p, a, lds_per_row, s);
-        case 3: return by_per<LN, 3, SPREAD, SPREAD>(p, a, lds_per_row, s);
+        case 2:
+            if constexpr (WIDE) return by_per<LN, 2, 3, 4>(p, a, lds_per_row, s);
+            return LTXNORM_ERR_UNSUPPORTED;
+        case 3:
+            if constexpr (WIDE) return by_per<LN, 3, SPREAD, 4>(p, a, lds_per_row, s);
+            return by_per<LN, 3, SPREAD, SPREAD>(p, a, lds_per_row, s);
         case 4: return by_per<LN, 4, SPREAD, SPREAD>(p, a, lds_per_row, s);
         case 5: return by_per<LN, 5, SPREAD, SPREAD>(p, a, lds_per_row, s);
         case 6: return by_per<LN, 6, SPREAD, SPREAD>(p, a, lds_per_row, s);
@@ -206,8 +212,8 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
     switch (c.kernel) {
         case Kernel::kNone: return LTXNORM_OK;
         case Kernel::kRmsNorm: return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
-        case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
-        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+        case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
+        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopePacked:
             return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kRopePackedOdd:
@@ -216,9 +222,9 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
         case Kernel::kRopePair:
             return by_plan<RopePairL<IO>, 2, 1, kMaxVecPerLane / 2>(c.plan, a, stream);
         case Kernel::kRopeInterleaved:
-            return by_plan<RopeIlL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+            return by_plan<RopeIlL<IO, false>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopeInterleavedShared:
-            return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+            return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kShort:
             switch (op) {
                 case Op::kRmsNorm: return launch_short<IO, GOp::kRms>(c.lanes_per_row, a, stream);

@@ -85,6 +85,24 @@ inline Plan plan_for(int64_t items, int one_wave_max, int spread) {
     return Plan{wpr, per, items == (int64_t)per * lanes};
 }
 
+// The split for AdaLN and the fused RoPE kernels, which read more than x and
+// the weight per vector (modulation rows, table slices) or exchange values
+// between lanes: rows of 257..768 vectors go over two or three wavefronts
+// with 3-4 vectors per lane instead of 3-6 wavefronts with 2.  Measured at
+// about 200 MB per launch, bf16 (% of 8 TB/s, plan_for's split -> this one):
+// AdaLN 55.6 -> 67.0 at hidden 2304, 59.8 -> 68.4 at 2560, 66.4 -> 67.6 at
+// 3072, 63.3 -> 65.2 at 5120, 63.7 -> 65.0 at 6144, even at 4096; rotate-half
+// RoPE (heads of 128) 65.5 -> 73.8 at 2304, 69.2 -> 74.5 at 2560, 73.5 ->
+// 74.8 at 3072, 72.6 -> 74.1 at 3584.  At 8192 (1024 vectors) AdaLN keeps
+// plan_for's 8 x 2 (65.3 against 62.1 for 4 x 4).
+constexpr int64_t kWideMin = (int64_t)kWave * 4 + 1;
+constexpr int64_t kWideMax = (int64_t)kWave * 4 * 3;
+constexpr int64_t kWideIlMax = (int64_t)kWave * 5;
+inline Plan plan_wide(int64_t items) {
+    if (items < kWideMin || items > kWideMax) return plan_for(items, 4, 2);
+    return plan_for(items, 4, 4);
+}
+
 // Rows per workgroup: four single-wavefront rows, two rows of 2-3
 // wavefronts, one row of 4-16 wavefronts.
 constexpr int rows_per_block(int wpr) { return wpr == 1 ? 4 : (wpr <= 3 ? 2 : 1); }
@@ -150,7 +168,7 @@ inline Choice choose(Op op, const Request& r, int E) {
             return gfits ? general : two_pass;
         case Op::kAdaLN:
             if (short_row) return short_rows;
-            if (whole && fits) return Choice{Kernel::kAdaLN, plan_for(nvec, 4, 2), 0, 0};
+            if (whole && fits) return Choice{Kernel::kAdaLN, plan_wide(nvec), 0, 0};
             return gfits ? general : two_pass;
         case Op::kRopeRotateHalf: {
             const int d = r.head_dim;
@@ -160,7 +178,7 @@ inline Choice choose(Op op, const Request& r, int E) {
                 const int P = d / (2 * E);
                 if ((P & (P - 1)) == 0 && P <= kWave / 2) {  // partner lanes within one wavefront
                     if (short_row) return short_rows;     // partner l ^ P inside the row's lanes
-                    return Choice{Kernel::kRopeXor, plan_for(nvec, 4, 2), 0, 0};
+                    return Choice{Kernel::kRopeXor, plan_wide(nvec), 0, 0};
                 }
             }
             const int vph = d / E;
@@ -182,7 +200,12 @@ inline Choice choose(Op op, const Request& r, int E) {
         case Op::kRopeInterleaved: {
             if (whole && fits && r.head_dim % E == 0) {
                 if (short_row) return short_rows;
-                const Plan p = plan_for(nvec, 4, 2);
+                // The wide split only where plan_for's 3 x 2 leaves a sixth
+                // or more of its slots idle: hidden 2304 (bf16, heads of
+                // 128) 68.8 -> 74.0 %, 2560 71.0 -> 74.0 %; from 384 vectors
+                // on, plan_for's split measured 1-4 points better (3072,
+                // 3584, 4096, 6144, 8192).
+                const Plan p = nvec <= kWideIlMax ? plan_wide(nvec) : plan_for(nvec, 4, 2);
                 const int vph = r.head_dim / E;
                 return Choice{(kWave * p.wpr) % vph == 0 ? Kernel::kRopeInterleavedShared
                                                          : Kernel::kRopeInterleaved,

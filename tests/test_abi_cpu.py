@@ -261,6 +261,14 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_RMSNORM, 3072, 0, 0, ltx.F32, "rmsnorm_kernel", 6, 2),
     (ltx.OP_RMSNORM, 65536, 0, 0, ltx.BF16, "rmsnorm_kernel", 16, 8),
     (ltx.OP_ADALN, 2048, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 1, 4),
+    # AdaLN and the fused RoPE kernels: rows of 257..768 vectors over 2-3
+    # wavefronts with 3-4 vectors per lane; longer rows keep the 2-vector split
+    (ltx.OP_ADALN, 2304, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 2, 3),
+    (ltx.OP_ADALN, 3072, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 2, 3),
+    (ltx.OP_ADALN, 4096, 0, 0, ltx.F16, "rmsnorm_adaln_kernel", 2, 4),
+    (ltx.OP_ADALN, 5120, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 3, 4),
+    (ltx.OP_ADALN, 2048, 0, 0, ltx.F32, "rmsnorm_adaln_kernel", 2, 4),
+    (ltx.OP_ADALN, 8192, 0, 0, ltx.BF16, "rmsnorm_adaln_kernel", 8, 2),
     # rows that are not whole vectors, and rows past the register budget
     (ltx.OP_RMSNORM, 3076, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 4, 2),
     (ltx.OP_RMSNORM, 1, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
@@ -271,7 +279,9 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     # rotate-half: power-of-two half heads, head-packed lanes, pairs in a lane,
     # LDS exchange, two passes
     (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_xor_kernel", 1, 4),
-    (ltx.OP_ROPE, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 2),
+    (ltx.OP_ROPE, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 2, 3),
+    (ltx.OP_ROPE, 6144, 48, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 4),
+    (ltx.OP_ROPE, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 8, 2),
     (ltx.OP_ROPE, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 3),
     (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 3, 2),
     (ltx.OP_ROPE, 960, 24, 40, ltx.F32, "rmsnorm_rope_packed_kernel", 1, 4),
@@ -283,6 +293,10 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     # interleaved: one table slice per row when a head's vectors divide the lanes
     (ltx.OP_ROPE_INTERLEAVED, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 1, 4),
     (ltx.OP_ROPE_INTERLEAVED, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 3),
+    # ... the wide split only for 257..320 vectors
+    (ltx.OP_ROPE_INTERLEAVED, 2304, 18, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 2, 3),
+    (ltx.OP_ROPE_INTERLEAVED, 2520, 35, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 2, 3),
+    (ltx.OP_ROPE_INTERLEAVED, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 3, 2),
     (ltx.OP_ROPE_INTERLEAVED, 70, 7, 10, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
     # short rows (at most 32 vectors): lanes per row given in the wpr column
     (ltx.OP_RMSNORM, 128, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, None),
@@ -391,7 +405,13 @@ def test_kernel_choice_always_covers_the_row():
                 assert d % E == 0
             continue
         wpr, rpb, threads = int(f["wavefronts_per_row"]), int(f["rows_per_block"]), int(f["threads"])
-        assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024 and wpr != 2
+        assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024
+        wide = (name in ("rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel") and 256 < touched <= 768) or \
+            (name.startswith("rmsnorm_rope_interleaved_kernel") and 256 < touched <= 320)
+        if wide:  # two or three wavefronts, 3-4 vectors per lane
+            assert wpr in (2, 3) and 3 <= int(f["vectors_per_lane"]) <= 4, desc
+        else:
+            assert wpr != 2, desc
         assert rpb == (4 if wpr == 1 else 2 if wpr <= 3 else 1)
         if name == "rmsnorm_rope_pair_kernel":
             per = int(f["pairs_per_lane"])

@@ -216,6 +216,49 @@ def test_lowp_rope(dtype, heads, head_dim, interleaved, rows, seq_len):
                label=f"rope {dtype} {heads}x{head_dim} il={interleaved}")
 
 
+# AdaLN and the fused RoPE kernels spread rows of 257..768 vectors (320 for
+# interleaved pairs) over two or three wavefronts with 3-4 vectors per lane:
+# every such instance (2 or 3 wavefronts, 3 or 4 vectors, last vector whole
+# or masked, shared or per-slot table slices) in the three dtypes, with an odd
+# row count so the second row slot of the last workgroup idles.
+WIDE_SHAPES = [
+    ("bf16", "adaln", 2304, 0), ("bf16", "adaln", 3584, 0), ("bf16", "adaln", 4104, 0),
+    ("bf16", "adaln", 4608, 0), ("bf16", "adaln", 5120, 0), ("bf16", "adaln", 6144, 0),
+    ("f16", "adaln", 4096, 0), ("f32", "adaln", 1152, 0), ("f32", "adaln", 2560, 0),
+    ("f32", "adaln", 3072, 0),
+    ("bf16", "half", 2304, 128), ("bf16", "half", 3584, 128), ("bf16", "half", 4224, 128),
+    ("bf16", "half", 4608, 128), ("bf16", "half", 5120, 128), ("f16", "half", 6144, 128),
+    ("f32", "half", 2048, 128), ("f32", "half", 2304, 128),
+    ("bf16", "il", 2304, 128), ("f16", "il", 2560, 128), ("bf16", "il", 2520, 72),
+    ("f32", "il", 1152, 64),
+]
+
+
+@pytest.mark.parametrize("dtype,op,hidden,head_dim", WIDE_SHAPES)
+@pytest.mark.parametrize("rows", [37, 1001])
+def test_wide_split_shapes(dtype, op, hidden, head_dim, rows):
+    code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+    opc = {"adaln": ltx.OP_ADALN, "half": ltx.OP_ROPE, "il": ltx.OP_ROPE_INTERLEAVED}[op]
+    heads = hidden // head_dim if head_dim else 0
+    desc = ltx.ltxnorm_describe_launch(opc, rows, hidden, heads, head_dim, code)
+    f = dict(kv.split("=") for kv in desc.split()[1:])
+    assert f["wavefronts_per_row"] in ("2", "3") and f["vectors_per_lane"] in ("3", "4"), desc
+    announce(f"wide split {dtype} {op} rows={rows} hidden={hidden} d={head_dim}: {desc}")
+    seed = hidden + rows + 29
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    if op == "adaln":
+        rps = 300
+        samples = -(-rows // rps)
+        sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.3, dtype=dtype)
+        sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.3, dtype=dtype)
+        check_adaln(x, w, sc, sh, rps, label=f"adaln {dtype} {rows}x{hidden}")
+    else:
+        c, s = datagen.rope_tables(4096 if rows > 100 else 17, head_dim)
+        check_rope(x, w, c, s, heads, head_dim, interleaved=op == "il",
+                   label=f"rope {dtype} {op} {rows}x{heads}x{head_dim}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_lowp_invariants(dtype):
     """NULL weight = ones; position 0 = RMSNorm; null modulation = RMSNorm;
@@ -227,9 +270,17 @@ def test_lowp_invariants(dtype):
     base = run_rms(x, w)
     assert np.array_equal(base, run_rms(x, w))
     assert np.array_equal(run_rms(x, None), run_rms(x, ones))
+    # position 0 equals RMSNorm bit for bit where both take the same row
+    # split (the split fixes the order of the sum of squares); elsewhere
+    # check_rope holds it to the oracle
     c0, s0 = datagen.rope_tables(1, 64)
-    assert np.array_equal(run_rope(x, w, c0, s0, 32, 64), base)
-    assert np.array_equal(run_rope(x, w, c0, s0, 32, 64, interleaved=True), base)
+    code = {"f16": ltx.F16, "f32": ltx.F32}[dtype]
+    rms_plan = ltx.ltxnorm_describe_launch(ltx.OP_RMSNORM, 200, 2048, 0, 0, code).split()[1:3]
+    for op, il in ((ltx.OP_ROPE, False), (ltx.OP_ROPE_INTERLEAVED, True)):
+        if ltx.ltxnorm_describe_launch(op, 200, 2048, 32, 64, code).split()[1:3] == rms_plan:
+            assert np.array_equal(run_rope(x, w, c0, s0, 32, 64, interleaved=il), base)
+        else:
+            check_rope(x, w, c0, s0, 32, 64, interleaved=il, label=f"rope {dtype} position 0")
     assert np.array_equal(run_adaln(x, w, None, None, 100), base)
     xt = dev_bf16(x)
     ltx.rmsnorm(xt, dev_bf16(w), 1e-6, out=xt)
@@ -382,6 +433,11 @@ def test_adaln_invariants():
     minus1 = np.full((3, 3072), 0xBF80, dtype=np.uint16)
     got = run_adaln(x, w, minus1, sh, 200)
     assert np.array_equal(got, np.repeat(sh, 200, axis=0))
+    # one NULL row: the kernel reads a NULL scale as +0 and a NULL shift as -0
+    zeros = np.zeros((3, 3072), dtype=np.uint16)
+    neg_zeros = np.full((3, 3072), 0x8000, dtype=np.uint16)
+    assert np.array_equal(run_adaln(x, w, None, sh, 200), run_adaln(x, w, zeros, sh, 200))
+    assert np.array_equal(run_adaln(x, w, sc, None, 200), run_adaln(x, w, sc, neg_zeros, 200))
     xt = dev_bf16(x)
     ltx.rmsnorm_adaln(xt, dev_bf16(w), dev_bf16(sc), dev_bf16(sh), 1e-6, out=xt, rows_per_sample=200)
     assert np.array_equal(host_bits(xt), ref)
