@@ -141,9 +141,10 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
 // 3..15 wavefronts with exactly SPREAD items per lane (2 wavefronts never
 // occur: a row too long for one wavefront needs more than 2 * ONE / SPREAD);
 // 16 wavefronts with SPREAD..MAXP items per lane.  WIDE adds plan_wide's
-// plans: two or three wavefronts with 3..4 items per lane.  lds_per_row:
+// plans: two or three wavefronts with 3..4 items per lane; PER4 > SPREAD
+// adds four wavefronts with SPREAD..PER4 (plan_wide_xor).  lds_per_row:
 // dynamic LDS bytes per row slot of the block.
-template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false>
+template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false, int PER4 = SPREAD>
 ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_per_row = 0) {
     switch (p.wpr) {
         case 1: return by_per<LN, 1, 1, ONE>(p, a, lds_per_row, s);
@@ -153,7 +154,7 @@ ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_
         case 3:
             if constexpr (WIDE) return by_per<LN, 3, SPREAD, 4>(p, a, lds_per_row, s);
             return by_per<LN, 3, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 4: return by_per<LN, 4, SPREAD, SPREAD>(p, a, lds_per_row, s);
+        case 4: return by_per<LN, 4, SPREAD, PER4>(p, a, lds_per_row, s);
         case 5: return by_per<LN, 5, SPREAD, SPREAD>(p, a, lds_per_row, s);
         case 6: return by_per<LN, 6, SPREAD, SPREAD>(p, a, lds_per_row, s);
         case 7: return by_per<LN, 7, SPREAD, SPREAD>(p, a, lds_per_row, s);
@@ -213,7 +214,7 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
         case Kernel::kNone: return LTXNORM_OK;
         case Kernel::kRmsNorm: return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
-        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
+        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3>(c.plan, a, stream);
         case Kernel::kRopePacked:
             return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kRopePackedOdd:

@@ -280,7 +280,9 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     # LDS exchange, two passes
     (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_xor_kernel", 1, 4),
     (ltx.OP_ROPE, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 2, 3),
-    (ltx.OP_ROPE, 6144, 48, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 4),
+    (ltx.OP_ROPE, 4608, 36, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 3),
+    (ltx.OP_ROPE, 5120, 40, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 4, 3),
+    (ltx.OP_ROPE, 6144, 48, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 4, 3),
     (ltx.OP_ROPE, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 8, 2),
     (ltx.OP_ROPE, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 3),
     (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 3, 2),
@@ -408,8 +410,10 @@ def test_kernel_choice_always_covers_the_row():
         assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024
         wide = (name in ("rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel") and 256 < touched <= 768) or \
             (name.startswith("rmsnorm_rope_interleaved_kernel") and 256 < touched <= 320)
-        if wide:  # two or three wavefronts, 3-4 vectors per lane
-            assert wpr in (2, 3) and 3 <= int(f["vectors_per_lane"]) <= 4, desc
+        if wide:  # two or three wavefronts with 3-4 vectors per lane, or four with 3
+            per = int(f["vectors_per_lane"])
+            four = name == "rmsnorm_rope_xor_kernel" and touched > 576
+            assert (wpr, per) == (4, 3) if four else (wpr in (2, 3) and 3 <= per <= 4), desc
         else:
             assert wpr != 2, desc
         assert rpb == (4 if wpr == 1 else 2 if wpr <= 3 else 1)

@@ -217,9 +217,10 @@ def test_lowp_rope(dtype, heads, head_dim, interleaved, rows, seq_len):
 
 
 # AdaLN and the fused RoPE kernels spread rows of 257..768 vectors (320 for
-# interleaved pairs) over two or three wavefronts with 3-4 vectors per lane:
-# every such instance (2 or 3 wavefronts, 3 or 4 vectors, last vector whole
-# or masked, shared or per-slot table slices) in the three dtypes, with an odd
+# interleaved pairs) over two or three wavefronts with 3-4 vectors per lane
+# (rotate-half: four wavefronts with 3 from 577 vectors on): every such
+# instance (2, 3 or 4 wavefronts, 3 or 4 vectors, last vector whole or
+# masked, shared or per-slot table slices) in the three dtypes, with an odd
 # row count so the second row slot of the last workgroup idles.
 WIDE_SHAPES = [
     ("bf16", "adaln", 2304, 0), ("bf16", "adaln", 3584, 0), ("bf16", "adaln", 4104, 0),
@@ -228,7 +229,7 @@ WIDE_SHAPES = [
     ("f32", "adaln", 3072, 0),
     ("bf16", "half", 2304, 128), ("bf16", "half", 3584, 128), ("bf16", "half", 4224, 128),
     ("bf16", "half", 4608, 128), ("bf16", "half", 5120, 128), ("f16", "half", 6144, 128),
-    ("f32", "half", 2048, 128), ("f32", "half", 2304, 128),
+    ("f32", "half", 2048, 128), ("f32", "half", 2304, 128), ("f32", "half", 2560, 128),
     ("bf16", "il", 2304, 128), ("f16", "il", 2560, 128), ("bf16", "il", 2520, 72),
     ("f32", "il", 1152, 64),
 ]
@@ -242,7 +243,8 @@ def test_wide_split_shapes(dtype, op, hidden, head_dim, rows):
     heads = hidden // head_dim if head_dim else 0
     desc = ltx.ltxnorm_describe_launch(opc, rows, hidden, heads, head_dim, code)
     f = dict(kv.split("=") for kv in desc.split()[1:])
-    assert f["wavefronts_per_row"] in ("2", "3") and f["vectors_per_lane"] in ("3", "4"), desc
+    assert (f["wavefronts_per_row"], f["vectors_per_lane"]) in (
+        ("2", "3"), ("2", "4"), ("3", "3"), ("3", "4"), ("4", "3")), desc
     announce(f"wide split {dtype} {op} rows={rows} hidden={hidden} d={head_dim}: {desc}")
     seed = hidden + rows + 29
     x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
