@@ -176,17 +176,21 @@ ltxnorm_status launch_long(const KArgs& a, hipStream_t stream) {
     return launch((const void*)&rmsnorm_long_kernel<IO, OP>, kLongThreads, 1, a, 0, stream);
 }
 
-// Short rows: the instance for the lanes per row.
+// Segmented rows: the instance for the lanes per row and vectors per lane.
 template <typename IO, GOp OP>
-ltxnorm_status launch_short(int lanes, const KArgs& a, hipStream_t stream) {
+ltxnorm_status launch_short(int lanes, int per, const KArgs& a, hipStream_t stream) {
     const void* fn = nullptr;
-    switch (lanes) {
-        case 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 1>; break;
-        case 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 2>; break;
-        case 4: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 4>; break;
-        case 8: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 8>; break;
-        case 16: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16>; break;
-        case 32: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32>; break;
+    switch (lanes * 8 + per) {
+        case 1 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 1, 1>; break;
+        case 2 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 2, 1>; break;
+        case 4 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 4, 1>; break;
+        case 8 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 8, 1>; break;
+        case 16 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 1>; break;
+        case 32 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 1>; break;
+        case 16 * 8 + 3: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 3>; break;
+        case 16 * 8 + 5: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 5>; break;
+        case 32 * 8 + 3: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 3>; break;
+        case 32 * 8 + 5: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 5>; break;
         default: return LTXNORM_ERR_UNSUPPORTED;
     }
     return launch(fn, kWave * kShortWavesPerBlock, kShortWavesPerBlock * (kWave / lanes), a, 0, stream);
@@ -228,10 +232,10 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
             return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kShort:
             switch (op) {
-                case Op::kRmsNorm: return launch_short<IO, GOp::kRms>(c.lanes_per_row, a, stream);
-                case Op::kAdaLN: return launch_short<IO, GOp::kAda>(c.lanes_per_row, a, stream);
-                case Op::kRopeRotateHalf: return launch_short<IO, GOp::kRopeHalf>(c.lanes_per_row, a, stream);
-                case Op::kRopeInterleaved: return launch_short<IO, GOp::kRopeIl>(c.lanes_per_row, a, stream);
+                case Op::kRmsNorm: return launch_short<IO, GOp::kRms>(c.lanes_per_row, c.plan.per, a, stream);
+                case Op::kAdaLN: return launch_short<IO, GOp::kAda>(c.lanes_per_row, c.plan.per, a, stream);
+                case Op::kRopeRotateHalf: return launch_short<IO, GOp::kRopeHalf>(c.lanes_per_row, c.plan.per, a, stream);
+                case Op::kRopeInterleaved: return launch_short<IO, GOp::kRopeIl>(c.lanes_per_row, c.plan.per, a, stream);
             }
             return LTXNORM_ERR_UNSUPPORTED;
         case Kernel::kGeneral:

@@ -54,17 +54,24 @@ rmsnorm_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Short rows (at most 32 vectors: H <= 256 bf16/fp16 or 128 fp32, as in
-// per-head normalisation).  S lanes per row, S the power of two at or above
-// the row's vector count, one vector per lane, 64 / S rows per wavefront and
-// four wavefronts per workgroup: a load instruction covers 64 / S
-// consecutive rows, where one wavefront per row would leave most lanes idle
-// (H = 128 measured 28 % of peak that way).  The sum of squares is reduced
-// inside each S-lane segment by the first log2 S steps of the wavefront
-// reduction (and an xor-16 exchange for S = 32), so every lane of a row ends
-// with the same bits.  RMSNorm, AdaLN, and RoPE whose partners stay inside a
-// row's lanes: rotate-half with power-of-two half heads (partner lane
-// l ^ P) and interleaved pairs.
+// Rows in segments of S lanes (S a power of two up to 32), V vectors per
+// lane: lane l of a row's segment holds vectors k*S + l, 64 / S rows per
+// wavefront, four wavefronts per workgroup.
+//  * Short rows (at most 32 vectors: H <= 256 bf16/fp16 or 128 fp32, as in
+//    per-head normalisation) take V = 1 and S the power of two at or above
+//    the vector count: one wavefront per row would leave most lanes idle
+//    (H = 128 measured 28 % of peak that way).
+//  * Rows of 33..160 vectors whose count leaves many of a wavefront's lanes
+//    idle take S = 16 or 32 with V = 3 or 5 (40 vectors: 16 x 3; 72: 16 x 5;
+//    88: 32 x 3; 144: 32 x 5), filling 80-100 % of the slots where one
+//    wavefront per row fills 56-75 % (the choice and its measurements are
+//    with segments_for).
+// A load instruction covers 64 / S rows' runs of S vectors.  The sum of
+// squares is reduced inside each segment by the first log2 S steps of the
+// wavefront reduction (and an xor-16 exchange for S = 32), so every lane of a
+// row ends with the same bits.  RMSNorm, AdaLN, and RoPE whose partners stay
+// inside a row's lanes: rotate-half with power-of-two half heads of P <= S/2
+// vectors (partner lane l ^ P in the same slot) and interleaved pairs.
 // ---------------------------------------------------------------------------
 template <int S>
 __device__ __forceinline__ float segment_sum(float v) {
@@ -80,7 +87,8 @@ __device__ __forceinline__ float segment_sum(float v) {
 }
 
 
-template <typename IO, GOp OP, int S>
+
+template <typename IO, GOp OP, int S, int V>
 __global__ void __launch_bounds__(kWave * kShortWavesPerBlock)
 rmsnorm_short_kernel(const KArgs a) {
     constexpr int E = IO::kEpv;
@@ -88,84 +96,108 @@ rmsnorm_short_kernel(const KArgs a) {
     constexpr int RPB = kShortWavesPerBlock * G;   // rows per workgroup
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int l = lane % S;                // vector within the row
+    const int l = lane % S;                // first vector of the lane within the row
     const int seg = lane / S;              // row within the wavefront
-    const bool lin = l < a.nvec;
-    u32x4 wv = (a.w != nullptr && lin) ? reinterpret_cast<const u32x4*>(a.w)[l] : splat(IO::kOne);
+    u32x4 wv[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int v = k * S + l;
+        wv[k] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+    }
 
     // rotation constants of this lane (the xor layout of the power-of-two
-    // kernel, within the row's lanes; or the interleaved table columns)
-    int src = 0, toff = 0;
+    // kernel, within the row's lanes: the same for every slot, since S is a
+    // multiple of 2P; or the interleaved table columns of each slot)
+    int src = 0, toff[V];
     float sgn = 1.0f;
+#pragma unroll
+    for (int k = 0; k < V; ++k) toff[k] = 0;
     if constexpr (OP == GOp::kRopeHalf) {
         const int P = a.vec_per_half;
         src = (lane ^ P) << 2;
         sgn = (l & P) ? 1.0f : -1.0f;
-        toff = (l & (P - 1)) * E;
+        toff[0] = (l & (P - 1)) * E;
     } else if constexpr (OP == GOp::kRopeIl) {
-        toff = (l % a.vec_per_head) * (E / 2);
+#pragma unroll
+        for (int k = 0; k < V; ++k) toff[k] = ((k * S + l) % a.vec_per_head) * (E / 2);
     }
 
     for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows; base += (int64_t)gridDim.x * RPB) {
         const int64_t row = base + wave * G + seg;
-        const bool in = lin && row < a.rows;
+        const bool rin = row < a.rows;
         const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
-        u32x4 xv = in ? load_stream(xr + l) : u32x4{0u, 0u, 0u, 0u};
+        u32x4 xv[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int v = k * S + l;
+            xv[k] = (rin && v < a.nvec) ? load_stream(xr + v) : u32x4{0u, 0u, 0u, 0u};
+        }
 
         // per-row side inputs, fetched together with x
-        u32x4 sv = {0u, 0u, 0u, 0u}, hv = splat(IO::kNegZero);
-        float c[E], sn[E];
+        u32x4 sv[V], hv[V];
+        constexpr int NT = OP == GOp::kRopeIl ? V : 1;   // table slices per row
+        constexpr int TW = OP == GOp::kRopeIl ? E / 2 : E;
+        float c[NT][TW], sn[NT][TW];
         if constexpr (OP == GOp::kAda) {
-            const int64_t sample = in ? row / a.rows_per_sample : 0;
-            if (a.scale != nullptr && in) sv = reinterpret_cast<const u32x4*>(a.scale)[sample * a.nvec + l];
-            if (a.shift != nullptr && in) hv = reinterpret_cast<const u32x4*>(a.shift)[sample * a.nvec + l];
-        } else if constexpr (OP == GOp::kRopeHalf) {
-            const int64_t pos = in ? row % a.seq_len : 0;
-            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
-            load_floats<E>(a.sin_tab + pos * a.half + toff, sn);
-        } else if constexpr (OP == GOp::kRopeIl) {
-            const int64_t pos = in ? row % a.seq_len : 0;
-            load_floats<E / 2>(a.cos_tab + pos * a.half + toff, c);
-            load_floats<E / 2>(a.sin_tab + pos * a.half + toff, sn);
+            const int64_t sample = rin ? row / a.rows_per_sample : 0;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const int v = k * S + l;
+                const bool in = rin && v < a.nvec;
+                sv[k] = (a.scale != nullptr && in) ? reinterpret_cast<const u32x4*>(a.scale)[sample * a.nvec + v]
+                                                   : u32x4{0u, 0u, 0u, 0u};
+                hv[k] = (a.shift != nullptr && in) ? reinterpret_cast<const u32x4*>(a.shift)[sample * a.nvec + v]
+                                                   : splat(IO::kNegZero);
+            }
+        } else if constexpr (OP == GOp::kRopeHalf || OP == GOp::kRopeIl) {
+            const int64_t pos = rin ? row % a.seq_len : 0;
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                load_floats<TW>(a.cos_tab + pos * a.half + toff[k], c[k]);
+                load_floats<TW>(a.sin_tab + pos * a.half + toff[k], sn[k]);
+            }
         }
 
-        float f[E], g[E];
-        IO::widen(xv, f);
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) part = fmaf(f[e], f[e], part);
+        const float part = sum_squares<IO, V>(xv);
         const float rstd = rstd_of(segment_sum<S>(part), a.hidden_f, a.eps);
-        keep_packed(wv);
-        IO::widen(wv, g);
 #pragma unroll
-        for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
+        for (int k = 0; k < V; ++k) {
+            const int v = k * S + l;
+            float f[E], g[E];
+            keep_packed(xv[k]);
+            IO::widen(xv[k], f);
+            keep_packed(wv[k]);
+            IO::widen(wv[k], g);
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
 
-        float o[E];
-        if constexpr (OP == GOp::kAda) {
-            float sc[E], sh[E];
-            IO::widen(sv, sc);
-            IO::widen(hv, sh);
+            float o[E];
+            if constexpr (OP == GOp::kAda) {
+                float sc[E], sh[E];
+                IO::widen(sv[k], sc);
+                IO::widen(hv[k], sh);
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = f[e] * (1.0f + sc[e]) + sh[e];
-        } else if constexpr (OP == GOp::kRopeHalf) {
-            // the partner lane's normalised values; -sin in the first half
+                for (int e = 0; e < E; ++e) o[e] = f[e] * (1.0f + sc[e]) + sh[e];
+            } else if constexpr (OP == GOp::kRopeHalf) {
+                // the partner lane's normalised values; -sin in the first half
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float par = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, f[e])));
-                o[e] = f[e] * c[e] + par * (sn[e] * sgn);
+                for (int e = 0; e < E; ++e) {
+                    const float par = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, f[e])));
+                    o[e] = f[e] * c[0][e] + par * (sn[0][e] * sgn);
+                }
+            } else if constexpr (OP == GOp::kRopeIl) {
+#pragma unroll
+                for (int j = 0; j < E / 2; ++j) {
+                    o[2 * j] = f[2 * j] * c[k][j] - f[2 * j + 1] * sn[k][j];
+                    o[2 * j + 1] = f[2 * j + 1] * c[k][j] + f[2 * j] * sn[k][j];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = f[e];
             }
-        } else if constexpr (OP == GOp::kRopeIl) {
-#pragma unroll
-            for (int j = 0; j < E / 2; ++j) {
-                o[2 * j] = f[2 * j] * c[j] - f[2 * j + 1] * sn[j];
-                o[2 * j + 1] = f[2 * j + 1] * c[j] + f[2 * j] * sn[j];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = f[e];
+            if (rin && v < a.nvec) store_stream(yr + v, IO::narrow(o));
         }
-        if (in) store_stream(yr + l, IO::narrow(o));
     }
 }
 

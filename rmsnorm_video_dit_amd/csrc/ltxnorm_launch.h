@@ -128,7 +128,7 @@ enum class Kernel {
     kRopePair,               // rmsnorm_rope_pair_kernel
     kRopeInterleaved,        // rmsnorm_rope_interleaved_kernel, table slice per slot
     kRopeInterleavedShared,  // rmsnorm_rope_interleaved_kernel, one table slice per row
-    kShort,                  // rmsnorm_short_kernel (rows of at most 32 vectors)
+    kShort,                  // rmsnorm_short_kernel (rows in segments of at most 32 lanes)
     kGeneral,                // rmsnorm_general_kernel (any row length)
     kLong,                   // rmsnorm_long_kernel (two passes)
 };
@@ -141,15 +141,43 @@ constexpr int kShortWavesPerBlock = 4;
 
 struct Choice {
     Kernel kernel;
-    Plan plan;            // one-pass kernels: row split
+    Plan plan;            // one-pass kernels: row split; segmented rows: per = vectors per lane
     int64_t lds_per_row;  // dynamic LDS bytes per row slot (general rotate-half)
-    int lanes_per_row;    // short rows: lanes per row (a power of two <= 32)
+    int lanes_per_row;    // segmented rows: lanes per row (a power of two <= 32)
 };
 
 inline int pow2_at_least(int64_t n) {
     int p = 1;
     while (p < n) p <<= 1;
     return p;
+}
+
+// Rows of 33..160 vectors in segments of S lanes with V vectors per lane,
+// where that fills more of a wavefront than one row per wavefront with
+// ceil(n / 64) vectors per lane: (S, V) among (16, 3), (16, 5), (32, 3) and,
+// with `with_32x5`, (32, 5), the fewest slots that still cover the row.
+// {0, 0} when none does better (row lengths near a multiple of 64).  Against
+// one wavefront per row, bf16 at about 200 MB per launch: RMSNorm at hidden
+// 320 (16 x 3) 52-60 -> 76 %, 576 (16 x 5) 73-74 -> 75.5 %; AdaLN at 320
+// 47 -> 69 %, 576 59 -> 69.5 %, 704 (32 x 3) 65.5 -> 70 %, 1152 (32 x 5) 67.1
+// -> 68.7 %; rotate-half RoPE (heads of 64) at 576 55 -> 68.7 %, 1152 67.4 ->
+// 70.4 %; interleaved at 576 60 -> 67 %.  32 x 5 lost for interleaved RoPE
+// (1152: 68 -> 66 %) and RMSNorm (75.9 -> 75.5 %), which keep one wavefront.
+struct Segments {
+    int lanes, per;
+};
+inline Segments segments_for(int64_t n, bool with_32x5) {
+    static constexpr Segments kShapes[] = {{16, 3}, {16, 5}, {32, 3}, {32, 5}};
+    const int64_t one_wave = (int64_t)kWave * ((n + kWave - 1) / kWave);
+    Segments best{0, 0};
+    if (n <= kMaxShortVectors || n > (int64_t)kWave * 4) return best;
+    for (const Segments& c : kShapes) {
+        if (c.lanes == 32 && c.per == 5 && !with_32x5) continue;
+        const int64_t slots = (int64_t)c.lanes * c.per;
+        if (slots >= n && slots < one_wave && (best.lanes == 0 || slots < (int64_t)best.lanes * best.per))
+            best = c;
+    }
+    return best;
 }
 
 // The kernel and row split for a validated request with E elements per
@@ -171,13 +199,18 @@ inline Choice choose(Op op, const Request& r, int E) {
     const int64_t nvec = H / E;
     const bool short_row = whole && nvec <= kMaxShortVectors;
     const Choice short_rows{Kernel::kShort, Plan{1, 1, false}, 0, short_row ? pow2_at_least(nvec) : 0};
+    const bool wide_op = op == Op::kAdaLN || op == Op::kRopeRotateHalf;
+    const Segments sg = whole ? segments_for(nvec, wide_op) : Segments{0, 0};
+    const Choice segmented{Kernel::kShort, Plan{1, sg.per, false}, 0, sg.lanes};
     switch (op) {
         case Op::kRmsNorm:
             if (short_row) return short_rows;
+            if (sg.lanes) return segmented;
             if (whole && fits) return Choice{Kernel::kRmsNorm, plan_for(nvec, 4, 2), 0, 0};
             return gfits ? general : two_pass;
         case Op::kAdaLN:
             if (short_row) return short_rows;
+            if (sg.lanes) return segmented;
             if (whole && fits) return Choice{Kernel::kAdaLN, plan_wide(nvec), 0, 0};
             return gfits ? general : two_pass;
         case Op::kRopeRotateHalf: {
@@ -188,6 +221,7 @@ inline Choice choose(Op op, const Request& r, int E) {
                 const int P = d / (2 * E);
                 if ((P & (P - 1)) == 0 && P <= kWave / 2) {  // partner lanes within one wavefront
                     if (short_row) return short_rows;     // partner l ^ P inside the row's lanes
+                    if (sg.lanes && 2 * P <= sg.lanes) return segmented;
                     return Choice{Kernel::kRopeXor, plan_wide_xor(nvec), 0, 0};
                 }
             }
@@ -210,6 +244,7 @@ inline Choice choose(Op op, const Request& r, int E) {
         case Op::kRopeInterleaved: {
             if (whole && fits && r.head_dim % E == 0) {
                 if (short_row) return short_rows;
+                if (sg.lanes) return segmented;
                 // The wide split only where plan_for's 3 x 2 leaves a sixth
                 // or more of its slots idle: hidden 2304 (bf16, heads of
                 // 128) 68.8 -> 74.0 %, 2560 71.0 -> 74.0 %; from 384 vectors

@@ -294,7 +294,7 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE, 65790, 255, 258, ltx.BF16, "rmsnorm_long_kernel", None, None),
     # interleaved: one table slice per row when a head's vectors divide the lanes
     (ltx.OP_ROPE_INTERLEAVED, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 1, 4),
-    (ltx.OP_ROPE_INTERLEAVED, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 3),
+    (ltx.OP_ROPE_INTERLEAVED, 1728, 24, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 4),
     # ... the wide split only for 257..320 vectors
     (ltx.OP_ROPE_INTERLEAVED, 2304, 18, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 2, 3),
     (ltx.OP_ROPE_INTERLEAVED, 2520, 35, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 2, 3),
@@ -310,7 +310,24 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE, 256, 2, 128, ltx.BF16, "rmsnorm_short_kernel", 32, None),
     (ltx.OP_ROPE_INTERLEAVED, 128, 2, 64, ltx.BF16, "rmsnorm_short_kernel", 16, None),
     (ltx.OP_ROPE, 144, 2, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 1),   # not a power of two
-    (ltx.OP_RMSNORM, 264, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 1),                   # 33 vectors
+    # rows of 33..160 vectors in segments of 16 or 32 lanes with 3 or 5 vectors
+    # per lane where that fills more of a wavefront (wpr column: lanes, per:
+    # vectors per lane); rows near a multiple of 64 vectors keep one wavefront
+    (ltx.OP_RMSNORM, 264, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, 3),             # 33 vectors
+    (ltx.OP_RMSNORM, 320, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, 3),
+    (ltx.OP_ADALN, 576, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, 5),
+    (ltx.OP_RMSNORM, 704, 0, 0, ltx.F16, "rmsnorm_short_kernel", 32, 3),
+    (ltx.OP_ADALN, 1152, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 32, 5),
+    (ltx.OP_ADALN, 576, 0, 0, ltx.F32, "rmsnorm_short_kernel", 32, 5),               # 144 fp32 vectors
+    (ltx.OP_ROPE, 1152, 18, 64, ltx.BF16, "rmsnorm_short_kernel", 32, 5),
+    (ltx.OP_ROPE_INTERLEAVED, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_interleaved_kernel", 1, 3),  # no 32 x 5
+    (ltx.OP_RMSNORM, 1152, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 3),
+    (ltx.OP_ROPE_INTERLEAVED, 576, 8, 72, ltx.BF16, "rmsnorm_short_kernel", 16, 5),
+    (ltx.OP_ROPE, 640, 5, 128, ltx.BF16, "rmsnorm_short_kernel", 16, 5),
+    (ltx.OP_ROPE, 640, 2, 320, ltx.BF16, "rmsnorm_rope_pair_kernel", 1, 1),          # not a power of two
+    (ltx.OP_ROPE, 1280, 5, 256, ltx.BF16, "rmsnorm_short_kernel", 32, 5),            # partner 16 lanes away
+    (ltx.OP_RMSNORM, 1000, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 2),                  # 125 vectors
+    (ltx.OP_RMSNORM, 512, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 1),                   # 64 vectors
 ])
 def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
     name, f = _describe(op, hidden, heads, head_dim, dtype)
@@ -319,6 +336,7 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
         lanes = int(f["lanes_per_row"])
         assert lanes == wpr and int(f["rows_per_wavefront"]) == 64 // lanes
         assert int(f["rows_per_block"]) == 4 * (64 // lanes) and f["threads"] == "256"
+        assert int(f["vectors_per_lane"]) == (per or 1)
     elif wpr is not None:
         assert int(f["wavefronts_per_row"]) == wpr
         per_key = "pairs_per_lane" if "pair" in name else "vectors_per_lane"
@@ -396,13 +414,18 @@ def test_kernel_choice_always_covers_the_row():
             assert f["threads"] == "1024"
             continue
         if name == "rmsnorm_short_kernel":
-            lanes = int(f["lanes_per_row"])
-            assert whole and H // E <= 32 and lanes <= 32 and lanes & (lanes - 1) == 0
-            assert lanes >= H // E and (lanes == 1 or lanes // 2 < H // E)
+            lanes, per, n = int(f["lanes_per_row"]), int(f["vectors_per_lane"]), H // E
+            assert whole and lanes <= 32 and lanes & (lanes - 1) == 0
             assert int(f["rows_per_wavefront"]) * lanes == 64
+            if per == 1:    # short rows: the power of two at or above the row
+                assert n <= 32 and lanes >= n and (lanes == 1 or lanes // 2 < n)
+            else:           # segments: fewer slots than one wavefront per row
+                assert (lanes, per) in ((16, 3), (16, 5), (32, 3), (32, 5)), desc
+                assert (lanes, per) != (32, 5) or op in (ltx.OP_ADALN, ltx.OP_ROPE), desc
+                assert 32 < n <= lanes * per < 64 * -(-n // 64), desc
             if op == ltx.OP_ROPE:
                 P = d // (2 * E)
-                assert d % (2 * E) == 0 and P & (P - 1) == 0
+                assert d % (2 * E) == 0 and P & (P - 1) == 0 and 2 * P <= lanes
             if op == ltx.OP_ROPE_INTERLEAVED:
                 assert d % E == 0
             continue

@@ -261,6 +261,55 @@ def test_wide_split_shapes(dtype, op, hidden, head_dim, rows):
                    label=f"rope {dtype} {op} {rows}x{heads}x{head_dim}")
 
 
+# Rows of 33..160 vectors in segments of 16 or 32 lanes with 3 or 5 vectors
+# per lane (several rows per wavefront): every (lanes, vectors) shape for each
+# operation that takes it, in the three dtypes, with per-slot and shared
+# interleaved table slices and rotate-half partners up to 16 lanes away; row
+# counts leave the last workgroup's segments partly idle.
+SEGMENT_SHAPES = [
+    # dtype, op, hidden, head_dim, lanes, vectors per lane
+    ("bf16", "rms", 320, 0, 16, 3), ("f16", "adaln", 384, 0, 16, 3), ("bf16", "half", 320, 64, 16, 3),
+    ("bf16", "il", 360, 72, 16, 3), ("f32", "rms", 160, 0, 16, 3),
+    ("bf16", "adaln", 576, 0, 16, 5), ("f16", "half", 576, 64, 16, 5), ("bf16", "il", 576, 72, 16, 5),
+    ("f32", "rms", 288, 0, 16, 5), ("f32", "adaln", 320, 0, 16, 5), ("bf16", "rms", 520, 0, 16, 5),
+    ("f16", "rms", 704, 0, 32, 3), ("bf16", "adaln", 768, 0, 32, 3), ("bf16", "half", 704, 64, 32, 3),
+    ("bf16", "il", 720, 80, 32, 3), ("f32", "half", 352, 32, 32, 3), ("f32", "il", 384, 64, 32, 3),
+    ("bf16", "adaln", 1152, 0, 32, 5), ("f32", "adaln", 576, 0, 32, 5), ("bf16", "half", 1152, 64, 32, 5),
+    ("bf16", "half", 1280, 256, 32, 5), ("f16", "adaln", 1088, 0, 32, 5),
+]
+
+
+@pytest.mark.parametrize("dtype,op,hidden,head_dim,lanes,per", SEGMENT_SHAPES)
+@pytest.mark.parametrize("rows", [37, 1001])
+def test_segmented_rows(dtype, op, hidden, head_dim, lanes, per, rows):
+    code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+    opc = {"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "half": ltx.OP_ROPE,
+           "il": ltx.OP_ROPE_INTERLEAVED}[op]
+    heads = hidden // head_dim if head_dim else 0
+    desc = ltx.ltxnorm_describe_launch(opc, rows, hidden, heads, head_dim, code)
+    f = dict(kv.split("=") for kv in desc.split()[1:])
+    assert desc.startswith("rmsnorm_short_kernel ") and (int(f["lanes_per_row"]), int(f["vectors_per_lane"])) \
+        == (lanes, per), desc
+    announce(f"segmented {dtype} {op} rows={rows} hidden={hidden} d={head_dim}: {lanes} x {per}")
+    seed = hidden + rows + 41
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    if op == "rms":
+        check_rms(x, w, label=f"rms {dtype} {rows}x{hidden}")
+        check_rms(x, None, label=f"rms {dtype} {rows}x{hidden} no weight")
+    elif op == "adaln":
+        rps = 300
+        samples = -(-rows // rps)
+        sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.3, dtype=dtype)
+        sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.3, dtype=dtype)
+        check_adaln(x, w, sc, sh, rps, label=f"adaln {dtype} {rows}x{hidden}")
+        check_adaln(x, w, None, sh, rps, label=f"adaln {dtype} {rows}x{hidden} no scale")
+    else:
+        c, s = datagen.rope_tables(4096 if rows > 100 else 17, head_dim)
+        check_rope(x, w, c, s, heads, head_dim, interleaved=op == "il",
+                   label=f"rope {dtype} {op} {rows}x{heads}x{head_dim}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_lowp_invariants(dtype):
     """NULL weight = ones; position 0 = RMSNorm; null modulation = RMSNorm;
