@@ -187,6 +187,12 @@ ltxnorm_status launch_short(int lanes, int per, const KArgs& a, hipStream_t stre
         case 8 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 8, 1>; break;
         case 16 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 1>; break;
         case 32 * 8 + 1: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 1>; break;
+        case 1 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 1, 2>; break;
+        case 2 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 2, 2>; break;
+        case 4 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 4, 2>; break;
+        case 8 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 8, 2>; break;
+        case 16 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 2>; break;
+        case 32 * 8 + 2: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 2>; break;
         case 16 * 8 + 3: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 3>; break;
         case 16 * 8 + 5: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 16, 5>; break;
         case 32 * 8 + 3: fn = (const void*)&rmsnorm_short_kernel<IO, OP, 32, 3>; break;

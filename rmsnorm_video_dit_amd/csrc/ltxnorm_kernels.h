@@ -57,21 +57,25 @@ rmsnorm_kernel(const KArgs a) {
 // Rows in segments of S lanes (S a power of two up to 32), V vectors per
 // lane: lane l of a row's segment holds vectors k*S + l, 64 / S rows per
 // wavefront, four wavefronts per workgroup.
-//  * Short rows (at most 32 vectors: H <= 256 bf16/fp16 or 128 fp32, as in
-//    per-head normalisation) take V = 1 and S the power of two at or above
-//    the vector count: one wavefront per row would leave most lanes idle
-//    (H = 128 measured 28 % of peak that way).
-//  * Rows of 33..160 vectors whose count leaves many of a wavefront's lanes
-//    idle take S = 16 or 32 with V = 3 or 5 (40 vectors: 16 x 3; 72: 16 x 5;
-//    88: 32 x 3; 144: 32 x 5), filling 80-100 % of the slots where one
-//    wavefront per row fills 56-75 % (the choice and its measurements are
-//    with segments_for).
+//  * Rows of up to 64 vectors (per-head normalisation, small hidden sizes):
+//    one wavefront per row would leave most lanes idle (hidden 128 measured
+//    28 % of peak that way).  Rows of up to 8 vectors take V = 1 on the power
+//    of two at or above the vector count; rows of 9..64 take V = 2 on half
+//    as many lanes (16 x 3 for 33..48 vectors), which beat one vector per
+//    lane, while segments under 8 lanes (128 bytes of a row per load) lost.
+//    Rotate-half partners are lane l ^ P in the same slot (P <= S/2) or, with
+//    V = 2 and P == S, the other slot of the same lane.
+//  * Rows of 65..160 vectors whose count leaves many of a wavefront's lanes
+//    idle take S = 16 or 32 with V = 3 or 5 (72 vectors: 16 x 5; 88: 32 x 3;
+//    144: 32 x 5), filling 80-100 % of the slots where one wavefront per row
+//    fills 56-75 %.  The choice and its measurements are with segments_for.
 // A load instruction covers 64 / S rows' runs of S vectors.  The sum of
 // squares is reduced inside each segment by the first log2 S steps of the
 // wavefront reduction (and an xor-16 exchange for S = 32), so every lane of a
 // row ends with the same bits.  RMSNorm, AdaLN, and RoPE whose partners stay
-// inside a row's lanes: rotate-half with power-of-two half heads of P <= S/2
-// vectors (partner lane l ^ P in the same slot) and interleaved pairs.
+// inside a row's lanes: rotate-half with power-of-two half heads (partner
+// lane l ^ P in the same slot for P <= S/2, the lane's other slot for V = 2
+// and P == S) and interleaved pairs.
 // ---------------------------------------------------------------------------
 template <int S>
 __device__ __forceinline__ float segment_sum(float v) {
@@ -161,6 +165,35 @@ rmsnorm_short_kernel(const KArgs a) {
 
         const float part = sum_squares<IO, V>(xv);
         const float rstd = rstd_of(segment_sum<S>(part), a.hidden_f, a.eps);
+        if constexpr (OP == GOp::kRopeHalf && V == 2) {
+            if (a.vec_per_half >= S) {
+                // P == S: the partner of slot k is slot 1 - k of the same
+                // lane; slot 0 holds the first half.  Same expression as the
+                // exchange below, so the bits do not depend on the path.
+                float f0[E], f1[E], g[E];
+                keep_packed(xv[0]);
+                keep_packed(xv[1]);
+                IO::widen(xv[0], f0);
+                IO::widen(xv[1], f1);
+                keep_packed(wv[0]);
+                IO::widen(wv[0], g);
+#pragma unroll
+                for (int e = 0; e < E; ++e) f0[e] = (f0[e] * rstd) * g[e];
+                keep_packed(wv[1]);
+                IO::widen(wv[1], g);
+#pragma unroll
+                for (int e = 0; e < E; ++e) f1[e] = (f1[e] * rstd) * g[e];
+                float o0[E], o1[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    o0[e] = f0[e] * c[0][e] + f1[e] * (sn[0][e] * -1.0f);
+                    o1[e] = f1[e] * c[0][e] + f0[e] * (sn[0][e] * 1.0f);
+                }
+                if (rin && l < a.nvec) store_stream(yr + l, IO::narrow(o0));
+                if (rin && S + l < a.nvec) store_stream(yr + S + l, IO::narrow(o1));
+                continue;
+            }
+        }
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const int v = k * S + l;

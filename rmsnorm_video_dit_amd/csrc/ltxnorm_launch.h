@@ -152,25 +152,42 @@ inline int pow2_at_least(int64_t n) {
     return p;
 }
 
-// Rows of 33..160 vectors in segments of S lanes with V vectors per lane,
-// where that fills more of a wavefront than one row per wavefront with
-// ceil(n / 64) vectors per lane: (S, V) among (16, 3), (16, 5), (32, 3) and,
-// with `with_32x5`, (32, 5), the fewest slots that still cover the row.
-// {0, 0} when none does better (row lengths near a multiple of 64).  Against
-// one wavefront per row, bf16 at about 200 MB per launch: RMSNorm at hidden
-// 320 (16 x 3) 52-60 -> 76 %, 576 (16 x 5) 73-74 -> 75.5 %; AdaLN at 320
-// 47 -> 69 %, 576 59 -> 69.5 %, 704 (32 x 3) 65.5 -> 70 %, 1152 (32 x 5) 67.1
-// -> 68.7 %; rotate-half RoPE (heads of 64) at 576 55 -> 68.7 %, 1152 67.4 ->
-// 70.4 %; interleaved at 576 60 -> 67 %.  32 x 5 lost for interleaved RoPE
-// (1152: 68 -> 66 %) and RMSNorm (75.9 -> 75.5 %), which keep one wavefront.
+// Rows of at most 160 vectors in segments of S lanes (a power of two up to
+// 32) with V vectors per lane, 64 / S rows per wavefront; {0, 0} leaves the
+// row to one wavefront per row with ceil(n / 64) vectors per lane.
+//  * n <= 8: one vector per lane on the power of two at or above n (two
+//    vectors on half the lanes measured 47 % against 75 % at hidden 32, 61
+//    against 75 % at 64: a load then reads half of each 128-byte line).
+//  * 9 <= n <= 64: two vectors per lane on the power of two at or above n / 2
+//    lanes (16 x 3 for 33..48, which needs fewer slots).
+//    Against one vector per lane on the power of two at or above n, or one
+//    wavefront per row (bf16, about 200 MB per launch, % of 8 TB/s): hidden
+//    128 (8 x 2) RMSNorm 70-75 -> 76.7, AdaLN 65-68 -> 73.6, rotate-half
+//    64 -> 69, interleaved 63 -> 68; 256 (16 x 2) 74 -> 77, 66 -> 73.7, 64.5
+//    -> 70.3, 63.5 -> 72.2; 512 (32 x 2) 73 -> 76.6, 69 -> 73.1, 66 -> 70.5,
+//    70 -> 73.  Four vectors per lane measured lower at 16 and 32 vectors.
+//  * 65..160: 16 x 5, 32 x 3 or, with `with_32x5`, 32 x 5 where it covers
+//    the row in fewer slots than one wavefront per row (fewest slots wins):
+//    AdaLN at hidden 576 (16 x 5) 59 -> 69.5 %, 704 (32 x 3) 65.5 -> 70 %,
+//    1152 (32 x 5) 67.1 -> 68.7 %; rotate-half RoPE (heads of 64) at 576 55
+//    -> 68.7 %, 1152 67.4 -> 70.4 %; interleaved at 576 60 -> 67 %.  32 x 5
+//    lost for interleaved RoPE (1152: 68 -> 66 %) and RMSNorm (75.9 -> 75.5
+//    %), which keep one wavefront; so does every row of 97..128 vectors (one
+//    wavefront with 2 vectors per lane beat 32 x 4 by 1-5 points for the
+//    fused operations at hidden 1024).
 struct Segments {
     int lanes, per;
 };
 inline Segments segments_for(int64_t n, bool with_32x5) {
-    static constexpr Segments kShapes[] = {{16, 3}, {16, 5}, {32, 3}, {32, 5}};
+    if (n < 1 || n > 160) return Segments{0, 0};
+    if (n <= 8) return Segments{pow2_at_least(n), 1};
+    if (n <= 64) {
+        if (n > 32 && n <= 48) return Segments{16, 3};
+        return Segments{pow2_at_least((n + 1) / 2), 2};
+    }
+    static constexpr Segments kShapes[] = {{16, 5}, {32, 3}, {32, 5}};
     const int64_t one_wave = (int64_t)kWave * ((n + kWave - 1) / kWave);
     Segments best{0, 0};
-    if (n <= kMaxShortVectors || n > (int64_t)kWave * 4) return best;
     for (const Segments& c : kShapes) {
         if (c.lanes == 32 && c.per == 5 && !with_32x5) continue;
         const int64_t slots = (int64_t)c.lanes * c.per;
@@ -204,12 +221,10 @@ inline Choice choose(Op op, const Request& r, int E) {
     const Choice segmented{Kernel::kShort, Plan{1, sg.per, false}, 0, sg.lanes};
     switch (op) {
         case Op::kRmsNorm:
-            if (short_row) return short_rows;
             if (sg.lanes) return segmented;
             if (whole && fits) return Choice{Kernel::kRmsNorm, plan_for(nvec, 4, 2), 0, 0};
             return gfits ? general : two_pass;
         case Op::kAdaLN:
-            if (short_row) return short_rows;
             if (sg.lanes) return segmented;
             if (whole && fits) return Choice{Kernel::kAdaLN, plan_wide(nvec), 0, 0};
             return gfits ? general : two_pass;
@@ -220,8 +235,10 @@ inline Choice choose(Op op, const Request& r, int E) {
             if (whole && fits && even) {
                 const int P = d / (2 * E);
                 if ((P & (P - 1)) == 0 && P <= kWave / 2) {  // partner lanes within one wavefront
-                    if (short_row) return short_rows;     // partner l ^ P inside the row's lanes
-                    if (sg.lanes && 2 * P <= sg.lanes) return segmented;
+                    // partner l ^ P inside the row's lanes, or the lane's
+                    // other slot (two vectors per lane, P == lanes)
+                    if (sg.lanes && (2 * P <= sg.lanes || (sg.per == 2 && P == sg.lanes))) return segmented;
+                    if (short_row) return short_rows;     // one vector per lane
                     return Choice{Kernel::kRopeXor, plan_wide_xor(nvec), 0, 0};
                 }
             }
@@ -243,7 +260,6 @@ inline Choice choose(Op op, const Request& r, int E) {
         }
         case Op::kRopeInterleaved: {
             if (whole && fits && r.head_dim % E == 0) {
-                if (short_row) return short_rows;
                 if (sg.lanes) return segmented;
                 // The wide split only where plan_for's 3 x 2 leaves a sixth
                 // or more of its slots idle: hidden 2304 (bf16, heads of

@@ -301,14 +301,18 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE_INTERLEAVED, 3072, 24, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 3, 2),
     (ltx.OP_ROPE_INTERLEAVED, 70, 7, 10, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
     # short rows (at most 32 vectors): lanes per row given in the wpr column
-    (ltx.OP_RMSNORM, 128, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, None),
-    (ltx.OP_RMSNORM, 8, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 1, None),
-    (ltx.OP_RMSNORM, 96, 0, 0, ltx.F16, "rmsnorm_short_kernel", 16, None),
-    (ltx.OP_RMSNORM, 128, 0, 0, ltx.F32, "rmsnorm_short_kernel", 32, None),
-    (ltx.OP_ADALN, 256, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 32, None),
-    (ltx.OP_ROPE, 64, 1, 64, ltx.BF16, "rmsnorm_short_kernel", 8, None),
-    (ltx.OP_ROPE, 256, 2, 128, ltx.BF16, "rmsnorm_short_kernel", 32, None),
-    (ltx.OP_ROPE_INTERLEAVED, 128, 2, 64, ltx.BF16, "rmsnorm_short_kernel", 16, None),
+    # (two vectors per lane on half the lanes; per column: vectors per lane)
+    (ltx.OP_RMSNORM, 128, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 8, 2),
+    (ltx.OP_RMSNORM, 8, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 1, 1),
+    (ltx.OP_RMSNORM, 16, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 2, 1),
+    (ltx.OP_RMSNORM, 72, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 8, 2),
+    (ltx.OP_ROPE, 128, 1, 128, ltx.BF16, "rmsnorm_short_kernel", 8, 2),   # partner in the lane's other slot
+    (ltx.OP_RMSNORM, 96, 0, 0, ltx.F16, "rmsnorm_short_kernel", 8, 2),
+    (ltx.OP_RMSNORM, 128, 0, 0, ltx.F32, "rmsnorm_short_kernel", 16, 2),
+    (ltx.OP_ADALN, 256, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 16, 2),
+    (ltx.OP_ROPE, 64, 1, 64, ltx.BF16, "rmsnorm_short_kernel", 8, 1),    # partner 4 lanes away
+    (ltx.OP_ROPE, 256, 2, 128, ltx.BF16, "rmsnorm_short_kernel", 16, 2),
+    (ltx.OP_ROPE_INTERLEAVED, 128, 2, 64, ltx.BF16, "rmsnorm_short_kernel", 8, 2),
     (ltx.OP_ROPE, 144, 2, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 1),   # not a power of two
     # rows of 33..160 vectors in segments of 16 or 32 lanes with 3 or 5 vectors
     # per lane where that fills more of a wavefront (wpr column: lanes, per:
@@ -327,7 +331,8 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE, 640, 2, 320, ltx.BF16, "rmsnorm_rope_pair_kernel", 1, 1),          # not a power of two
     (ltx.OP_ROPE, 1280, 5, 256, ltx.BF16, "rmsnorm_short_kernel", 32, 5),            # partner 16 lanes away
     (ltx.OP_RMSNORM, 1000, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 2),                  # 125 vectors
-    (ltx.OP_RMSNORM, 512, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 1),                   # 64 vectors
+    (ltx.OP_RMSNORM, 512, 0, 0, ltx.BF16, "rmsnorm_short_kernel", 32, 2),             # 64 vectors
+    (ltx.OP_RMSNORM, 1024, 0, 0, ltx.BF16, "rmsnorm_kernel", 1, 2),                  # 128 vectors
 ])
 def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
     name, f = _describe(op, hidden, heads, head_dim, dtype)
@@ -417,15 +422,20 @@ def test_kernel_choice_always_covers_the_row():
             lanes, per, n = int(f["lanes_per_row"]), int(f["vectors_per_lane"]), H // E
             assert whole and lanes <= 32 and lanes & (lanes - 1) == 0
             assert int(f["rows_per_wavefront"]) * lanes == 64
-            if per == 1:    # short rows: the power of two at or above the row
-                assert n <= 32 and lanes >= n and (lanes == 1 or lanes // 2 < n)
+            if per == 1:    # one vector: rows of up to 8, or rotate-half partners too far
+                assert n <= 8 or (op == ltx.OP_ROPE and n <= 32), desc
+                assert lanes >= n and (lanes == 1 or lanes // 2 < n)
+            elif per == 2:  # 9..64 vectors: half the power of two at or above n
+                assert 9 <= n <= 64 and not 32 < n <= 48, desc
+                assert lanes == 1 << ((n - 1).bit_length() - 1), desc
             else:           # segments: fewer slots than one wavefront per row
                 assert (lanes, per) in ((16, 3), (16, 5), (32, 3), (32, 5)), desc
                 assert (lanes, per) != (32, 5) or op in (ltx.OP_ADALN, ltx.OP_ROPE), desc
                 assert 32 < n <= lanes * per < 64 * -(-n // 64), desc
             if op == ltx.OP_ROPE:
                 P = d // (2 * E)
-                assert d % (2 * E) == 0 and P & (P - 1) == 0 and 2 * P <= lanes
+                assert d % (2 * E) == 0 and P & (P - 1) == 0
+                assert 2 * P <= lanes or (per == 2 and P == lanes), desc
             if op == ltx.OP_ROPE_INTERLEAVED:
                 assert d % E == 0
             continue

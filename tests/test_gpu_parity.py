@@ -261,7 +261,7 @@ def test_wide_split_shapes(dtype, op, hidden, head_dim, rows):
                    label=f"rope {dtype} {op} {rows}x{heads}x{head_dim}")
 
 
-# Rows of 33..160 vectors in segments of 16 or 32 lanes with 3 or 5 vectors
+# Rows of up to 160 vectors in segments of 1-32 lanes with 1, 2, 3 or 5 vectors
 # per lane (several rows per wavefront): every (lanes, vectors) shape for each
 # operation that takes it, in the three dtypes, with per-slot and shared
 # interleaved table slices and rotate-half partners up to 16 lanes away; row
@@ -276,6 +276,17 @@ SEGMENT_SHAPES = [
     ("bf16", "il", 720, 80, 32, 3), ("f32", "half", 352, 32, 32, 3), ("f32", "il", 384, 64, 32, 3),
     ("bf16", "adaln", 1152, 0, 32, 5), ("f32", "adaln", 576, 0, 32, 5), ("bf16", "half", 1152, 64, 32, 5),
     ("bf16", "half", 1280, 256, 32, 5), ("f16", "adaln", 1088, 0, 32, 5),
+    # two vectors per lane on half the lanes (rows of up to 64 vectors)
+    ("bf16", "rms", 16, 0, 2, 1), ("bf16", "rms", 24, 0, 4, 1), ("bf16", "il", 32, 8, 4, 1),
+    ("bf16", "rms", 128, 0, 8, 2), ("bf16", "il", 128, 64, 8, 2), ("f16", "adaln", 256, 0, 16, 2),
+    ("bf16", "half", 256, 128, 16, 2), ("f32", "rms", 128, 0, 16, 2), ("bf16", "rms", 512, 0, 32, 2),
+    ("bf16", "adaln", 448, 0, 32, 2), ("f32", "half", 256, 64, 32, 2), ("f32", "adaln", 40, 0, 8, 2),
+    ("bf16", "rms", 72, 0, 8, 2),
+    # rotate-half partners in the lane's other slot (P == lanes, two vectors per lane)
+    ("bf16", "half", 128, 128, 8, 2), ("f16", "half", 256, 256, 16, 2), ("f32", "half", 128, 128, 16, 2),
+    ("bf16", "half", 512, 512, 32, 2),
+    # rows of up to 8 vectors: one vector per lane
+    ("bf16", "half", 64, 64, 8, 1),
 ]
 
 
