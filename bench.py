@@ -522,7 +522,7 @@ def main():
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
                 ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
                 ("rms_1x256x262144", "rmsnorm_long", "two-pass"),
-                ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, 4 per wavefront")):
+                ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, several per wavefront")):
             rc = datagen.GENERAL_CONFIGS[name]
             rw = Workload(rc, dev, stream)
             rsec = rw.time_steps(args.steps, args.warmup, graph)
