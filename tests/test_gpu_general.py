@@ -272,7 +272,8 @@ def test_rope_packed_invariants(head_dim):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("op,hidden,d", [("rms", 2048, 0), ("rms", 3076, 0), ("half", 2048, 64),
-                                         ("il", 2048, 64), ("half", 1152, 72), ("adaln", 2048, 0)])
+                                         ("il", 2048, 64), ("half", 1152, 72), ("adaln", 2048, 0),
+                                         ("rms", 128, 0), ("adaln", 576, 0), ("half", 1152, 64)])
 def test_offsets_past_2_31(op, hidden, d):
     """A tensor of more than 2^31 elements built on the device by repeating
     one seeded 4096-row block; the last rows (element offsets past 2^31) and
