@@ -298,10 +298,13 @@ int main() {
     check_rmsnorm(st, 129, 2048, 2);    // one wavefront per row
     check_rmsnorm(st, 50, 3076, 3);     // rows that start inside a vector
     check_rmsnorm(st, 3000, 96, 4);     // short rows, several per wavefront
+    check_rmsnorm(st, 1001, 320, 6);    // 16-lane segments, 3 vectors per lane
     check_rope(st, false, 64, 32, 64, 16);
     check_rope(st, true, 64, 32, 64, 16);
     check_rope(st, false, 20, 16, 72, 7);
+    check_rope(st, false, 333, 1, 128, 9);   // one head per row: the partner in the lane's other slot
     check_adaln(st, 10, 1024, 5);
+    check_adaln(st, 301, 1152, 100);    // 32-lane segments, 5 vectors per lane
     check_f32(st, 9, 1000);
     HIP_OK(hipStreamDestroy(st));
     std::printf(g_failures == 0 ? "ok\n" : "%d failures\n", g_failures);
