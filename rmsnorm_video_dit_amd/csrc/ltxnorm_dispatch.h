@@ -137,14 +137,25 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
     }
 }
 
+// One wavefront count W of 4..15: items per lane LO..HI, and ALSO (when
+// nonzero) as a single extra instance.
+template <typename LN, int W, int LO, int HI, int ALSO>
+ltxnorm_status by_per_also(const Plan& p, const KArgs& a, size_t lds_per_row, hipStream_t s) {
+    if constexpr (ALSO > 0) {
+        if (p.per == ALSO) return by_per<LN, W, ALSO, ALSO>(p, a, lds_per_row, s);
+    }
+    return by_per<LN, W, LO, HI>(p, a, lds_per_row, s);
+}
+
 // Plans that plan_for can produce: one wavefront with 1..ONE items per lane;
 // 3..15 wavefronts with exactly SPREAD items per lane (2 wavefronts never
 // occur: a row too long for one wavefront needs more than 2 * ONE / SPREAD);
 // 16 wavefronts with SPREAD..MAXP items per lane.  WIDE adds plan_wide's
 // plans: two or three wavefronts with 3..4 items per lane; PER4 > SPREAD
-// adds four wavefronts with SPREAD..PER4 (plan_wide_xor).  lds_per_row:
-// dynamic LDS bytes per row slot of the block.
-template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false, int PER4 = SPREAD>
+// adds four wavefronts with SPREAD..PER4 (plan_wide_xor); ALSO4 adds
+// ALSO4 items per lane at 4..15 wavefronts (plan_wide_xor past 768
+// vectors).  lds_per_row: dynamic LDS bytes per row slot of the block.
+template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false, int PER4 = SPREAD, int ALSO4 = 0>
 ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_per_row = 0) {
     switch (p.wpr) {
         case 1: return by_per<LN, 1, 1, ONE>(p, a, lds_per_row, s);
@@ -154,18 +165,18 @@ ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_
         case 3:
             if constexpr (WIDE) return by_per<LN, 3, SPREAD, 4>(p, a, lds_per_row, s);
             return by_per<LN, 3, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 4: return by_per<LN, 4, SPREAD, PER4>(p, a, lds_per_row, s);
-        case 5: return by_per<LN, 5, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 6: return by_per<LN, 6, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 7: return by_per<LN, 7, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 8: return by_per<LN, 8, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 9: return by_per<LN, 9, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 10: return by_per<LN, 10, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 11: return by_per<LN, 11, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 12: return by_per<LN, 12, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 13: return by_per<LN, 13, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 14: return by_per<LN, 14, SPREAD, SPREAD>(p, a, lds_per_row, s);
-        case 15: return by_per<LN, 15, SPREAD, SPREAD>(p, a, lds_per_row, s);
+        case 4: return by_per_also<LN, 4, SPREAD, PER4, (ALSO4 > PER4 ? ALSO4 : 0)>(p, a, lds_per_row, s);
+        case 5: return by_per_also<LN, 5, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 6: return by_per_also<LN, 6, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 7: return by_per_also<LN, 7, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 8: return by_per_also<LN, 8, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 9: return by_per_also<LN, 9, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 10: return by_per_also<LN, 10, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 11: return by_per_also<LN, 11, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 12: return by_per_also<LN, 12, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 13: return by_per_also<LN, 13, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 14: return by_per_also<LN, 14, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
+        case 15: return by_per_also<LN, 15, SPREAD, SPREAD, ALSO4>(p, a, lds_per_row, s);
         case 16: return by_per<LN, 16, SPREAD, MAXP>(p, a, lds_per_row, s);
         default: return LTXNORM_ERR_UNSUPPORTED;
     }
@@ -224,7 +235,7 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
         case Kernel::kNone: return LTXNORM_OK;
         case Kernel::kRmsNorm: return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
-        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3>(c.plan, a, stream);
+        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3, 4>(c.plan, a, stream);
         case Kernel::kRopePacked:
             return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kRopePackedOdd:

@@ -103,12 +103,16 @@ inline Plan plan_wide(int64_t items) {
     return plan_for(items, 4, 4);
 }
 
-// Rotate-half RoPE takes plan_wide's split up to 512 vectors and 3 vectors
-// per lane over three or four wavefronts for 513..768 (hidden 5120, heads
-// of 128: 71.9 -> 73.2 %; 6144: 72.0 -> 73.8 %).  Up to 512 vectors that
-// split would be 3 x 3, which measured 2-3 points below plan_wide's.
+// Rotate-half RoPE takes plan_wide's split up to 512 vectors, 3 vectors per
+// lane over three or four wavefronts for 513..768 (hidden 5120, heads of
+// 128: 71.9 -> 73.2 %; 6144: 72.0 -> 73.8 %; up to 512 vectors that split
+// would be 3 x 3, which measured 2-3 points below plan_wide's), and 4 vectors
+// per lane past 768 (against plan_for's 2, heads of 128: hidden 6656 68.3 ->
+// 71.8 %, 8192 70.3 -> 71.7 %, 12288 66.2 -> 69.8 %, 16384 65.3 -> 68.8 %;
+// at 24576 the two tie, and past 4096 vectors both are 16 wavefronts).
 inline Plan plan_wide_xor(int64_t items) {
-    if (items < kWideMin || items > kWideMax) return plan_for(items, 4, 2);
+    if (items < kWideMin) return plan_for(items, 4, 2);
+    if (items > kWideMax) return plan_for(items, 4, 4);
     if (items <= (int64_t)kWave * 4 * 2) return plan_wide(items);
     return plan_for(items, 4, 3);
 }

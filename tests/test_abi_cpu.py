@@ -283,7 +283,10 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE, 4608, 36, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 3, 3),
     (ltx.OP_ROPE, 5120, 40, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 4, 3),
     (ltx.OP_ROPE, 6144, 48, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 4, 3),
-    (ltx.OP_ROPE, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 8, 2),
+    (ltx.OP_ROPE, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 4, 4),      # 4 vectors past 768
+    (ltx.OP_ROPE, 16384, 128, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 8, 4),
+    (ltx.OP_ROPE, 65536, 512, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 16, 8),
+    (ltx.OP_ROPE_INTERLEAVED, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 8, 2),
     (ltx.OP_ROPE, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 3),
     (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 3, 2),
     (ltx.OP_ROPE, 960, 24, 40, ltx.F32, "rmsnorm_rope_packed_kernel", 1, 4),
@@ -449,6 +452,8 @@ def test_kernel_choice_always_covers_the_row():
             assert (wpr, per) == (4, 3) if four else (wpr in (2, 3) and 3 <= per <= 4), desc
         else:
             assert wpr != 2, desc
+        if name == "rmsnorm_rope_xor_kernel" and touched > 768:  # 4 vectors per lane
+            assert int(f["vectors_per_lane"]) == 4 or wpr == 16, desc
         assert rpb == (4 if wpr == 1 else 2 if wpr <= 3 else 1)
         if name == "rmsnorm_rope_pair_kernel":
             per = int(f["pairs_per_lane"])
