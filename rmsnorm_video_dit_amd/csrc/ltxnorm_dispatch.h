@@ -237,9 +237,9 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
         case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3, 4>(c.plan, a, stream);
         case Kernel::kRopePacked:
-            return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+            return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopePackedOdd:
-            if constexpr (E == 8) return by_plan<RopePackedL<IO, true>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+            if constexpr (E == 8) return by_plan<RopePackedL<IO, true>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
             return LTXNORM_ERR_UNSUPPORTED;  // not chosen for 4-element vectors
         case Kernel::kRopePair:
             return by_plan<RopePairL<IO>, 2, 1, kMaxVecPerLane / 2>(c.plan, a, stream);

@@ -248,9 +248,13 @@ inline Choice choose(Op op, const Request& r, int E) {
             }
             const int vph = d / E;
             if (whole && fits && (even || odd) && vph <= kWave / 2) {
-                // heads packed into wavefronts (lw of 64 lanes used)
+                // heads packed into wavefronts (lw of 64 lanes used); the
+                // wide split for 257..768 lane slots' worth of vectors, as
+                // for the other fused kernels (bf16, about 200 MB per launch:
+                // 32 x 72 57 -> 70.6 %, 40 x 72 65 -> 72 %, 32 x 80 61 -> 71 %,
+                // 32 x 96 66.5 -> 71 %)
                 const int lw = kWave - kWave % vph;
-                Plan p = plan_for((nvec * kWave + lw - 1) / lw, 4, 2);
+                Plan p = plan_wide((nvec * kWave + lw - 1) / lw);
                 p.per = (int)((nvec + (int64_t)lw * p.wpr - 1) / ((int64_t)lw * p.wpr));
                 p.full = false;
                 if (p.per <= kMaxVecPerLane)

@@ -288,7 +288,9 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_ROPE, 65536, 512, 128, ltx.BF16, "rmsnorm_rope_xor_kernel", 16, 8),
     (ltx.OP_ROPE_INTERLEAVED, 8192, 64, 128, ltx.BF16, "rmsnorm_rope_interleaved_kernel(shared)", 8, 2),
     (ltx.OP_ROPE, 1152, 16, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 1, 3),
-    (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 3, 2),
+    (ltx.OP_ROPE, 2560, 32, 80, ltx.BF16, "rmsnorm_rope_packed_kernel", 2, 3),
+    (ltx.OP_ROPE, 3072, 32, 96, ltx.BF16, "rmsnorm_rope_packed_kernel", 2, 4),
+    (ltx.OP_ROPE, 2304, 32, 72, ltx.BF16, "rmsnorm_rope_packed_kernel(odd)", 2, 3),
     (ltx.OP_ROPE, 960, 24, 40, ltx.F32, "rmsnorm_rope_packed_kernel", 1, 4),
     (ltx.OP_ROPE, 3072, 3, 1024, ltx.BF16, "rmsnorm_rope_pair_kernel", 3, 1),
     (ltx.OP_ROPE, 1040, 20, 52, ltx.BF16, "rmsnorm_general_kernel", 1, 3),
@@ -445,6 +447,7 @@ def test_kernel_choice_always_covers_the_row():
         wpr, rpb, threads = int(f["wavefronts_per_row"]), int(f["rows_per_block"]), int(f["threads"])
         assert 1 <= wpr <= 16 and threads == 64 * wpr * rpb <= 1024
         wide = (name in ("rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel") and 256 < touched <= 768) or \
+            (name.startswith("rmsnorm_rope_packed_kernel") and 256 < -(-touched * 64 // (64 - 64 % (d // E))) <= 768) or \
             (name.startswith("rmsnorm_rope_interleaved_kernel") and 256 < touched <= 320)
         if wide:  # two or three wavefronts with 3-4 vectors per lane, or four with 3
             per = int(f["vectors_per_lane"])

@@ -235,6 +235,9 @@ WIDE_SHAPES = [
     # rotate-half past 768 vectors: 4 vectors per lane over 4..15 wavefronts
     ("bf16", "half", 6656, 128), ("f16", "half", 8192, 128), ("bf16", "half", 10240, 128),
     ("f32", "half", 4224, 128), ("bf16", "half", 13312, 64),
+    # head-packed rotate-half (heads not a power of two): the wide split too
+    ("bf16", "half", 2304, 72), ("bf16", "half", 2880, 72), ("bf16", "half", 2560, 80),
+    ("f16", "half", 3072, 96), ("f32", "half", 2560, 40),
 ]
 
 
