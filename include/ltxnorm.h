@@ -221,10 +221,13 @@ typedef enum ltxnorm_op {
  * buf, truncated to len bytes, for example
  *     "rmsnorm_kernel wavefronts_per_row=3 vectors_per_lane=2 rows_per_block=2
  *      threads=384 lds_bytes=0"
- * (the kernel names are those a profiler shows).  The general kernel's line
- * ends in "grid=resident": its grid is capped at the number of workgroups
- * the device holds at once, each workgroup looping over rows; every other
- * kernel takes one workgroup per group of rows.  heads and head_dim are
+ * (the kernel names are those a profiler shows).  Rows of up to 160
+ * vectors may share wavefronts instead, in segments of a few lanes:
+ *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2
+ *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
+ * The general kernel's line ends in "grid=resident": its grid is capped at
+ * the number of workgroups the device holds at once, each workgroup looping
+ * over rows; every other kernel takes one workgroup per group of rows.  heads and head_dim are
  * read for the RoPE operations only.  LTXNORM_OP_ADALN describes a call
  * with modulation rows (one with neither runs LTXNORM_OP_RMSNORM's kernel).
  *
