@@ -327,6 +327,40 @@ def test_segmented_rows(dtype, op, hidden, head_dim, lanes, per, rows):
                    label=f"rope {dtype} {op} {rows}x{heads}x{head_dim}")
 
 
+# Both sides of every boundary of the row-split rules (vectors per row):
+# one vector per lane up to 8, two from 9, 16 x 3 for 33..48, 32 x 2 from 49,
+# 16 x 5 / 32 x 3 / 32 x 5 segments to 160, one wavefront to 256, the wide
+# split to 768 (rotate-half: 3 vectors from 513, 4 wavefronts from 577, 4
+# vectors past 768; interleaved: to 320).  Interleaved pairs use heads of 8
+# so odd vector counts occur; rotate-half uses heads of 16 (even counts).
+BOUNDARY_VECTORS = [8, 9, 32, 33, 48, 49, 64, 65, 80, 81, 96, 97, 128, 129, 160, 161,
+                    256, 257, 320, 321, 512, 513, 576, 577, 768, 769]
+
+
+@pytest.mark.parametrize("n", BOUNDARY_VECTORS)
+@pytest.mark.parametrize("op", ["rms", "adaln", "il", "half"])
+def test_split_rule_boundaries(op, n):
+    if op == "half" and n % 2:
+        n += 1
+    hidden = 8 * n
+    rows = 37
+    announce(f"split boundary {op} vectors={n}: "
+             f"{ltx.ltxnorm_describe_launch({'rms': ltx.OP_RMSNORM, 'adaln': ltx.OP_ADALN, 'il': ltx.OP_ROPE_INTERLEAVED, 'half': ltx.OP_ROPE}[op], rows, hidden, hidden // 8 if op == 'il' else hidden // 16 if op == 'half' else 0, 8 if op == 'il' else 16 if op == 'half' else 0)}")
+    seed = 1000 + n
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1)
+    w = datagen.make_w(hidden, seed=seed, stream=2)
+    if op == "rms":
+        check_rms(x, w, label=f"rms boundary {n}")
+    elif op == "adaln":
+        sc = datagen.make_x(2, hidden, seed=seed, stream=4, sigma=0.3)
+        sh = datagen.make_x(2, hidden, seed=seed, stream=5, sigma=0.3)
+        check_adaln(x, w, sc, sh, 20, label=f"adaln boundary {n}")
+    else:
+        d = 8 if op == "il" else 16
+        c, s = datagen.rope_tables(29, d)
+        check_rope(x, w, c, s, hidden // d, d, interleaved=op == "il", label=f"rope {op} boundary {n}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_lowp_invariants(dtype):
     """NULL weight = ones; position 0 = RMSNorm; null modulation = RMSNorm;
