@@ -137,9 +137,11 @@ enum class Kernel {
     kLong,                   // rmsnorm_long_kernel (two passes)
 };
 
-// Short rows: lanes per row is the power of two at or above the row's
-// vectors (one vector per lane), 64 / lanes rows per wavefront, four
-// wavefronts per workgroup.
+// Rows of at most kMaxShortVectors vectors can always take one vector per
+// lane on the power of two at or above their vector count (64 / lanes rows
+// per wavefront): the layout rotate-half falls back to when two vectors per
+// lane would put a vector's partner outside the row's segment.  Segmented
+// rows take four wavefronts per workgroup.
 constexpr int kMaxShortVectors = 32;
 constexpr int kShortWavesPerBlock = 4;
 
