@@ -344,8 +344,11 @@ def test_split_rule_boundaries(op, n):
         n += 1
     hidden = 8 * n
     rows = 37
-    announce(f"split boundary {op} vectors={n}: "
-             f"{ltx.ltxnorm_describe_launch({'rms': ltx.OP_RMSNORM, 'adaln': ltx.OP_ADALN, 'il': ltx.OP_ROPE_INTERLEAVED, 'half': ltx.OP_ROPE}[op], rows, hidden, hidden // 8 if op == 'il' else hidden // 16 if op == 'half' else 0, 8 if op == 'il' else 16 if op == 'half' else 0)}")
+    d = {"il": 8, "half": 16}.get(op, 0)
+    opc = {"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "il": ltx.OP_ROPE_INTERLEAVED,
+           "half": ltx.OP_ROPE}[op]
+    desc = ltx.ltxnorm_describe_launch(opc, rows, hidden, hidden // d if d else 0, d)
+    announce(f"split boundary {op} vectors={n}: {desc}")
     seed = 1000 + n
     x = datagen.make_x(rows, hidden, seed=seed, stream=1)
     w = datagen.make_w(hidden, seed=seed, stream=2)
@@ -356,7 +359,6 @@ def test_split_rule_boundaries(op, n):
         sh = datagen.make_x(2, hidden, seed=seed, stream=5, sigma=0.3)
         check_adaln(x, w, sc, sh, 20, label=f"adaln boundary {n}")
     else:
-        d = 8 if op == "il" else 16
         c, s = datagen.rope_tables(29, d)
         check_rope(x, w, c, s, hidden // d, d, interleaved=op == "il", label=f"rope {op} boundary {n}")
 
