@@ -75,6 +75,7 @@ PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datag
           "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
           "rms_odd": "rms_4x4096x3076", "rope_d72": "rope_2x4096x1152_h16d72",
           "rms_long": "rms_1x256x262144", "rms_short": "rms_2x4096x24_d128",
+          "adaln_seg": "adaln_8x4096x1152",
           "rope_large": "rope_4x4096x3072_h24d128", "ropei_large": "ropei_4x4096x3072_h24d128",
           "adaln_large": "adaln_4x4096x3072"}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
@@ -522,7 +523,8 @@ def main():
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
                 ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
                 ("rms_1x256x262144", "rmsnorm_long", "two-pass"),
-                ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, several per wavefront")):
+                ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, several per wavefront"),
+                ("adaln_8x4096x1152", "rmsnorm_adaln_seg", "segmented rows, several per wavefront")):
             rc = datagen.GENERAL_CONFIGS[name]
             rw = Workload(rc, dev, stream)
             rsec = rw.time_steps(args.steps, args.warmup, graph)

@@ -222,8 +222,8 @@ CONFIGS = {
 # Shapes outside the pages' set that exercise the kernels for rows of any
 # length, with the same value recipe: a hidden size that is not a whole number
 # of 16-byte vectors, a head size the vector kernels cannot pair (16 heads x
-# 72, rotate-half), rows longer than the register budget, and rows of one
-# head (per-head normalisation).
+# 72, rotate-half), rows longer than the register budget, rows of one head
+# (per-head normalisation), and AdaLN rows of 144 vectors.
 GENERAL_CONFIGS = {
     "rms_4x4096x3076": Config("rms_4x4096x3076", 9, 4, 4096, 3076),
     "rope_2x4096x1152_h16d72": Config("rope_2x4096x1152_h16d72", 10, 2, 4096, 1152,
@@ -232,6 +232,9 @@ GENERAL_CONFIGS = {
     # per-head normalisation (query/key norm): rows of one 128-element head,
     # [2 x 4096 x 24 heads] of them
     "rms_2x4096x24_d128": Config("rms_2x4096x24_d128", 12, 2, 4096 * 24, 128),
+    # AdaLN at hidden 1152 (the PixArt size), rows of 144 vectors that
+    # several rows share a wavefront for
+    "adaln_8x4096x1152": Config("adaln_8x4096x1152", 16, 8, 4096, 1152, adaln_sigma=0.25),
 }
 # The fused operations at the headline's size ([4 x 4096 x 3072]), large
 # enough that the launch floor no longer sets their rate: RoPE with 24 heads
