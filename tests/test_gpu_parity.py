@@ -363,6 +363,53 @@ def test_split_rule_boundaries(op, n):
         check_rope(x, w, c, s, hidden // d, d, interleaved=op == "il", label=f"rope {op} boundary {n}")
 
 
+def _random_shapes(count, seed):
+    """Seeded shapes of every operation and dtype: hidden sizes from 1 to
+    about 20000 (whole vectors or not), even head sizes from 2 to 1200,
+    1..40 rows; at most 2^21 elements each."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < count:
+        dtype = str(rng.choice(["bf16", "f16", "f32"]))
+        op = str(rng.choice(["rms", "adaln", "half", "il"]))
+        rows = int(rng.integers(1, 41))
+        if op in ("half", "il"):
+            d = 2 * int(rng.choice([rng.integers(1, 40), rng.integers(1, 600), 32, 36, 64]))
+            heads = int(rng.integers(1, max(2, 20000 // d)))
+            hidden = heads * d
+        else:
+            d = heads = 0
+            hidden = int(rng.choice([rng.integers(1, 2000), rng.integers(1, 20000),
+                                     8 * rng.integers(1, 2500)]))
+        if rows * hidden <= (1 << 21):
+            shapes.append((dtype, op, rows, hidden, heads, d))
+    return shapes
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_random_shapes(case):
+    """Every (kernel, row split) the dispatch can reach has a compiled
+    instance: seeded random shapes of every operation and dtype, each
+    checked element by element against the oracle."""
+    for dtype, op, rows, hidden, heads, d in _random_shapes(60, 20261203 + case):
+        announce(f"random {dtype} {op} rows={rows} hidden={hidden} heads={heads} d={d}")
+        seed = rows * 7919 + hidden
+        x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+        w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+        if op == "rms":
+            check_rms(x, w, label=f"random rms {dtype} {rows}x{hidden}")
+        elif op == "adaln":
+            rps = max(1, rows // 3)
+            samples = -(-rows // rps)
+            sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.3, dtype=dtype)
+            sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.3, dtype=dtype)
+            check_adaln(x, w, sc, sh, rps, label=f"random adaln {dtype} {rows}x{hidden}")
+        else:
+            c, s = datagen.rope_tables(23, d)
+            check_rope(x, w, c, s, heads, d, interleaved=op == "il",
+                       label=f"random rope {op} {dtype} {rows}x{heads}x{d}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_lowp_invariants(dtype):
     """NULL weight = ones; position 0 = RMSNorm; null modulation = RMSNorm;
