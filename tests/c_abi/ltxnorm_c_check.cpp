@@ -38,7 +38,7 @@ void oracle_round_dt(const double* y, int64_t n, float* ref32, void* ref_out, in
 
 namespace {
 
-constexpr int kOracleBf16 = 0, kOracleF32 = 2;
+constexpr int kOracleBf16 = 0, kOracleF16 = 1, kOracleF32 = 2;
 int g_failures = 0;
 
 #define HIP_OK(call)                                                                  \
@@ -260,6 +260,55 @@ void check_f32(hipStream_t st, int64_t rows, int64_t hidden) {
     expect(s == LTXNORM_OK && bad == 0, label);
 }
 
+// fp16 through the _dt entry point: within one fp16 ulp of the oracle's
+// rounded result (values encoded with the host's IEEE half conversion).
+double from_f16(uint16_t b) {
+    _Float16 h;
+    std::memcpy(&h, &b, 2);
+    return (double)h;
+}
+
+double ulp_f16(double v) {
+    const double a = std::fabs(v);
+    if (a < std::ldexp(1.0, -14)) return std::ldexp(1.0, -24);
+    int e;
+    std::frexp(a, &e);
+    return std::ldexp(1.0, e - 11);
+}
+
+void check_f16(hipStream_t st, int64_t rows, int64_t hidden) {
+    Rng r{77};
+    std::vector<uint16_t> x(rows * hidden), w(hidden);
+    for (auto& e : x) {
+        const _Float16 h = (_Float16)r.normal();
+        std::memcpy(&e, &h, 2);
+    }
+    for (auto& e : w) {
+        const _Float16 h = (_Float16)(1.0 + 0.25 * r.normal());
+        std::memcpy(&e, &h, 2);
+    }
+    Dev dx(x.size() * 2), dy(x.size() * 2), dw(w.size() * 2);
+    upload(dx.p, x);
+    upload(dw.p, w);
+    const ltxnorm_status s =
+        ltxnorm_rmsnorm_fwd_dt(dy.p, dx.p, dw.p, rows, hidden, 1e-6f, LTXNORM_F16, st);
+    HIP_OK(hipStreamSynchronize(st));
+    std::vector<double> y(x.size());
+    oracle_rmsnorm_dt(y.data(), x.data(), w.data(), rows, hidden, 1e-6f, kOracleF16);
+    std::vector<uint16_t> ref(x.size());
+    oracle_round_dt(y.data(), (int64_t)y.size(), nullptr, ref.data(), kOracleF16);
+    const auto got = download<uint16_t>(dy.p, x.size());
+    int64_t bad = 0;
+    for (size_t i = 0; i < got.size(); ++i) {
+        const double g = from_f16(got[i]), f = from_f16(ref[i]);
+        if (!(std::fabs(g - f) <= ulp_f16(f))) ++bad;
+    }
+    char label[96];
+    std::snprintf(label, sizeof label, "rmsnorm fp16 %lldx%lld (%lld beyond one ulp)",
+                  (long long)rows, (long long)hidden, (long long)bad);
+    expect(s == LTXNORM_OK && bad == 0, label);
+}
+
 void check_statuses(hipStream_t st) {
     Dev a(1 << 20);
     char* base = static_cast<char*>(a.p);
@@ -306,6 +355,8 @@ int main() {
     check_adaln(st, 10, 1024, 5);
     check_adaln(st, 301, 1152, 100);    // 32-lane segments, 5 vectors per lane
     check_f32(st, 9, 1000);
+    check_f16(st, 37, 3072);            // three wavefronts per row
+    check_f16(st, 1001, 320);           // 16-lane segments
     HIP_OK(hipStreamDestroy(st));
     std::printf(g_failures == 0 ? "ok\n" : "%d failures\n", g_failures);
     return g_failures == 0 ? 0 : 1;
