@@ -109,9 +109,11 @@ rmsnorm_short_kernel(const KArgs a) {
         wv[k] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
     }
 
-    // rotation constants of this lane (the xor layout of the power-of-two
-    // kernel, within the row's lanes: the same for every slot, since S is a
-    // multiple of 2P; or the interleaved table columns of each slot)
+    // rotation constants of this lane: the xor layout of the power-of-two
+    // kernel within the row's lanes, whose table slice (v mod P) is the same
+    // for every slot, whether S is a multiple of 2P or P == S (then src and
+    // sgn go unused: the partner is the lane's other slot); or the
+    // interleaved table columns of each slot
     int src = 0, toff[V];
     float sgn = 1.0f;
 #pragma unroll
