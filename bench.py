@@ -1,42 +1,55 @@
 """Benchmark: effective HBM bandwidth of RMSNorm bf16 at [4 x 4096 x 3072] on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--windows N]
 
 One step is one launch of the RMSNorm path (load, square-accumulate, reduce,
 scale, round, store) over the whole [4 x 4096 x 3072] bf16 batch.  Inputs are
 seeded synthetic tensors (x ~ N(0,1), weight ~ U(0.5,1.5)), resident in HBM
 before timing starts.  Consecutive steps cycle through enough copies of the
 input and output buffers (>= 1 GiB in total) that the 256 MB memory-side
-Infinity Cache cannot serve a step from the previous one.  Timing uses HIP
-events recorded on the stream the kernels are launched on.  The K timed
-launches are issued one by one on the stream; `--launch graph` captures them
-into one HIP graph and replays it once instead (the library only enqueues
-kernels, so the launches capture as they are).  The line reports the
-headline in the other mode too ("graph_launch" / "stream_launch"); at these
-sizes the two agree, since the host-side cost of issuing a launch is hidden
-behind the previous kernel.
+Infinity Cache cannot serve a step from the previous one.
+
+Timing: after W warm-up launches, N windows (default 5) of exactly K launches
+each are timed with HIP events recorded on the stream the kernels are
+launched on.  Before each window the stream is held behind a short spin
+kernel while the host enqueues the window's K launches, so a window measures
+K back-to-back kernels and not the host's latency in issuing the first one;
+each window is bracketed by device synchronisation.  value and ms_per_step
+come from the median window, with the fastest and slowest beside them.  The
+K launches are issued one by one on the stream; `--launch graph` captures
+them into one HIP graph and replays it once per window instead (the library
+only enqueues kernels, so the launches capture as they are).  The line
+reports the headline in the other mode too ("graph_launch" /
+"stream_launch").
 
 value = algorithmic bytes per step (read x + write y + read weight once,
 201,332,736 B) / seconds per step, in GB/s (10^9 B/s); it is compared with
-MI355X's 8 TB/s HBM peak in the "roofline" object.  The same line reports
-the fused RMSNorm+RoPE workload ([2 x 4096 x 2048], 32 heads x 64, fp32
-cos/sin tables) under "rope" (rotate-half pairs) and "rope_interleaved"
-(adjacent pairs), the AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample
-scale/shift) under "adaln", the other four shapes of the pages' RMSNorm
-micro-benchmark under "pages_shapes" (with the page's H100 ms as context),
-the headline RMSNorm with fp16 and fp32 I/O under "rms_f16" / "rms_f32" (and
-the RoPE / AdaLN workloads in fp16 or fp32 under "rope_f16", "rope_f32",
-"adaln_f32"), RoPE (24 heads x 128, both pairings) and AdaLN at the
-headline's size under "rope_large", "rope_interleaved_large" and
-"adaln_large", four shapes outside the pages' set under "general" (hidden 3076, not a whole number of 16-byte vectors; 16 heads x 72 with
-rotate-half pairs; rows of 262144, beyond the register budget; per-head rows
-of 128), and the CPU oracle timed on this host under "cpu_baseline".  The
-same CPU leg compares every timed workload's output, element by element over
-the whole batch, with the oracle's result ("parity").  Prints one JSON line.
+MI355X's 8 TB/s HBM peak in the "roofline" object, and with copy kernels
+moving the same buffers, timed the same way in the same run (ceiling/copy.hip:
+plain and non-temporal 16-byte copies, non-temporal read-only and write-only
+streams, and the runtime's device copy), under "copy_ceiling" and
+"pct_of_copy_ceiling".  The same line reports the fused RMSNorm+RoPE
+workload ([2 x 4096 x 2048], 32 heads x 64, fp32 cos/sin tables) under
+"rope" (rotate-half pairs) and "rope_interleaved" (adjacent pairs), the
+AdaLN-modulated RMSNorm ([2 x 4096 x 2048], per-sample scale/shift) under
+"adaln", the other four shapes of the pages' RMSNorm micro-benchmark under
+"pages_shapes" (with the page's H100 ms as context), the headline RMSNorm with
+fp16 and fp32 I/O under "rms_f16" / "rms_f32" (and the RoPE / AdaLN workloads
+in fp16 or fp32 under "rope_f16", "rope_f32", "adaln_f32"), RoPE (24 heads x
+128, both pairings) and AdaLN at the headline's size under "rope_large",
+"rope_interleaved_large" and "adaln_large", five shapes outside the pages'
+set under "general" (hidden 3076, not a whole number of 16-byte vectors; 16
+heads x 72 with rotate-half pairs; rows of 262144, beyond the register
+budget; per-head rows of 128; AdaLN at hidden 1152), and the CPU oracle timed
+on this host under "cpu_baseline".  The same CPU leg compares every timed
+workload's output, element by element over the whole batch, with the
+oracle's result ("parity").  Prints one JSON line.
 
---probe rms|rms_f16|rms_f32|rope|ropei|adaln|rms_odd|rope_d72|rms_long|rms_short|rope_large|
-ropei_large|adaln_large|copy
-runs a few launches only, for rocprofv3 counter passes.
+--probe NAME (a short name below, or any workload of the pages' table, e.g.
+rms_1x1024x2048) runs --launches launches of one workload with the same
+rotating buffers and nothing else, for rocprofv3 kernel traces and counter
+passes; --probe copy runs the runtime's device copy of the headline's bytes
+(the counters' calibration), --probe copy_nt the non-temporal copy kernel.
 """
 from __future__ import annotations
 
@@ -79,6 +92,7 @@ PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datag
           "rope_large": "rope_4x4096x3072_h24d128", "ropei_large": "ropei_4x4096x3072_h24d128",
           "adaln_large": "adaln_4x4096x3072"}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
+ALL_CONFIGS = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS, **datagen.LARGE_CONFIGS}
 
 
 def gbps(nbytes: float, seconds: float) -> float:
@@ -189,37 +203,153 @@ class Workload:
         same input, so any set's output is the timed kernel's result)."""
         return to_host(self.y[0])
 
-    def time_steps(self, steps: int, warmup: int, graph: bool = True):
-        """Warm up, then time exactly `steps` launches with HIP events on the
-        launch stream; returns seconds per step.  With `graph`, the `steps`
-        launches are captured into one HIP graph first (they only enqueue
-        kernels) and the timed region is one replay of it: every launch still
-        runs in full, without the host-side cost of issuing it."""
+    def time_steps(self, clock: "Clock", steps: int, warmup: int, graph: bool = False) -> list:
+        """Warm up, then time `clock.windows` windows of exactly `steps`
+        launches each (see Clock); returns seconds per step for every window.
+        With `graph`, the `steps` launches are captured into one HIP graph
+        first (they only enqueue kernels) and each window is one replay of it:
+        every launch still runs in full, without the host-side cost of issuing
+        it."""
         import torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
         if graph:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=self.stream):
                 for i in range(steps):
                     self.step(warmup + i)
             torch.cuda.synchronize()
-            t0.record(self.stream)
-            with torch.cuda.stream(self.stream):
-                g.replay()
-            t1.record(self.stream)
-            torch.cuda.synchronize()
+
+            def issue():
+                with torch.cuda.stream(self.stream):
+                    g.replay()
+            res = clock.time(issue, steps)
             del g
-        else:
-            t0.record(self.stream)
+            return res
+
+        def issue():
             for i in range(steps):
                 self.step(i)
+        return clock.time(issue, steps)
+
+
+class Clock:
+    """Times windows of K launches on one stream with HIP events recorded on
+    that stream.  Before each window the stream is held behind a spin kernel
+    (torch's sleep kernel, about `hold_us` long) while the host records the
+    start event and enqueues the K launches; the start event therefore fires
+    when the first launch can begin at once, and the window measures K
+    back-to-back kernels, not the host's time to issue the first of them.
+    Each window is bracketed by device synchronisation on both sides."""
+
+    def __init__(self, stream, windows: int = 5, hold_us: float = 2000.0):
+        import torch
+        self.stream, self.windows = stream, windows
+        n = 2_000_000
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(1000)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.cuda._sleep(n)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = max(e0.elapsed_time(e1) * 1e3, 1.0)
+        self.cycles_per_us = n / us
+        self.hold_us = hold_us
+        self.hold_cycles = max(1, int(hold_us * self.cycles_per_us))
+
+    def time(self, issue, steps: int) -> list:
+        """issue() enqueues exactly `steps` launches on the stream; returns
+        seconds per launch for each of the windows."""
+        import torch
+        out = []
+        for _ in range(self.windows):
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(self.stream):
+                torch.cuda._sleep(self.hold_cycles)
+            t0.record(self.stream)
+            issue()
             t1.record(self.stream)
             torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e-3 / steps
+            out.append(t0.elapsed_time(t1) * 1e-3 / steps)
+        return out
+
+
+def stats(per_step: list) -> dict:
+    """Median, min and max seconds per step over the windows."""
+    s = sorted(per_step)
+    return {"median": s[len(s) // 2] if len(s) % 2 else 0.5 * (s[len(s) // 2 - 1] + s[len(s) // 2]),
+            "min": s[0], "max": s[-1]}
+
+
+def timing_fields(per_step: list, nbytes: int) -> dict:
+    """The per-workload timing fields: value from the median window, with the
+    fastest and slowest windows beside it."""
+    st = stats(per_step)
+    return {"value": round(gbps(nbytes, st["median"]), 2), "unit": "GB/s",
+            "ms_per_step": round(st["median"] * 1e3, 6),
+            "gpu_ms_median": round(st["median"] * 1e3, 6),
+            "gpu_ms_min": round(st["min"] * 1e3, 6), "gpu_ms_max": round(st["max"] * 1e3, 6),
+            "frac": round(gbps(nbytes, st["median"]) / HBM_PEAK_GBPS, 4)}
+
+
+def copy_ceilings(clock: Clock, wl: Workload, steps: int, warmup: int) -> dict:
+    """The bandwidth ceiling on the same bytes: the committed copy kernels
+    (ceiling/copy.hip) moving each rotating set's x into its y (plain and
+    non-temporal 16-byte copies at 1, 2, 4 and 8 vectors per thread), a
+    non-temporal read-only and write-only stream of the same buffers, and
+    the runtime's device-to-device copy, each timed like the kernels."""
+    import torch
+    import ceiling
+    nvec = wl.x[0].numel() * wl.x[0].element_size() // 16
+    copy_bytes = 2 * 16 * nvec
+    sink = torch.zeros(256, dtype=torch.int32, device=wl.x[0].device)
+    h = wl.stream.cuda_stream
+    out = {}
+
+    def run(key, mode, per, nbytes):
+        def step(i):
+            k = i % wl.nsets
+            ceiling.copy(wl.y[k].data_ptr(), wl.x[k].data_ptr(), nvec, mode, per, sink.data_ptr(), h)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+
+        def issue():
+            for i in range(steps):
+                step(i)
+        res = timing_fields(clock.time(issue, steps), nbytes)
+        res["bytes_per_step"] = nbytes
+        out[key] = res
+
+    for per in (1, 2, 4, 8):
+        run(f"nt_copy_x{per}", ceiling.NT_COPY, per, copy_bytes)
+    for per in (2, 4):
+        run(f"plain_copy_x{per}", ceiling.PLAIN, per, copy_bytes)
+    run("nt_read_x4", ceiling.NT_READ, 4, copy_bytes // 2)
+    run("nt_write_x4", ceiling.NT_WRITE, 4, copy_bytes // 2)
+
+    def memcpy_step(i):
+        k = i % wl.nsets
+        wl.y[k].copy_(wl.x[k])
+    with torch.cuda.stream(wl.stream):
+        for i in range(warmup):
+            memcpy_step(i)
+    torch.cuda.synchronize()
+
+    def memcpy_issue():
+        with torch.cuda.stream(wl.stream):
+            for i in range(steps):
+                memcpy_step(i)
+    out["runtime_d2d_copy"] = {**timing_fields(clock.time(memcpy_issue, steps), copy_bytes),
+                               "bytes_per_step": copy_bytes}
+    best_key = max((k for k in out if "copy" in k), key=lambda k: out[k]["value"])
+    return {"best": best_key, "value": out[best_key]["value"], "unit": "GB/s", "kernels": out}
 
 
 def describe(cfg: datagen.Config, dtype: str = "bf16") -> str:
@@ -250,61 +380,86 @@ def launch_floor_us(stream, launches: int = 1000) -> float:
     return t0.elapsed_time(t1) * 1e3 / launches
 
 
-def cpu_baseline(cfg: datagen.Config, inp: dict, checks: list, budget_s: float = 10.0) -> dict:
-    """The CPU oracle (double arithmetic, one rounding) on this host's cores,
-    rows split into contiguous blocks across a thread pool; repeated over the
-    full batch until `budget_s` has passed.  The same leg then checks every
-    timed kernel's output against the oracle (`checks`, see oracle_parity) and
-    returns that report under "parity"."""
+def cpu_threads() -> tuple:
+    """(threads to use, CPUs this process may run on, CPUs of the host).  The
+    pool takes every CPU the process may run on, capped by OMP_NUM_THREADS
+    when the environment sets it (the CPU share a job on a shared host is
+    given)."""
+    host = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = host
+    t = avail
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        t = min(t, int(env))
+    return max(1, t), avail, host
+
+
+def cpu_baseline(cfg: datagen.Config, inp: dict, checks: list, runs: int = 3,
+                 run_s: float = 2.0) -> dict:
+    """The CPU oracle (double arithmetic, one rounding) on this host: the full
+    batch split into contiguous row blocks over a thread pool, and the full
+    batch on one thread.  Each is timed `runs` times (a pooled run repeats
+    whole passes for about `run_s` seconds) and the median per-pass time is
+    reported.  The same
+    leg then checks every timed kernel's output against the oracle (`checks`,
+    see oracle_parity) and returns that report under "parity"."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     o = oracle.Oracle()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, avail, host = cpu_threads()
     x, w = inp["x"], inp["w"]
-    blocks = np.array_split(np.arange(cfg.rows), threads)
+    blocks = [b for b in np.array_split(np.arange(cfg.rows), threads) if len(b)]
 
     def work(b):
-        if len(b) == 0:
-            return 0
         y = o.rmsnorm(x[b[0]:b[-1] + 1], w, cfg.eps)
         o.round(y)
         return len(b)
 
-    passes = 0
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        while True:
-            list(ex.map(work, blocks))
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    per_pass = el / passes
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
 
-    # one thread on a 2048-row slice of the batch, for about 3 s
-    sub = np.arange(min(2048, cfg.rows))
-    sub_bytes = 4 * len(sub) * cfg.hidden + 2 * cfg.hidden
-    n1 = 0
-    t1 = time.perf_counter()
-    while True:
-        work(sub)
-        n1 += 1
-        el1 = time.perf_counter() - t1
-        if el1 >= budget_s * 0.3:
-            break
+    pool_s, passes = [], []
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, blocks))  # first touch of the pages and the library
+        for _ in range(runs):
+            # one run: whole passes over the batch until run_s has passed
+            n, t0 = 0, time.perf_counter()
+            while True:
+                list(ex.map(work, blocks))
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= run_s:
+                    break
+            pool_s.append(el / n)
+            passes.append(n)
+    one_s = []
+    whole = np.arange(cfg.rows)
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        work(whole)
+        one_s.append(time.perf_counter() - t0)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(gbps(cfg.algorithmic_bytes(), per_pass), 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"full {cfg.name} batch ({cfg.rows} rows x {cfg.hidden}), {passes} passes "
-                      f"in {el:.1f} s; double arithmetic + rounding to bf16; "
-                      f"{per_pass * 1e3:.1f} ms per pass",
-            "single_thread": {"value": round(gbps(sub_bytes, el1 / n1), 3), "unit": "GB/s",
-                              "sample": f"{len(sub)} rows x {cfg.hidden}, {n1} passes in {el1:.1f} s"},
+    nbytes = cfg.algorithmic_bytes()
+    return {"value": round(gbps(nbytes, med(pool_s)), 3), "unit": "GB/s",
+            "cores": threads, "threads": threads, "host_cpus": host, "cpus_available": avail,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "kind": "oracle",
+            "ms_median": round(med(pool_s) * 1e3, 2), "ms_runs": [round(s * 1e3, 2) for s in pool_s],
+            "sample": f"the full {cfg.name} batch ({cfg.rows} rows x {cfg.hidden}, {nbytes} "
+                      f"algorithmic bytes) in {len(blocks)} contiguous row blocks over {threads} "
+                      f"threads; {runs} runs of {passes} passes, median per-pass time; double "
+                      f"arithmetic + rounding to bf16",
+            "single_thread": {"value": round(gbps(nbytes, med(one_s)), 3), "unit": "GB/s",
+                              "ms_median": round(med(one_s) * 1e3, 2),
+                              "sample": f"the full batch on one thread, median of {runs} runs"},
             "cpu_model": model,
             "parity": oracle_parity(checks)}
 
@@ -343,37 +498,45 @@ def oracle_parity(checks: list, workers: int = 4) -> dict:
     with cf.ThreadPoolExecutor(workers) as ex:
         reps = dict(ex.map(one, checks))
     return {"all_pass": all(r["pass"] for r in reps.values()),
-            "rule": "|gpu - oracle| <= 1 ulp of the output type (bf16/fp16), or 2^-18 (|ref| + m) "
+            "rule": "|gpu - oracle| <= 1 ulp of the output type (bf16/fp16), or 2^-20 (|ref| + m) "
                     "for fp32; a 2^-16 m floor where RoPE / AdaLN terms of magnitude m cancel",
             "seconds": round(time.perf_counter() - t0, 1),
             "workloads": reps}
 
 
 def probe(kind: str, launches: int):
-    """A handful of launches for counter collection (rocprofv3 --pmc)."""
+    """A short run of one workload for rocprofv3 (kernel traces and counter
+    passes), with the benchmark's rotating buffer sets."""
     import torch
     dev = torch.device("cuda:0")
     s = torch.cuda.Stream()
-    if kind == "copy":
-        n = datagen.CONFIGS[datagen.HEADLINE].rows * datagen.CONFIGS[datagen.HEADLINE].hidden
-        a = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
-        b = torch.empty_like(a)
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for _ in range(launches):
-                b.copy_(a)
+    if kind in ("copy", "copy_nt"):
+        cfg = datagen.CONFIGS[datagen.HEADLINE]
+        wl = Workload(cfg, dev, s)
+        n = cfg.rows * cfg.hidden
+        if kind == "copy":  # the runtime's copy kernel: the counters' calibration
+            with torch.cuda.stream(s):
+                for i in range(launches):
+                    wl.y[i % wl.nsets].copy_(wl.x[i % wl.nsets])
+        else:
+            import ceiling
+            for i in range(launches):
+                k = i % wl.nsets
+                ceiling.copy(wl.y[k].data_ptr(), wl.x[k].data_ptr(), 2 * n // 16, ceiling.NT_COPY,
+                             2, None, s.cuda_stream)
         torch.cuda.synchronize()
-        print(json.dumps({"probe": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+        print(json.dumps({"probe": kind, "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS, **datagen.LARGE_CONFIGS}[PROBES[kind]]
+    cfg = ALL_CONFIGS[PROBES.get(kind, kind)]
     dtype = kind[4:] if kind in ("rms_f16", "rms_f32") else "bf16"
-    wl = Workload(cfg, dev, s, max_sets=2, dtype=dtype)
+    wl = Workload(cfg, dev, s, dtype=dtype)
     for i in range(launches):
         wl.step(i)
     torch.cuda.synchronize()
     print(json.dumps({"probe": kind, "workload": cfg.name, "dtype": dtype, "launches": launches,
-                      "algorithmic_bytes": wl.nbytes}), flush=True)
+                      "rotating_sets": wl.nsets, "algorithmic_bytes": wl.nbytes,
+                      "kernel": describe(cfg, dtype)}), flush=True)
 
 
 def main():
@@ -381,6 +544,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--windows", type=int, default=5,
+                    help="timed windows of --steps launches each; the median is reported")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the RoPE, AdaLN, other-dtype and general line items (the "
@@ -388,7 +553,9 @@ def main():
     ap.add_argument("--no-pages", action="store_true",
                     help="skip the pages' other RMSNorm shapes (one of them runs the headline's "
                          "kernel instance, which would merge the two in a per-kernel trace)")
-    ap.add_argument("--probe", choices=sorted(PROBES) + ["copy"])
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the copy-ceiling kernels (they would appear in a kernel trace)")
+    ap.add_argument("--probe", choices=sorted(PROBES) + sorted(datagen.CONFIGS) + ["copy", "copy_nt"])
     ap.add_argument("--launches", type=int, default=10)
     ap.add_argument("--launch", choices=["stream", "graph"], default="stream",
                     help="issue the timed launches one by one on the stream (default) or as one "
@@ -413,23 +580,29 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     name = torch.cuda.get_device_name(0)
+    clock = Clock(stream, windows=max(1, args.windows))
+    graph = args.launch == "graph"
+
+    def timed(rw, mode_graph=graph):
+        return timing_fields(rw.time_steps(clock, args.steps, args.warmup, mode_graph), rw.nbytes)
 
     cfg = datagen.CONFIGS[datagen.HEADLINE]
     wl = Workload(cfg, dev, stream)
-    graph = args.launch == "graph"
-    sec = wl.time_steps(args.steps, args.warmup, graph)
-    value = gbps(cfg.algorithmic_bytes(), sec)
-    sec_other = wl.time_steps(args.steps, args.warmup, not graph)  # the other launch mode
+    head = timed(wl)
+    other = timed(wl, not graph)  # the other launch mode
     checks = [("headline", cfg, "bf16", wl.host, wl.output())]
+    value = head["value"]
+    sec = head["ms_per_step"] * 1e-3
     traffic = read_traffic("rmsnorm", cfg.name)
+    ceil = None if args.no_ceiling else copy_ceilings(clock, wl, args.steps, args.warmup)
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(sec * 1e3, 6),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / H100_GBPS_4x4096x3072, 3),
@@ -440,9 +613,17 @@ def main():
                    "bytes_per_step": cfg.algorithmic_bytes(), "rotating_sets": wl.nsets,
                    "seed": datagen.BASE_SEED, "x_fnv": datagen.fnv1a64(wl.host["x"]),
                    "device": name},
+        "dtype_note": "dtype is the arithmetic type (binary32 accumulation and scaling); the "
+                      "tensors are bf16 (config.io_dtype)",
+        "timing": {"windows": clock.windows, "launches_per_window": args.steps,
+                   "gpu_ms_median": head["gpu_ms_median"], "gpu_ms_min": head["gpu_ms_min"],
+                   "gpu_ms_max": head["gpu_ms_max"], "hold_us": clock.hold_us,
+                   "method": "HIP events on the launch stream around each window of --steps "
+                             "launches, the stream held behind a spin kernel while the host "
+                             "enqueues them; value and ms_per_step from the median window"},
         "pct_of_peak": round(pct_of_peak(value, HBM_PEAK_GBPS), 2),
-        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": head["frac"],
                      "traffic": None if traffic is None else round(traffic / sec / 1e9, 2),
                      "kernel": "rmsnorm_kernel",
                      "launch_shape": describe(cfg),
@@ -450,14 +631,14 @@ def main():
         "baseline_note": "vs_baseline divides by the H100 figure for this shape on the "
                          "pages (0.157 ms = 1282.4 GB/s); another GPU, context only",
     }
+    if ceil is not None:
+        line["copy_ceiling"] = ceil
+        line["pct_of_copy_ceiling"] = round(100.0 * value / ceil["value"], 2)
     if traffic is not None:
         line["roofline"]["traffic_bytes_per_launch"] = int(traffic)
-    line["launch"] = ("one HIP graph of the K launches, replayed once in the timed region"
+    line["launch"] = ("one HIP graph of the K launches, replayed once per window"
                       if graph else "K launches issued one by one on the stream")
-    line["graph_launch" if not graph else "stream_launch"] = {
-        "value": round(gbps(cfg.algorithmic_bytes(), sec_other), 2), "unit": "GB/s",
-        "ms_per_step": round(sec_other * 1e3, 6),
-        "frac": round(gbps(cfg.algorithmic_bytes(), sec_other) / HBM_PEAK_GBPS, 4)}
+    line["graph_launch" if not graph else "stream_launch"] = other
     floor = launch_floor_us(stream)
     line["launch_floor_us"] = round(floor, 3)
     line["launch_floor_note"] = ("per-launch time of an empty kernel launched back to back on the "
@@ -469,20 +650,18 @@ def main():
 
     # the other shapes of the pages' micro-benchmark table, in both launch modes
     line["pages_shapes"] = {}
-    for name in () if args.no_pages else ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
-                                          "rms_2x4096x3072_outliers"):
-        rc = datagen.CONFIGS[name]
+    for wname in () if args.no_pages else ("rms_1x1024x2048", "rms_2x1024x2048", "rms_4x1024x2048",
+                                           "rms_2x4096x3072_outliers"):
+        rc = datagen.CONFIGS[wname]
         rw = Workload(rc, dev, stream)
-        rsec = rw.time_steps(args.steps, args.warmup, graph)
-        gsec = rw.time_steps(args.steps, args.warmup, not graph)
-        rv = gbps(rw.nbytes, rsec)
-        line["pages_shapes"][name] = {
-            "kernel": describe(rc), "ms_per_step": round(rsec * 1e3, 6),
-            ("graph" if not graph else "stream") + "_ms_per_step": round(gsec * 1e3, 6),
-            "value": round(rv, 2), "unit": "GB/s", "frac": round(rv / HBM_PEAK_GBPS, 4),
+        r = timed(rw)
+        g = timed(rw, not graph)
+        line["pages_shapes"][wname] = {
+            "kernel": describe(rc), **r,
+            ("graph" if not graph else "stream") + "_ms_per_step": g["ms_per_step"],
             "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
-            "h100_ms_on_the_pages": H100_MS[name]}
-        checks.append((name, rc, "bf16", rw.host, rw.output()))
+            "h100_ms_on_the_pages": H100_MS[wname]}
+        checks.append((wname, rc, "bf16", rw.host, rw.output()))
         del rw
         torch.cuda.empty_cache()
     if not args.no_pages:
@@ -491,7 +670,7 @@ def main():
                                         "removes the host-side issue cost")
 
     if not args.no_rope:
-        for key, name, kernel, dtype in (
+        for key, wname, kernel, dtype in (
                 ("rope", datagen.ROPE, "rmsnorm_rope", "bf16"),
                 ("rope_interleaved", datagen.ROPE_INTERLEAVED, "rmsnorm_rope_interleaved", "bf16"),
                 ("adaln", datagen.ADALN, "rmsnorm_adaln", "bf16"),
@@ -503,39 +682,35 @@ def main():
                 ("rope_large", "rope_4x4096x3072_h24d128", "rmsnorm_rope_large", "bf16"),
                 ("rope_interleaved_large", "ropei_4x4096x3072_h24d128", "rmsnorm_rope_il_large", "bf16"),
                 ("adaln_large", "adaln_4x4096x3072", "rmsnorm_adaln_large", "bf16")):
-            rc = {**datagen.CONFIGS, **datagen.LARGE_CONFIGS}[name]
+            rc = ALL_CONFIGS[wname]
             rw = Workload(rc, dev, stream, dtype=dtype)
-            rsec = rw.time_steps(args.steps, args.warmup, graph)
-            rv = gbps(rw.nbytes, rsec)
+            r = timed(rw)
             rtraffic = read_traffic(kernel, rc.name)
-            line[key] = {"workload": rc.name, "io_dtype": dtype, "kernel": describe(rc, dtype),
-                         "value": round(rv, 2),
-                         "unit": "GB/s", "ms_per_step": round(rsec * 1e3, 6),
+            line[key] = {"workload": rc.name, "io_dtype": dtype, "kernel": describe(rc, dtype), **r,
                          "bytes_per_step": rw.nbytes, "rotating_sets": rw.nsets,
-                         "frac": round(rv / HBM_PEAK_GBPS, 4),
-                         "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
+                         "traffic": None if rtraffic is None
+                         else round(rtraffic / (r["ms_per_step"] * 1e-3) / 1e9, 2)}
             checks.append((key, rc, dtype, rw.host, rw.output()))
             del rw
             torch.cuda.empty_cache()
         # shapes served by the kernels for rows of any length
         line["general"] = {}
-        for name, kernel, path in (
+        for wname, kernel, path in (
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
                 ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
                 ("rms_1x256x262144", "rmsnorm_long", "two-pass"),
                 ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, several per wavefront"),
                 ("adaln_8x4096x1152", "rmsnorm_adaln_seg", "segmented rows, several per wavefront")):
-            rc = datagen.GENERAL_CONFIGS[name]
+            rc = datagen.GENERAL_CONFIGS[wname]
             rw = Workload(rc, dev, stream)
-            rsec = rw.time_steps(args.steps, args.warmup, graph)
-            rv = gbps(rw.nbytes, rsec)
+            r = timed(rw)
             rtraffic = read_traffic(kernel, rc.name)
-            line["general"][name] = {
-                "path": path, "kernel": describe(rc), "value": round(rv, 2), "unit": "GB/s",
-                "ms_per_step": round(rsec * 1e3, 6), "bytes_per_step": rw.nbytes,
-                "rotating_sets": rw.nsets, "frac": round(rv / HBM_PEAK_GBPS, 4),
-                "traffic": None if rtraffic is None else round(rtraffic / rsec / 1e9, 2)}
-            checks.append((name, rc, "bf16", rw.host, rw.output()))
+            line["general"][wname] = {
+                "path": path, "kernel": describe(rc), **r, "bytes_per_step": rw.nbytes,
+                "rotating_sets": rw.nsets,
+                "traffic": None if rtraffic is None
+                else round(rtraffic / (r["ms_per_step"] * 1e-3) / 1e9, 2)}
+            checks.append((wname, rc, "bf16", rw.host, rw.output()))
             del rw
             torch.cuda.empty_cache()
 
