@@ -256,13 +256,23 @@ def _check_act(x, name, like=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_weight(weight, x):
+    """The weight is [hidden] in x's dtype: the kernels read exactly hidden
+    values from it, so a shorter tensor is refused here, before any launch."""
+    if weight is None:
+        return
+    _check_act(weight, "weight", x)
+    hidden = x.shape[-1] if x.dim() else 0
+    if weight.numel() != hidden:
+        raise ValueError(f"weight must hold hidden = {hidden} values, got {weight.numel()}")
+
+
 def rmsnorm(x, weight=None, eps: float = 1e-6, out=None):
     """RMSNorm over the last dimension of ``x`` (bf16, fp16 or fp32; weight
     [H] of the same dtype, or None)."""
     import torch
     _check_act(x, "x")
-    if weight is not None:
-        _check_act(weight, "weight", x)
+    _check_weight(weight, x)
     hidden = x.shape[-1]
     if out is None:
         out = torch.empty_like(x)
@@ -282,8 +292,7 @@ def rmsnorm_rope(x, weight, cos_tab, sin_tab, heads: int, head_dim: int, eps: fl
     ``interleaved``; row r uses table row r mod cos_tab.shape[0]."""
     import torch
     _check_act(x, "x")
-    if weight is not None:
-        _check_act(weight, "weight", x)
+    _check_weight(weight, x)
     for t, n in ((cos_tab, "cos_tab"), (sin_tab, "sin_tab")):
         if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous float32 GPU tensor")
@@ -311,7 +320,8 @@ def rmsnorm_adaln(x, weight, scale, shift, eps: float = 1e-6, out=None, rows_per
     sample r // S."""
     import torch
     _check_act(x, "x")
-    for t, n in ((weight, "weight"), (scale, "scale"), (shift, "shift")):
+    _check_weight(weight, x)
+    for t, n in ((scale, "scale"), (shift, "shift")):
         if t is not None:
             _check_act(t, n, x)
     hidden = x.shape[-1]
@@ -320,16 +330,20 @@ def rmsnorm_adaln(x, weight, scale, shift, eps: float = 1e-6, out=None, rows_per
         if x.dim() != 3:
             raise ValueError("give rows_per_sample for x that is not [B, S, H]")
         rows_per_sample = x.shape[1]
+    rows_per_sample = int(rows_per_sample)
     if out is None:
         out = torch.empty_like(x)
     else:
         _check_act(out, "out", x)
         if out.shape != x.shape:
             raise ValueError("out must have the shape of x")
-    samples = -(-rows // rows_per_sample) if rows else 0
-    for t, n in ((scale, "scale"), (shift, "shift")):
-        if t is not None and t.numel() != samples * hidden:
-            raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
-    ltxnorm_rmsnorm_adaln_fwd_dt(out, x, weight, scale, shift, rows, hidden,
-                                 max(rows_per_sample, 1), eps, _dtype_code(x), None)
+    if rows_per_sample >= 1:
+        samples = -(-rows // rows_per_sample) if rows else 0
+        for t, n in ((scale, "scale"), (shift, "shift")):
+            if t is not None and t.numel() != samples * hidden:
+                raise ValueError(f"{n} must hold [{samples}, {hidden}] values")
+    # rows_per_sample < 1 goes to the library unchanged, which refuses it
+    # with LTXNORM_ERR_SHAPE before any launch
+    ltxnorm_rmsnorm_adaln_fwd_dt(out, x, weight, scale, shift, rows, hidden, rows_per_sample, eps,
+                                 _dtype_code(x), None)
     return out

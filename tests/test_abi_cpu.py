@@ -237,6 +237,63 @@ def test_python_front_end_refuses_host_tensors():
         ltx.rmsnorm_rope(x, None, torch.zeros(4, 8), torch.zeros(4, 8), 4, 16)
 
 
+class FakeDeviceTensor:
+    """Stands in for a GPU tensor in the binding's argument checks: a shape, a
+    dtype and a fake aligned address that nothing dereferences (every call
+    below fails its checks before any launch)."""
+    is_cuda = True
+
+    def __init__(self, shape, dtype, addr):
+        self.shape, self.dtype, self.addr = tuple(shape), dtype, addr
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return int(np.prod(self.shape)) if self.shape else 1
+
+    def dim(self):
+        return len(self.shape)
+
+    def data_ptr(self):
+        return self.addr
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "rope", "adaln"])
+@pytest.mark.parametrize("wlen", [2047, 2049, 1])
+def test_front_end_refuses_a_weight_of_the_wrong_length(op, wlen):
+    """The kernels read hidden weight values: a shorter (or longer) weight is
+    refused by the binding before the library is called."""
+    import torch
+    bf = torch.bfloat16
+    x = FakeDeviceTensor((2, 4, 2048), bf, A + 64 * MB)
+    out = FakeDeviceTensor((2, 4, 2048), bf, A)
+    w = FakeDeviceTensor((wlen,), bf, A + 128 * MB)
+    with pytest.raises(ValueError, match="weight must hold"):
+        if op == "rmsnorm":
+            ltx.rmsnorm(x, w, out=out)
+        elif op == "rope":
+            tab = FakeDeviceTensor((4, 32), torch.float32, A + 130 * MB)
+            ltx.rmsnorm_rope(x, w, tab, tab, 32, 64, out=out)
+        else:
+            ltx.rmsnorm_adaln(x, w, None, None, out=out)
+
+
+@pytest.mark.parametrize("rps", [0, -1, -4096])
+def test_front_end_passes_rows_per_sample_to_the_library(rps, monkeypatch):
+    """rows_per_sample below 1 reaches the C ABI unchanged, which refuses it
+    with LTXNORM_ERR_SHAPE before any HIP call (the stream handle is never
+    used)."""
+    import torch
+    monkeypatch.setattr(ltx, "_stream", lambda s: 0)
+    bf = torch.bfloat16
+    x = FakeDeviceTensor((8, 2048), bf, A + 64 * MB)
+    out = FakeDeviceTensor((8, 2048), bf, A)
+    with pytest.raises(ltx.LtxnormError) as e:
+        ltx.rmsnorm_adaln(x, None, None, None, out=out, rows_per_sample=rps)
+    assert e.value.status == ltx.ERR_SHAPE
+
+
 def test_error_raises_with_status():
     with pytest.raises(ltx.LtxnormError) as e:
         ltx.ltxnorm_rmsnorm_fwd(A, A + 64 * MB, None, 4, (1 << 24) + 1, 1e-6, 0)
