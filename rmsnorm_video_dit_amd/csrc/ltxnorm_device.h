@@ -49,6 +49,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "ltxnorm_launch.h"
 
@@ -180,6 +181,58 @@ __device__ __forceinline__ float dpp(float v) {
                                                               0xF, 0xF, false));
 }
 
+// The value of lane l ^ P, for P a power of two up to 32, without a round
+// trip through the LDS crossbar (ds_bpermute): DPP moves inside each 16-lane
+// row, the gfx950 lane swaps across rows.  Every lane of the wavefront must
+// be active.
+//  * P = 1, 2: quad_perm [1,0,3,2] / [2,3,0,1].
+//  * P = 4: row_half_mirror (j -> j ^ 7 within the row), then quad_perm
+//    [3,2,1,0] (j -> j ^ 3): j ^ 4.
+//  * P = 8: row_mirror (j -> j ^ 15), then row_half_mirror (j -> j ^ 7): j ^ 8.
+//  * P = 16: v_permlane16_swap of the value with itself swaps the odd rows
+//    of the first copy with the even rows of the second, so the first result
+//    holds rows (0, 0, 2, 2) and the second rows (1, 1, 3, 3): a lane of an
+//    even row takes the second, a lane of an odd row the first.
+//  * P = 32: v_permlane32_swap likewise gives halves (lo, lo) and (hi, hi).
+template <int P>
+__device__ __forceinline__ float xor_lane(float v) {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16 || P == 32, "P: 1..32");
+    if constexpr (P == 1) {
+        return dpp<0xB1>(v);
+    } else if constexpr (P == 2) {
+        return dpp<0x4E>(v);
+    } else if constexpr (P == 4) {
+        return dpp<0x1B>(dpp<0x141>(v));
+    } else if constexpr (P == 8) {
+        return dpp<0x141>(dpp<0x140>(v));
+    } else {
+        const uint32_t b = __builtin_bit_cast(uint32_t, v);
+        const bool upper = (threadIdx.x & P) != 0;
+        if constexpr (P == 16) {
+            const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+            return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+            return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+        }
+    }
+}
+
+// Call f(std::integral_constant<int, P>{}) for a wave-uniform P in {1, 2,
+// 4, 8, 16, 32}: one scalar branch per call, so that what f does for its P
+// (every xor_lane<P> of a row) is straight-line code.
+template <typename F>
+__device__ __forceinline__ void with_pow2(int P, F&& f) {
+    switch (P) {
+        case 1: f(std::integral_constant<int, 1>{}); break;
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 8: f(std::integral_constant<int, 8>{}); break;
+        case 16: f(std::integral_constant<int, 16>{}); break;
+        default: f(std::integral_constant<int, 32>{}); break;
+    }
+}
+
 // Sum over the 64 lanes of a fully active wavefront.  Inside each row of 16
 // lanes: xor-1 and xor-2 swaps (quad_perm), then the 8-lane and 16-lane
 // mirrors; each step adds two equal-shaped partial sums, so all lanes of a
@@ -280,17 +333,33 @@ __device__ __forceinline__ void load_row(u32x4* xv, const u32x4* xr, int t, int 
     }
 }
 
-// RoPE table slices through one wavefront-wide load.  fetch(): lanes
-// [0, nc) load chunk `lane` (W consecutive floats) of the position's cos row
-// and of its sin row; the other lanes load nothing.  gather(), once the loads
-// have landed: each lane takes the two W-float chunks that start at columns
-// col0 and col1 (multiples of W) from the lanes holding them, with
-// ds_bpermute.  Two partial loads per wavefront replace four 16-byte loads
-// per lane, for kernels whose rows are short enough that table reads weigh
-// (hidden 1152, heads of 72: 64 -> 71 % of peak at about 200 MB).
-template <int W>
-struct TableChunks {
+// RoPE table slices handed out through LDS, for kernels whose lanes need
+// table columns that other lanes fetched.  fetch(): lanes [0, nc) load chunk
+// `lane` (W consecutive floats) of the position's cos row and of its sin
+// row; the other lanes load nothing.  share(), once those loads have landed:
+// the same lanes write their chunks into this wavefront's LDS region.
+// take(col): each lane reads the W floats at column col (a multiple of W) of
+// both tables, one 8- or 16-byte LDS read per table; lanes reading the same
+// chunk read the same address.  Two partial global loads, two LDS writes and
+// two LDS reads per chunk a lane needs replace a 16-byte global load per
+// table per lane (rows short enough that table reads weigh: hidden 1152,
+// heads of 72), and the 2 W ds_bpermute transfers per chunk of an exchange
+// between lanes, whose many-to-one reads conflicted in the LDS banks.
+// NW wavefronts per workgroup; a wavefront's region holds up to MAXC chunks
+// per table.  LDS accesses of one wavefront complete in order, so the reads
+// see the writes without a workgroup barrier, and the next row's writes come
+// after this row's reads.
+template <int W, int NW, int MAXC>
+struct TableLds {
+    static_assert(W == 2 || W == 4, "chunks of 2 or 4 floats");
     float tc[W], ts[W];
+    float* cos_region;
+    float* sin_region;
+    __device__ __forceinline__ explicit TableLds(int wave) {
+        __shared__ __attribute__((aligned(16))) float lds[NW][2][MAXC * W];
+        cos_region = &lds[wave][0][0];
+        sin_region = &lds[wave][1][0];
+    }
     __device__ __forceinline__ void fetch(const float* crow, const float* srow, int lane, int nc) {
 #pragma unroll
         for (int j = 0; j < W; ++j) tc[j] = ts[j] = 0.0f;
@@ -299,23 +368,36 @@ struct TableChunks {
             load_floats<W>(srow + lane * W, ts);
         }
     }
-    // one chunk: the W floats at column col
-    __device__ __forceinline__ void gather1(int col, float* c, float* s) const {
-        const int a0 = (col / W) << 2;
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-            c[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, tc[j])));
-            s[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, ts[j])));
+    __device__ __forceinline__ void share(int lane, int nc) {
+        if (lane < nc) {
+            if constexpr (W == 4) {
+                *reinterpret_cast<f32x4*>(cos_region + lane * W) = f32x4{tc[0], tc[1], tc[2], tc[3]};
+                *reinterpret_cast<f32x4*>(sin_region + lane * W) = f32x4{ts[0], ts[1], ts[2], ts[3]};
+            } else {
+                *reinterpret_cast<f32x2*>(cos_region + lane * W) = f32x2{tc[0], tc[1]};
+                *reinterpret_cast<f32x2*>(sin_region + lane * W) = f32x2{ts[0], ts[1]};
+            }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __device__ __forceinline__ void gather(int col0, int col1, float* c, float* s) const {
-        const int a0 = (col0 / W) << 2, a1 = (col1 / W) << 2;  // ds_bpermute byte addresses
+    __device__ __forceinline__ void take(int col, float* c, float* s) const {
+        if constexpr (W == 4) {
+            const f32x4 vc = *reinterpret_cast<const f32x4*>(cos_region + col);
+            const f32x4 vs = *reinterpret_cast<const f32x4*>(sin_region + col);
 #pragma unroll
-        for (int j = 0; j < W; ++j) {
-            c[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, tc[j])));
-            c[W + j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, tc[j])));
-            s[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, ts[j])));
-            s[W + j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, ts[j])));
+            for (int j = 0; j < 4; ++j) {
+                c[j] = vc[j];
+                s[j] = vs[j];
+            }
+        } else {
+            const f32x2 vc = *reinterpret_cast<const f32x2*>(cos_region + col);
+            const f32x2 vs = *reinterpret_cast<const f32x2*>(sin_region + col);
+            c[0] = vc[0];
+            c[1] = vc[1];
+            s[0] = vs[0];
+            s[1] = vs[1];
         }
     }
 };

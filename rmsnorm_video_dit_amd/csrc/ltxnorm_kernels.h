@@ -71,8 +71,9 @@ rmsnorm_kernel(const KArgs a) {
 //    fills 56-75 %.  The choice and its measurements are with segments_for.
 // A load instruction covers 64 / S rows' runs of S vectors.  The sum of
 // squares is reduced inside each segment by the first log2 S steps of the
-// wavefront reduction (and an xor-16 exchange for S = 32), so every lane of a
-// row ends with the same bits.  RMSNorm, AdaLN, and RoPE whose partners stay
+// wavefront reduction (and the xor-16 lane swap for S = 32), so every lane of
+// a row ends with the same bits.  Partner values move between lanes with DPP
+// and the lane swaps (xor_lane), not through the LDS crossbar.  RMSNorm, AdaLN, and RoPE whose partners stay
 // inside a row's lanes: rotate-half with power-of-two half heads (partner
 // lane l ^ P in the same slot for P <= S/2, the lane's other slot for V = 2
 // and P == S) and interleaved pairs.
@@ -83,10 +84,7 @@ __device__ __forceinline__ float segment_sum(float v) {
     if constexpr (S >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: xor 2
     if constexpr (S >= 8) v += dpp<0x141>(v);   // row_half_mirror: 8 lanes
     if constexpr (S >= 16) v += dpp<0x140>(v);  // row_mirror: 16 lanes
-    if constexpr (S >= 32) {                    // the other 16 lanes
-        const int src = (((int)threadIdx.x & (kWave - 1)) ^ 16) << 2;
-        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
-    }
+    if constexpr (S >= 32) v += xor_lane<16>(v);  // the other 16 lanes
     return v;
 }
 
@@ -111,16 +109,15 @@ rmsnorm_short_kernel(const KArgs a) {
 
     // rotation constants of this lane: the xor layout of the power-of-two
     // kernel within the row's lanes, whose table slice (v mod P) is the same
-    // for every slot, whether S is a multiple of 2P or P == S (then src and
-    // sgn go unused: the partner is the lane's other slot); or the
+    // for every slot, whether S is a multiple of 2P or P == S (then sgn goes
+    // unused: the partner is the lane's other slot); or the
     // interleaved table columns of each slot
-    int src = 0, toff[V];
+    int toff[V];
     float sgn = 1.0f;
 #pragma unroll
     for (int k = 0; k < V; ++k) toff[k] = 0;
     if constexpr (OP == GOp::kRopeHalf) {
         const int P = a.vec_per_half;
-        src = (lane ^ P) << 2;
         sgn = (l & P) ? 1.0f : -1.0f;
         toff[0] = (l & (P - 1)) * E;
     } else if constexpr (OP == GOp::kRopeIl) {
@@ -216,11 +213,12 @@ rmsnorm_short_kernel(const KArgs a) {
                 for (int e = 0; e < E; ++e) o[e] = f[e] * (1.0f + sc[e]) + sh[e];
             } else if constexpr (OP == GOp::kRopeHalf) {
                 // the partner lane's normalised values; -sin in the first half
+                // (P <= S / 2 <= 16 here)
+                with_pow2(a.vec_per_half, [&](auto pc) {
+                    constexpr int PC = decltype(pc)::value < 16 ? decltype(pc)::value : 16;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float par = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, f[e])));
-                    o[e] = f[e] * c[0][e] + par * (sn[0][e] * sgn);
-                }
+                    for (int e = 0; e < E; ++e) o[e] = f[e] * c[0][e] + xor_lane<PC>(f[e]) * (sn[0][e] * sgn);
+                });
             } else if constexpr (OP == GOp::kRopeIl) {
 #pragma unroll
                 for (int j = 0; j < E / 2; ++j) {
@@ -242,10 +240,11 @@ rmsnorm_short_kernel(const KArgs a) {
 // 32.  Lane t holds vectors k*L + t (full 1 KiB lines per load
 // instruction); the partner of vector v is v ^ P: the same slot of lane
 // t ^ P in the same wavefront.  Each lane normalises its own vector and
-// fetches the partner's normalised binary32 values with ds_bpermute
-// (exchanging the finished values rather than raw x halves the VALU work per
-// vector, which matters because with one row per wavefront the whole grid is
-// resident and compute is not hidden behind later loads).  A lane's half
+// fetches the partner's normalised binary32 values with DPP moves or a lane
+// swap (xor_lane), a few VALU cycles each instead of an LDS-crossbar round
+// trip per value (exchanging the finished values rather than raw x halves
+// the VALU work per vector, which matters because with one row per wavefront
+// the whole grid is resident and compute is not hidden behind later loads).  A lane's half
 // (bit P of t) and its table slice (floats kEpv * (t mod P) .. + kEpv) do not
 // depend on the slot, so each lane reads one table slice per row.
 // ---------------------------------------------------------------------------
@@ -256,65 +255,68 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
-    const int P = a.vec_per_half;
-    const int src = ((ln.lane ^ P) & (kWave - 1)) << 2;  // ds_bpermute byte address
-    const float sgn = (ln.t & P) ? 1.0f : -1.0f;  // second half adds, first subtracts
-    const int toff = (ln.t & (P - 1)) * E;
+    // one copy of the row loop per partner distance P (a scalar branch at
+    // entry): inside it every exchange is straight-line DPP or lane-swap
+    // code, and each copy is register-allocated on its own (one loop with a
+    // branch per row measured 93 VGPRs against 79)
+    with_pow2(a.vec_per_half, [&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        const float sgn = (ln.t & P) ? 1.0f : -1.0f;  // second half adds, first subtracts
+        const int toff = (ln.t & (P - 1)) * E;
 
-    u32x4 wv[VPL];
-    load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+        u32x4 wv[VPL];
+        load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
-    int parity = 0;
-    for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
-         base += (int64_t)gridDim.x * RPB, parity ^= 1) {
-        const int64_t row = base + ln.slot;
-        const bool active = row < a.rows;
-        if (WPR == 1 && !active) continue;
-        const int64_t pos = active ? row % a.seq_len : 0;
-        const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
-        u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+        int parity = 0;
+        for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
+             base += (int64_t)gridDim.x * RPB, parity ^= 1) {
+            const int64_t row = base + ln.slot;
+            const bool active = row < a.rows;
+            if (WPR == 1 && !active) continue;
+            const int64_t pos = active ? row % a.seq_len : 0;
+            const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
+            u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
-        u32x4 xv[VPL];
-        load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
-        // The table slice is an L2 hit.  With several wavefronts per row it is
-        // fetched together with x, off the critical path behind the row's
-        // barrier (H = 3072, d = 128: 69.6 -> 74.1 % of peak; H = 2304:
-        // 58.0 -> 64.3 %); with one wavefront per row either order measured
-        // the same, and fetching it after the reduction keeps registers free.
-        float c[E], ss[E];
-        if constexpr (WPR > 1) {
-            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
-            load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+            u32x4 xv[VPL];
+            load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
+            // The table slice is an L2 hit.  With several wavefronts per row
+            // it is fetched together with x, off the critical path behind the
+            // row's barrier (H = 3072, d = 128: 69.6 -> 74.1 % of peak;
+            // H = 2304: 58.0 -> 64.3 %); with one wavefront per row either
+            // order measured the same, and fetching it after the reduction
+            // keeps registers free.
+            float c[E], ss[E];
+            if constexpr (WPR > 1) {
+                load_floats<E>(a.cos_tab + pos * a.half + toff, c);
+                load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+            }
+            const float part = sum_squares<IO, VPL>(xv);
+            const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+            if constexpr (WPR == 1) {
+                load_floats<E>(a.cos_tab + pos * a.half + toff, c);
+                load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
+            }
+            // the partner term enters with -sin in the first half, +sin in the second
+#pragma unroll
+            for (int e = 0; e < E; ++e) ss[e] *= sgn;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = k * L + ln.t;
+                const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
+                keep_packed(xv[k]);
+                keep_packed(wv[k]);
+                float own[E], g[E], o[E];
+                IO::widen(xv[k], own);
+                IO::widen(wv[k], g);
+#pragma unroll
+                for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
+                // the partner lane's normalised values, exact binary32 bits
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + xor_lane<P>(own[e]) * ss[e];
+                if (in) store_stream(yr + v, IO::narrow(o));
+            }
         }
-        const float part = sum_squares<IO, VPL>(xv);
-        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-        if constexpr (WPR == 1) {
-            load_floats<E>(a.cos_tab + pos * a.half + toff, c);
-            load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
-        }
-        // the partner term enters with -sin in the first half, +sin in the second
-#pragma unroll
-        for (int e = 0; e < E; ++e) ss[e] *= sgn;
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int v = k * L + ln.t;
-            const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
-            keep_packed(xv[k]);
-            keep_packed(wv[k]);
-            float own[E], g[E], par[E], o[E];
-            IO::widen(xv[k], own);
-            IO::widen(wv[k], g);
-#pragma unroll
-            for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
-            // the partner lane's normalised values, exact binary32 bits
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                par[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, own[e])));
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + par[e] * ss[e];
-            if (in) store_stream(yr + v, IO::narrow(o));
-        }
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -333,7 +335,7 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 //    fixed register.
 // The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot;
 // the wavefront reads the position's table rows once and the lanes take
-// their slices from each other (TableChunks).
+// their slices through LDS (TableLds).
 // ---------------------------------------------------------------------------
 template <typename IO, int VPL, int WPR, bool ODD>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
@@ -402,11 +404,14 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
         // (vph chunks of G floats per table) and handed out after the
         // reduction: lane l needs the chunks at columns col0 and col1
         float c[E], ss[E];
-        TableChunks<G> tabs;
+        // (a.half / G = vph <= 32 chunks per table)
+        TableLds<G, Layout<WPR>::kThreads / kWave, kWave / 2> tabs(ln.slot * WPR + ln.wave_in_row);
         tabs.fetch(a.cos_tab + pos * a.half, a.sin_tab + pos * a.half, l, a.half / G);
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
-        tabs.gather(col0, col1, c, ss);
+        tabs.share(l, a.half / G);
+        tabs.take(col0, c, ss);
+        tabs.take(col1, c + G, ss + G);
 #pragma unroll
         for (int e = 0; e < G; ++e) {
             ss[e] *= sg0;
@@ -593,7 +598,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         float c[NT][NP], sn[NT][NP];
         constexpr bool kGather = !SHARED && WPR == 1;
         const bool gathered = kGather && vph <= kWave;
-        TableChunks<NP> tabs;
+        TableLds<NP, Layout<WPR>::kThreads / kWave, kWave> tabs(ln.slot * WPR + ln.wave_in_row);
         if constexpr (kGather) {
             if (gathered) tabs.fetch(crow, srow, ln.lane, vph);
         }
@@ -601,7 +606,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
 #pragma unroll
             for (int k = 0; k < NT; ++k) {
                 if (gathered) {
-                    tabs.gather1(toff[k], c[k], sn[k]);
+                    tabs.take(toff[k], c[k], sn[k]);
                 } else {
                     load_floats<NP>(crow + toff[k], c[k]);
                     load_floats<NP>(srow + toff[k], sn[k]);
@@ -613,6 +618,9 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         }
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        if constexpr (kGather) {
+            if (gathered) tabs.share(ln.lane, vph);
+        }
         if (WPR == 1 || gathered) load_tables();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -621,7 +629,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
             if constexpr (!SHARED && !kAll) {
                 if (k > 0) {
                     if (gathered) {
-                        tabs.gather1(toff[k], c[0], sn[0]);
+                        tabs.take(toff[k], c[0], sn[0]);
                     } else {
                         load_floats<NP>(crow + toff[k], c[0]);
                         load_floats<NP>(srow + toff[k], sn[0]);
