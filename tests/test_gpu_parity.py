@@ -169,7 +169,8 @@ def test_workload_full_size_lowp(name, dtype):
         assert rep["n_exact"] >= 0.99 * rep["n"]
     elif not (cfg.rope or cfg.adaln):
         # binary32 out, no cancelling sum: a few units of the last place
-        assert rep["max_ulp"] <= 64
+        # (4 measured; the rule allows 16 units of 2^-24 relative)
+        assert rep["max_ulp"] <= 16
     if dtype == "f16":
         # 16-bit outputs: only strongly cancelled outputs need the floor
         assert rep["n_floor_bound"] <= 1e-4 * rep["n"]
