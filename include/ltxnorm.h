@@ -176,8 +176,8 @@ LTXNORM_API ltxnorm_status ltxnorm_rmsnorm_rope_interleaved_fwd_dt(
     ltxnorm_dtype dtype, hipStream_t stream);
 
 /*
- * RMSNorm with per-sample adaptive modulation (AdaLN, as used in DiT blocks
- * for conditioning): Hugging Face cuda-kernels skill page, section
+ * RMSNorm with per-sample adaptive modulation (AdaLN, the conditioning step
+ * of a DiT block): Hugging Face cuda-kernels skill page, section
  * "Kernel-Specific Guidelines", AdaLN, gives norm(x) * weight * (1 + scale)
  * + shift.  Computed as
  *     y[r, j] = ((x[r, j] * rstd_r) * w[j]) * (1 + scale[b, j]) + shift[b, j]

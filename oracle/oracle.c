@@ -41,8 +41,8 @@
  *
  *  - RMSNorm with adaptive modulation (AdaLN).  The skill page (section
  *    "Kernel-Specific Guidelines", item AdaLN) gives the formula
- *    norm(x) * weight * (1 + scale) + shift, used in DiT blocks for
- *    conditioning.  Read with per-sample scale and shift rows: row r of x
+ *    norm(x) * weight * (1 + scale) + shift, the conditioning step of a
+ *    DiT block.  Read with per-sample scale and shift rows: row r of x
  *    belongs to sample b = r / rows_per_sample and uses scale[b, :] and
  *    shift[b, :]; norm(x) * weight is the RMSNorm above.  One rounding.
  *
