@@ -84,13 +84,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 KERNEL_SOURCES = (sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.hip")))
                   + sorted(glob.glob(os.path.join(ROOT, "rmsnorm_video_dit_amd", "csrc", "*.h"))))
 DTYPE_CODE = {"bf16": 0, "f16": 1, "f32": 2}
-PROBES = {"rms": datagen.HEADLINE, "rms_f16": datagen.HEADLINE, "rms_f32": datagen.HEADLINE,
-          "rope": datagen.ROPE, "ropei": datagen.ROPE_INTERLEAVED, "adaln": datagen.ADALN,
-          "rms_odd": "rms_4x4096x3076", "rope_d72": "rope_2x4096x1152_h16d72",
-          "rms_long": "rms_1x256x262144", "rms_short": "rms_2x4096x24_d128",
-          "adaln_seg": "adaln_8x4096x1152",
-          "rope_large": "rope_4x4096x3072_h24d128", "ropei_large": "ropei_4x4096x3072_h24d128",
-          "adaln_large": "adaln_4x4096x3072"}
+# --probe names: workload and I/O dtype of each benchmark line
+PROBES = {"rms": (datagen.HEADLINE, "bf16"), "rms_f16": (datagen.HEADLINE, "f16"),
+          "rms_f32": (datagen.HEADLINE, "f32"), "rope": (datagen.ROPE, "bf16"),
+          "ropei": (datagen.ROPE_INTERLEAVED, "bf16"), "adaln": (datagen.ADALN, "bf16"),
+          "rope_f16": (datagen.ROPE, "f16"), "rope_f32": (datagen.ROPE, "f32"),
+          "adaln_f32": (datagen.ADALN, "f32"),
+          "rms_odd": ("rms_4x4096x3076", "bf16"), "rope_d72": ("rope_2x4096x1152_h16d72", "bf16"),
+          "rms_long": ("rms_1x256x262144", "bf16"), "rms_short": ("rms_2x4096x24_d128", "bf16"),
+          "adaln_seg": ("adaln_8x4096x1152", "bf16"),
+          "rope_large": ("rope_4x4096x3072_h24d128", "bf16"),
+          "ropei_large": ("ropei_4x4096x3072_h24d128", "bf16"),
+          "adaln_large": ("adaln_4x4096x3072", "bf16")}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 ALL_CONFIGS = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS, **datagen.LARGE_CONFIGS}
 
@@ -528,8 +533,8 @@ def probe(kind: str, launches: int):
         print(json.dumps({"probe": kind, "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "launches": launches}), flush=True)
         return
-    cfg = ALL_CONFIGS[PROBES.get(kind, kind)]
-    dtype = kind[4:] if kind in ("rms_f16", "rms_f32") else "bf16"
+    name, dtype = PROBES.get(kind, (kind, "bf16"))
+    cfg = ALL_CONFIGS[name]
     wl = Workload(cfg, dev, s, dtype=dtype)
     for i in range(launches):
         wl.step(i)

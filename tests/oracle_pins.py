@@ -549,6 +549,49 @@ def pin_bf16_rounding(o):
     assert np.array_equal(got[inf], (bits[inf] >> 16).astype(np.uint16))
 
 
+_FORK_ORACLE = None  # the oracle under test, inherited by forked workers
+
+
+def _bf16_block_mismatches(block) -> int:
+    """Mismatches of the oracle's bf16 rounding against the neighbour-distance
+    formulation over every binary32 pattern whose upper 16 bits lie in
+    [u0, u1): all 2^16 dropped-bit patterns of each.  NaN patterns must give a
+    quiet NaN of the same sign, infinities themselves."""
+    u0, u1 = block
+    o = _FORK_ORACLE
+    uppers = np.arange(u0, u1, dtype=np.uint32)
+    lows = np.arange(1 << 16, dtype=np.uint32)
+    bits = ((uppers[:, None] << 16) | lows[None, :]).reshape(-1)
+    f = bits.view(np.float32)
+    got = o.bf16_from_f32(f)
+    finite = np.isfinite(f)
+    bad = int(np.count_nonzero(got[finite] != _bf16_nearest_reference(f[finite])))
+    nan = np.isnan(f)
+    g = got[nan]
+    bad += int(np.count_nonzero(((g & 0x7F80) != 0x7F80) | ((g & 0x0040) == 0)
+                                | (np.signbit(f[nan]) != ((g & 0x8000) != 0))))
+    inf = np.isinf(f)
+    bad += int(np.count_nonzero(got[inf] != (bits[inf] >> 16).astype(np.uint16)))
+    return bad
+
+
+def pin_bf16_rounding_exhaustive(o):
+    """Every one of the 2^32 binary32 bit patterns: the oracle's bf16 rounding
+    equals the neighbour-distance formulation (finite values), NaN stays a
+    quiet NaN of the same sign, +-Inf stays +-Inf.  Blocks of 128 upper
+    halves (8 M patterns) run in a pool of forked worker processes."""
+    import multiprocessing as mp
+    import os
+    global _FORK_ORACLE
+    _FORK_ORACLE = o
+    step = 128
+    blocks = [(u, u + step) for u in range(0, 1 << 16, step)]
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with mp.get_context("fork").Pool(workers) as pool:
+        bad = sum(pool.map(_bf16_block_mismatches, blocks, chunksize=4))
+    assert bad == 0, f"{bad} binary32 patterns round differently"
+
+
 def pin_round_twice(o):
     """oracle_round: binary32 of the double, then its bf16 (hand-worked cases
     across a tie, a carry into the exponent, and a negative value)."""
@@ -673,4 +716,5 @@ PINS = [
     pin_bf16_rounding, pin_round_twice,
     pin_f16_decode_all_patterns, pin_f16_encode, pin_lowp_constant_rows, pin_lowp_brute_force,
     pin_lowp_rope_matches_widened_bf16_path,
+    pin_bf16_rounding_exhaustive,
 ]
