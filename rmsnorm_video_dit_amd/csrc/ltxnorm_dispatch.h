@@ -213,9 +213,33 @@ ltxnorm_status launch_short(int lanes, int per, const KArgs& a, hipStream_t stre
     return launch(fn, kWave * kShortWavesPerBlock, kShortWavesPerBlock * (kWave / lanes), a, 0, stream);
 }
 
+// Long rows in chunks: partial sums, then every chunk but the first, then
+// the first chunk of every row (whose output holds the staged partials).
+template <typename IO, GOp OP>
+ltxnorm_status launch_split(const Choice& c, const KArgs& a, hipStream_t stream) {
+    if constexpr (OP == GOp::kRopeHalf) {
+        return LTXNORM_ERR_UNSUPPORTED;  // not chosen: rotate-half pairs span chunks
+    } else {
+        KArgs copy = a;
+        int chunks = c.chunks;
+        void* params[] = {&copy, &chunks};
+        const void* fns[3] = {(const void*)&rmsnorm_split_partial_kernel<IO>,
+                              (const void*)&rmsnorm_split_apply_kernel<IO, OP, false>,
+                              (const void*)&rmsnorm_split_apply_kernel<IO, OP, true>};
+        const int64_t grids[3] = {a.rows * chunks, a.rows * (chunks - 1), a.rows};
+        for (int i = 0; i < 3; ++i) {
+            const hipError_t e = hipLaunchKernel(fns[i], dim3((unsigned)grids[i]), dim3(kSplitThreads),
+                                                 params, 0, stream);
+            if (e != hipSuccess) return LTXNORM_ERR_HIP;
+        }
+        return LTXNORM_OK;
+    }
+}
+
 template <typename IO, GOp OP>
 ltxnorm_status launch_general(const Choice& c, const KArgs& a, hipStream_t stream) {
     if (c.kernel == Kernel::kLong) return launch_long<IO, OP>(a, stream);
+    if (c.kernel == Kernel::kSplit) return launch_split<IO, OP>(c, a, stream);
     return by_plan<GeneralL<IO, OP>, 4, 2, kMaxGeneralVecPerLane>(c.plan, a, stream,
                                                                   (size_t)c.lds_per_row);
 }
@@ -257,6 +281,7 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
             return LTXNORM_ERR_UNSUPPORTED;
         case Kernel::kGeneral:
         case Kernel::kLong:
+        case Kernel::kSplit:
             switch (op) {
                 case Op::kRmsNorm: return launch_general<IO, GOp::kRms>(c, a, stream);
                 case Op::kAdaLN: return launch_general<IO, GOp::kAda>(c, a, stream);

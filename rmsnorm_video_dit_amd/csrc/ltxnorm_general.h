@@ -87,33 +87,48 @@ __device__ __forceinline__ void store_elems(void* base, int64_t start, const u32
     }
 }
 
-// Elements F .. F + kEpv - 1 of the 2 kEpv elements in words W[0..7].
+// Word I (a compile-time index) of the 8-word concatenation of lo and hi.
+template <int I>
+__device__ __forceinline__ uint32_t word8(const u32x4 lo, const u32x4 hi) {
+    if constexpr (I < 4)
+        return lo[I];
+    else
+        return hi[I - 4];
+}
+
+// Elements F .. F + kEpv - 1 of the 2 kEpv elements held in lo and hi.
 template <int ELEM_BYTES, int F>
-__device__ __forceinline__ u32x4 take(const uint32_t* W) {
+__device__ __forceinline__ u32x4 take(const u32x4 lo, const u32x4 hi) {
     constexpr int kByte = F * ELEM_BYTES;
     constexpr int o = kByte / 4;
-    u32x4 r;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        if constexpr (kByte % 4 == 0)
-            r[m] = W[o + m];
-        else
-            r[m] = (W[o + m] >> 16) | (W[o + m + 1] << 16);
+    if constexpr (kByte % 4 == 0) {
+        return u32x4{word8<o>(lo, hi), word8<o + 1>(lo, hi), word8<o + 2>(lo, hi), word8<o + 3>(lo, hi)};
+    } else {
+        return u32x4{(word8<o>(lo, hi) >> 16) | (word8<o + 1>(lo, hi) << 16),
+                     (word8<o + 1>(lo, hi) >> 16) | (word8<o + 2>(lo, hi) << 16),
+                     (word8<o + 2>(lo, hi) >> 16) | (word8<o + 3>(lo, hi) << 16),
+                     (word8<o + 3>(lo, hi) >> 16) | (word8<o + 4>(lo, hi) << 16)};
     }
-    return r;
 }
 
 // The same for a shift f known only at run time but uniform across the
-// wavefront: a chain of uniform branches, each with compile-time indices (a
-// select over the words instead was turned into a runtime-indexed array in
-// private memory and measured 12 points of peak slower).
+// wavefront: a chain of uniform branches, each with compile-time word
+// indices and its result kept opaque (keep_packed), so that the optimiser
+// cannot merge the branches into one read of a runtime-indexed array, which
+// lands in private (scratch) memory: a select over the words written that
+// way measured 12 points of peak slower, and the merge also happened by
+// itself to the branch chain over a word array for binary32 rows.
 template <typename IO, int F = 1>
-__device__ __forceinline__ u32x4 take_at(const uint32_t* W, int f) {
+__device__ __forceinline__ u32x4 take_at(const u32x4 lo, const u32x4 hi, int f) {
     if constexpr (F >= IO::kEpv) {
-        return u32x4{W[0], W[1], W[2], W[3]};
+        return lo;
     } else {
-        if (f == F) return take<16 / IO::kEpv, F>(W);
-        return take_at<IO, F + 1>(W, f);
+        if (f == F) {
+            u32x4 r = take<16 / IO::kEpv, F>(lo, hi);
+            keep_packed(r);
+            return r;
+        }
+        return take_at<IO, F + 1>(lo, hi, f);
     }
 }
 
@@ -128,9 +143,7 @@ __device__ __forceinline__ u32x4 load_window(const void* base, int64_t start, in
     if (f == 0) {
         if (start >= 0 && start + E <= n) return v[c];
     } else if (c >= 0 && (c + 2) * E <= n) {
-        const u32x4 lo = v[c], hi = v[c + 1];
-        const uint32_t W[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return take_at<IO>(W, f);
+        return take_at<IO>(v[c], v[c + 1], f);
     }
     return load_elems<IO>(base, start, 0, n);
 }
@@ -246,8 +259,7 @@ __device__ __forceinline__ u32x4 weight_window(u32x4 lo, u32x4 hi, int f) {
     if (f == 0) return hi;
     keep_packed(lo);
     keep_packed(hi);
-    const uint32_t W[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return take_at<IO>(W, f);
+    return take_at<IO>(lo, hi, f);
 }
 
 // Interleaved RoPE on one normalised vector: pairs (2i, 2i + 1) of a head
@@ -458,12 +470,148 @@ rmsnorm_general_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Rows beyond the register budget: helpers shared by the two-pass kernel and
+// the split kernels.
+// ---------------------------------------------------------------------------
+
+// A row's place in the global vector grid of x (and of out).
+template <int E>
+struct RowSpan {
+    int64_t s;  // the row's first element
+    int first;  // its place in its vector
+    int64_t g0; // that vector
+    int nch;    // vectors the row touches
+    int fw;     // (-first) mod E: the shift of the row's weight windows
+    __device__ __forceinline__ RowSpan(int64_t row, int H)
+        : s(row * H), first((int)(s & (E - 1))), g0(s / E), nch((first + H + E - 1) / E),
+          fw((-first) & (E - 1)) {}
+};
+
+// U vectors of a row, row-relative vectors q0 + u * stride + t: loads issued
+// before any use (the pattern of the one-pass kernel), whole vectors first,
+// then the tensor's final partial vector under a uniform branch, then the
+// neighbouring rows' elements zeroed.  Vectors past the row are zero.
+template <typename IO, int U>
+__device__ __forceinline__ void load_span(const KArgs& a, const RowSpan<IO::kEpv>& r, int64_t whole,
+                                          int q0, int stride, int t, u32x4* v) {
+    constexpr int E = IO::kEpv;
+    const int H = a.hidden;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * stride + t;
+        const bool in = q < r.nch && r.g0 + q < whole;
+        const u32x4* p = static_cast<const u32x4*>(a.x) + r.g0 + q;
+        v[u] = in ? *p : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (r.s + H > whole * E) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * stride + t;
+            if (q < r.nch && r.g0 + q >= whole) v[u] = load_elems<IO>(a.x, (r.g0 + q) * E, r.s, r.s + H);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j0 = (q0 + u * stride + t) * E - r.first;
+        const int lo = j0 < 0 ? -j0 : 0;
+        const int hi = H - j0 >= E ? E : (H - j0 > 0 ? H - j0 : 0);
+        v[u] = keep_range<IO>(v[u], lo, hi);
+    }
+}
+
+// Normalise U vectors of row `row` (as load_span places them), apply the
+// AdaLN modulation or the interleaved rotation, and store them: every
+// operation but rotate-half, whose pairs are half a head apart.
+template <typename IO, GOp OP, int U>
+__device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEpv>& r, int64_t row,
+                                           int64_t whole, int q0, int stride, int t, float rstd) {
+    static_assert(OP != GOp::kRopeHalf, "rotate-half pairs are not element-wise");
+    constexpr int E = IO::kEpv;
+    const int H = a.hidden;
+    const int64_t msample = OP == GOp::kAda ? (row / a.rows_per_sample) * H : 0;
+    const int fm = (int)((msample - r.first) & (E - 1));
+    const float* crow = nullptr;
+    const float* srow = nullptr;
+    if constexpr (OP == GOp::kRopeIl) {
+        const int64_t pos = row % a.seq_len;
+        crow = a.cos_tab + pos * a.half;
+        srow = a.sin_tab + pos * a.half;
+    }
+    const int wfull = H / E;  // whole weight chunks
+    u32x4 v[U], wl[U], wh[U];
+    load_span<IO, U>(a, r, whole, q0, stride, t, v);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * stride + t;
+        wl[u] = whole_weight_chunk<IO>(a.w, q - 1, H);
+        wh[u] = whole_weight_chunk<IO>(a.w, q, H);
+    }
+    if (a.w != nullptr && wfull * E != H && q0 + stride * (U - 1) + stride > wfull) {
+        // windows reaching the weight's partial last chunk
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * stride + t;
+            if (q - 1 == wfull) wl[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
+            if (q == wfull) wh[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * stride + t;
+        if (q < r.nch) {
+            const int j0 = q * E - r.first;
+            float f[E], g[E];
+            IO::widen(v[u], f);
+            IO::widen(weight_window<IO>(wl[u], wh[u], r.fw), g);
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
+            if constexpr (OP == GOp::kAda) {
+                float sc[E], sh[E];
+                const u32x4 sv = a.scale ? load_window<IO>(a.scale, msample + j0, fm, a.mod_elems)
+                                         : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 hv = a.shift ? load_window<IO>(a.shift, msample + j0, fm, a.mod_elems)
+                                         : splat(IO::kNegZero);
+                IO::widen(sv, sc);
+                IO::widen(hv, sh);
+#pragma unroll
+                for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+            }
+            if constexpr (OP == GOp::kRopeIl) {
+                float o[E];
+                rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
+                store_row_vec<IO>(a.out, r.g0, q, j0, H, IO::narrow(o));
+            } else {
+                store_row_vec<IO>(a.out, r.g0, q, j0, H, IO::narrow(f));
+            }
+        }
+    }
+}
+
+// Long rows are summed in chunks of kSplitChunk vectors, the same way by the
+// two-pass kernel and the split kernels, so a row's rstd has the same bits
+// whichever of them a call takes (in place or not).  A chunk: 256 threads,
+// thread t adds the squares of vectors k * 256 + t (k = 0..7, in order), then
+// the wavefront tree, then the 4 wavefronts' sums in order.  The row: lane l
+// adds chunk sums l, l + 64, l + 128, ... in order, then the wavefront tree.
+// At most 8 terms per lane chain, 33 per partial chain, two 6-level trees.
+constexpr int kSplitThreads = 256;
+constexpr int kSplitVpt = 8;                                // vectors per thread and chunk
+constexpr int kSplitChunk = kSplitThreads * kSplitVpt;      // vectors per chunk
+constexpr int kSplitMaxChunks = kSplitMaxChunkCount;        // partials a wavefront reads at once
+static_assert(kSplitChunk == kSplitChunkVectors, "chunk size shared with the host");
+// chunks of the longest row (2^24 elements, 4 per vector, starting inside a vector)
+constexpr int kLongMaxChunks = ((1 << 22) + 1 + kSplitChunk - 1) / kSplitChunk;
+constexpr int kLongGroups = kLongThreads / kSplitThreads;  // chunks summed at once
+
+// ---------------------------------------------------------------------------
 // Two-pass kernel for rows beyond the register budget: one row per
-// 1024-thread workgroup.  Pass 1 streams the row for its sum of squares;
-// pass 2 reads it again, normalises and stores.  Both passes load x through
-// the caches: at [256 x 262144] bf16, pass 2 with non-temporal loads
-// measured 69.8 us against 68.1 us cached, and non-temporal loads in both
-// passes 75.9 us.
+// 1024-thread workgroup.  Pass 1 streams the row for its sum of squares, four
+// chunks at a time (one per group of 256 threads); pass 2 reads it again,
+// normalises and stores.  Both passes load x through the caches: at
+// [256 x 262144] bf16, pass 2 with non-temporal loads measured 69.8 us
+// against 68.1 us cached, and non-temporal loads in both passes 75.9 us.
+// The library takes it for calls in place and for rotate-half pairs; the
+// split kernels below take the other long rows.
 // ---------------------------------------------------------------------------
 template <typename IO, GOp OP>
 __global__ void __launch_bounds__(kLongThreads)
@@ -471,138 +619,52 @@ rmsnorm_long_kernel(const KArgs a) {
     constexpr int E = IO::kEpv;
     constexpr int T = kLongThreads;
     constexpr int U = kLongUnroll<IO>;
-    __shared__ float partials[2][kLongWaves];
+    __shared__ float wsums[2][kLongWaves];
+    __shared__ float chunk_sums[kLongMaxChunks];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int group = wave / (kSplitThreads / kWave), gt = tid % kSplitThreads;
+    const int lane = tid & (kWave - 1);
     const int H = a.hidden;
     const int64_t whole = a.rows * (int64_t)H / E;  // whole vectors in x
 
-    int parity = 0;
-    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
-        const int64_t s = row * H;
-        const int first = (int)(s & (E - 1));
-        const int64_t g0 = s / E;
-        const int nch = (first + H + E - 1) / E;
-        const int fw = (-first) & (E - 1);
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const RowSpan<E> r(row, H);
 
-        // U row vectors from q0, loads issued before any use (the pattern of
-        // the one-pass kernel): whole vectors, then the tensor's final
-        // partial vector under a uniform branch, then the neighbouring rows'
-        // elements zeroed.
-        auto load_vecs = [&](int q0, u32x4* v) {
+        // pass 1: the chunk sums, four chunks at a time (a group's chunk past
+        // the row is all zeros and is not recorded)
+        const int chunks = (r.nch + kSplitChunk - 1) / kSplitChunk;
+        for (int c0 = 0, it = 0; c0 < chunks; c0 += kLongGroups, ++it) {
+            const int c = c0 + group;
+            u32x4 v[kSplitVpt];
+            load_span<IO, kSplitVpt>(a, r, whole, c * kSplitChunk, kSplitThreads, gt, v);
+            const float s = wave_sum(sum_squares<IO, kSplitVpt>(v));
+            if (lane == 0) wsums[it & 1][wave] = s;
+            __syncthreads();
+            if (gt == 0 && c < chunks) {
+                float t = 0.0f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = q0 + u * T + tid;
-                const bool in = q < nch && g0 + q < whole;
-                const u32x4* p = static_cast<const u32x4*>(a.x) + g0 + q;
-                v[u] = in ? *p : u32x4{0u, 0u, 0u, 0u};
+                for (int i = 0; i < kSplitThreads / kWave; ++i) t += wsums[it & 1][group * (kSplitThreads / kWave) + i];
+                chunk_sums[c] = t;
             }
-            if (s + H > whole * E) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int q = q0 + u * T + tid;
-                    if (q < nch && g0 + q >= whole) v[u] = load_elems<IO>(a.x, (g0 + q) * E, s, s + H);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j0 = (q0 + u * T + tid) * E - first;
-                const int lo = j0 < 0 ? -j0 : 0;
-                const int hi = H - j0 >= E ? E : (H - j0 > 0 ? H - j0 : 0);
-                v[u] = keep_range<IO>(v[u], lo, hi);
-            }
-        };
-
-        // pass 1: sum of squares, U vectors in flight per thread.  Each
-        // chunk's sum enters a compensated (Neumaier) running sum: a row of
-        // up to 2^24 elements gives a thread thousands of chunks, and the
-        // plain running sum's error would grow with their number, while this
-        // one stays within a few roundings (the terms are non-negative).
-        float part = 0.0f, comp = 0.0f;
-        for (int q0 = 0; q0 < nch; q0 += T * U) {
-            u32x4 v[U];
-            load_vecs(q0, v);
-            const float c = sum_squares<IO, U>(v);
-            const float t = part + c;
-            comp += part >= c ? (part - t) + c : (c - t) + part;
-            part = t;
         }
-        part += comp;
-        float sum = wave_sum(part);
-        if ((tid & (kWave - 1)) == 0) partials[parity][wave] = sum;
         __syncthreads();
-        sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kLongWaves; ++i) sum += partials[parity][i];
-        const float rstd = rstd_of(sum, a.hidden_f, a.eps);
-
-        const float* crow = nullptr;
-        const float* srow = nullptr;
-        if constexpr (OP == GOp::kRopeIl || OP == GOp::kRopeHalf) {
-            const int64_t pos = row % a.seq_len;
-            crow = a.cos_tab + pos * a.half;
-            srow = a.sin_tab + pos * a.half;
-        }
+        // the row total, as the split kernels add it
+        float t = 0.0f;
+        for (int i = lane; i < chunks; i += kWave) t += chunk_sums[i];
+        const float rstd = rstd_of(wave_sum(t), a.hidden_f, a.eps);
 
         if constexpr (OP != GOp::kRopeHalf) {
             // pass 2: vectors in the row's vector grid
-            const int64_t msample = OP == GOp::kAda ? (row / a.rows_per_sample) * H : 0;
-            const int fm = (int)((msample - first) & (E - 1));
-            const int wfull = H / E;  // whole weight chunks
-            for (int q0 = 0; q0 < nch; q0 += T * U) {
-                u32x4 v[U], wl[U], wh[U];
-                load_vecs(q0, v);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int q = q0 + u * T + tid;
-                    wl[u] = whole_weight_chunk<IO>(a.w, q - 1, H);
-                    wh[u] = whole_weight_chunk<IO>(a.w, q, H);
-                }
-                if (a.w != nullptr && wfull * E != H && q0 + T * U > wfull) {
-                    // windows reaching the weight's partial last chunk
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int q = q0 + u * T + tid;
-                        if (q - 1 == wfull) wl[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
-                        if (q == wfull) wh[u] = load_elems<IO>(a.w, (int64_t)wfull * E, 0, H);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int q = q0 + u * T + tid;
-                    if (q < nch) {
-                        const int j0 = q * E - first;
-                        float f[E], g[E];
-                        IO::widen(v[u], f);
-                        IO::widen(weight_window<IO>(wl[u], wh[u], fw), g);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
-                        if constexpr (OP == GOp::kAda) {
-                            float sc[E], sh[E];
-                            const u32x4 sv = a.scale ? load_window<IO>(a.scale, msample + j0, fm, a.mod_elems)
-                                                     : u32x4{0u, 0u, 0u, 0u};
-                            const u32x4 hv = a.shift ? load_window<IO>(a.shift, msample + j0, fm, a.mod_elems)
-                                                     : splat(IO::kNegZero);
-                            IO::widen(sv, sc);
-                            IO::widen(hv, sh);
-#pragma unroll
-                            for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
-                        }
-                        if constexpr (OP == GOp::kRopeIl) {
-                            float o[E];
-                            rope_interleaved_vec<E>(a, crow, srow, j0, f, o);
-                            store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(o));
-                        } else {
-                            store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(f));
-                        }
-                    }
-                }
-            }
+            for (int q0 = 0; q0 < r.nch; q0 += T * U) apply_span<IO, OP, U>(a, r, row, whole, q0, T, tid, rstd);
         } else {
             // pass 2, rotate-half: unit = window of up to E elements of a
             // head's first half (head h, columns i0 .. i0 + cnt) and its
             // partner window half a head later; one thread reads and writes
             // both, so in-place calls stay correct.
+            const int64_t pos = row % a.seq_len;
+            const float* crow = a.cos_tab + pos * a.half;
+            const float* srow = a.sin_tab + pos * a.half;
             const int d = a.head_dim, half = a.half;
             const int nw = (half + E - 1) / E;  // windows per half head
             const int64_t units = (int64_t)(H / d) * nw;
@@ -612,7 +674,7 @@ rmsnorm_long_kernel(const KArgs a) {
                 const int i0 = (int)(u - (int64_t)h * nw) * E;
                 const int cnt = half - i0 < E ? half - i0 : E;
                 const int ja = h * d + i0, jb = ja + half;
-                const int64_t ea = s + ja, eb = s + jb;
+                const int64_t ea = r.s + ja, eb = r.s + jb;
                 float xa[E], xb[E], ga[E], gb[E];
                 IO::widen(load_window<IO>(a.x, ea, (int)(ea & (E - 1)), total), xa);
                 IO::widen(load_window<IO>(a.x, eb, (int)(eb & (E - 1)), total), xb);
@@ -638,6 +700,94 @@ rmsnorm_long_kernel(const KArgs a) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split kernels for rows beyond the register budget, out of place: row r is
+// cut into chunks of kSplitChunk vectors of its vector grid, one 256-thread
+// workgroup per chunk, so a launch of few long rows still fills the GPU (the
+// two-pass kernel gives each row one workgroup: 64 rows of 2^20 elements
+// kept 64 of 256 CUs busy).  Three launches, no scratch memory and no wait
+// between workgroups:
+//  1. rmsnorm_split_partial_kernel: each chunk's sum of squares (a fixed
+//     tree) goes to the row's staging area, binary32 words at the start of
+//     the row's first whole output vector; it lies in chunk 0 of the output.
+//  2. rmsnorm_split_apply_kernel<..., false>: every chunk but chunk 0 adds
+//     the row's partials in a fixed order (every workgroup of the row gets
+//     the same bits), normalises its chunk and stores it.
+//  3. rmsnorm_split_apply_kernel<..., true>: chunk 0 of every row does the
+//     same, after all of its wavefronts have read the partials it then
+//     overwrites.
+// x is read twice, as in the two-pass kernel.  In place (out == x) the
+// staging area would overwrite x, so those calls take the two-pass kernel.
+// ---------------------------------------------------------------------------
+
+// The row's staging area: binary32 words from its first whole output vector.
+template <int E>
+__device__ __forceinline__ float* split_stage(void* out, const RowSpan<E>& r) {
+    return reinterpret_cast<float*>(static_cast<u32x4*>(out) + r.g0 + (r.first != 0 ? 1 : 0));
+}
+
+template <typename IO>
+__global__ void __launch_bounds__(kSplitThreads)
+rmsnorm_split_partial_kernel(const KArgs a, int chunks) {
+    constexpr int E = IO::kEpv;
+    __shared__ float wsum[kSplitThreads / kWave];
+    const int64_t b = blockIdx.x;
+    const int64_t row = b / chunks;
+    const int c = (int)(b - row * chunks);
+    const int64_t whole = a.rows * (int64_t)a.hidden / E;
+    const RowSpan<E> r(row, a.hidden);
+    u32x4 v[kSplitVpt];
+    load_span<IO, kSplitVpt>(a, r, whole, c * kSplitChunk, kSplitThreads, (int)threadIdx.x, v);
+    const float s = wave_sum(sum_squares<IO, kSplitVpt>(v));
+    if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kSplitThreads / kWave; ++i) t += wsum[i];
+        split_stage<E>(a.out, r)[c] = t;
+    }
+}
+
+template <typename IO, GOp OP, bool CHUNK0>
+__global__ void __launch_bounds__(kSplitThreads)
+rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
+    constexpr int E = IO::kEpv;
+    constexpr int U = kLongUnroll<IO>;
+    const int64_t b = blockIdx.x;
+    int64_t row;
+    int c;
+    if constexpr (CHUNK0) {
+        row = b;
+        c = 0;
+    } else {
+        row = b / (chunks - 1);
+        c = 1 + (int)(b - row * (chunks - 1));
+    }
+    const int64_t whole = a.rows * (int64_t)a.hidden / E;
+    const RowSpan<E> r(row, a.hidden);
+    // The row's sum of squares: lane l adds partials l, l + 64, ... in that
+    // order (all of them loaded first), then the wavefront tree.  Every
+    // wavefront of every workgroup of the row computes the same bits.
+    const float* stage = split_stage<E>(a.out, r);
+    const int lane = threadIdx.x & (kWave - 1);
+    float p[kSplitMaxChunks / kWave];
+#pragma unroll
+    for (int j = 0; j < kSplitMaxChunks / kWave; ++j) {
+        const int i = j * kWave + lane;
+        p[j] = i < chunks ? stage[i] : 0.0f;
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSplitMaxChunks / kWave; ++j) t += p[j];
+    const float rstd = rstd_of(wave_sum(t), a.hidden_f, a.eps);
+    if constexpr (CHUNK0) __syncthreads();  // every wavefront has read the partials
+#pragma unroll
+    for (int u0 = 0; u0 < kSplitVpt; u0 += U)
+        apply_span<IO, OP, U>(a, r, row, whole, c * kSplitChunk + u0 * kSplitThreads, kSplitThreads,
+                              (int)threadIdx.x, rstd);
 }
 
 }  // namespace

@@ -50,6 +50,13 @@ constexpr int64_t kMaxGeneralRowVectors = (int64_t)kMaxWavesPerRow * kWave * kMa
 // Dynamic LDS the rotate-half general kernel may take per workgroup.
 constexpr int64_t kMaxExchangeLds = 64 * 1024 - 256;
 constexpr int kLongThreads = 1024;        // two-pass kernel: one row per workgroup
+// Split kernels (rows beyond the register budget, out of place): chunks of
+// kSplitChunkVectors vectors of a row, one 256-thread workgroup each, at most
+// kSplitMaxChunkCount chunks per row (the partials a wavefront reads at once)
+// and at most 2^31 - 1 workgroups per launch; other long rows take the
+// two-pass kernel.
+constexpr int kSplitChunkVectors = 2048;
+constexpr int kSplitMaxChunkCount = 2048;
 
 // Samples (modulation rows) for `rows` rows of `rows_per_sample` each, the
 // last possibly partial: ceil(rows / rows_per_sample) without overflow for
@@ -134,7 +141,8 @@ enum class Kernel {
     kRopeInterleavedShared,  // rmsnorm_rope_interleaved_kernel, one table slice per row
     kShort,                  // rmsnorm_short_kernel (rows in segments of at most 32 lanes)
     kGeneral,                // rmsnorm_general_kernel (any row length)
-    kLong,                   // rmsnorm_long_kernel (two passes)
+    kLong,                   // rmsnorm_long_kernel (two passes, one workgroup per row)
+    kSplit,                  // rmsnorm_split_* kernels (long rows in chunks, three launches)
 };
 
 // Rows of at most kMaxShortVectors vectors can always take one vector per
@@ -150,6 +158,7 @@ struct Choice {
     Plan plan;            // one-pass kernels: row split; segmented rows: per = vectors per lane
     int64_t lds_per_row;  // dynamic LDS bytes per row slot (general rotate-half)
     int lanes_per_row;    // segmented rows: lanes per row (a power of two <= 32)
+    int chunks = 0;       // split kernels: chunks per row
 };
 
 inline int pow2_at_least(int64_t n) {
@@ -218,7 +227,16 @@ inline Choice choose(Op op, const Request& r, int E) {
     const bool gfits = touched <= kMaxGeneralRowVectors;
     const Plan gp = plan_for(touched, 4, 2);
     const Choice general{Kernel::kGeneral, gp, 0, 0};
-    const Choice two_pass{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0, 0};
+    // rows past the budget: in chunks over many workgroups when the call is
+    // out of place (the partial sums are staged in the row's own output) and
+    // the operation is element-wise after the norm; otherwise two passes in
+    // one workgroup per row
+    const bool in_place = r.out != nullptr && r.out == r.x;
+    const int64_t chunks = (touched + kSplitChunkVectors - 1) / kSplitChunkVectors;
+    const bool split = !in_place && op != Op::kRopeRotateHalf && chunks <= kSplitMaxChunkCount &&
+                       r.rows <= ((int64_t)1 << 31) / chunks - 1;
+    const Choice two_pass = split ? Choice{Kernel::kSplit, Plan{4, kSplitChunkVectors / 256, false}, 0, 0, (int)chunks}
+                                  : Choice{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0, 0};
     const int64_t nvec = H / E;
     const bool short_row = whole && nvec <= kMaxShortVectors;
     const Choice short_rows{Kernel::kShort, Plan{1, 1, false}, 0, short_row ? pow2_at_least(nvec) : 0};
@@ -302,6 +320,7 @@ inline const char* kernel_name(Kernel k) {
         case Kernel::kShort: return "rmsnorm_short_kernel";
         case Kernel::kGeneral: return "rmsnorm_general_kernel";
         case Kernel::kLong: return "rmsnorm_long_kernel";
+        case Kernel::kSplit: return "rmsnorm_split_kernels";
     }
     return "?";
 }

@@ -20,11 +20,12 @@ fp16 outputs use the same rule with the binary16 spacing 2^(floor(log2|v|)
 result, so the bound is the evaluation error itself: |gpu - ref32| <=
 F32_REL * (|ref32| + m) with F32_REL = 2^-20, 16 units of 2^-24.  The sum of
 squares is the only long chain: at most 32 binary32 terms per lane, a
-6-level tree and up to 16 cross-wavefront partials (a thread of the
-two-pass kernel adds its chunks with a compensated sum), so with
-round-to-nearest errors of either sign its relative error is a few units of
-2^-24; the square root halves it, and the scaling, rotation or modulation
-adds at most three roundings.  The largest error measured over full-size
+6-level tree and up to 16 cross-wavefront partials; rows beyond the
+register budget are summed in chunks of 2048 vectors (8 terms per lane, a
+tree, 4 partials) whose sums are added 33 at most per lane and by a second
+tree.  With round-to-nearest errors of either sign its relative error is a
+few units of 2^-24; the square root halves it, and the scaling, rotation or
+modulation adds at most three roundings.  The largest error measured over full-size
 workloads is 4 units (RMSNorm) and 3 units of |ref32| + m (RoPE, AdaLN), so
 the bound keeps a margin of four while an evaluation ten times less accurate
 fails.  This is the "1 bf16 ulp against the oracle's binary32 result rounded

@@ -330,9 +330,15 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_RMSNORM, 3076, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 4, 2),
     (ltx.OP_RMSNORM, 1, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
     (ltx.OP_ADALN, 3070, 0, 0, ltx.F32, "rmsnorm_general_kernel", 7, 2),
-    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
-    (ltx.OP_RMSNORM, 65529, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
-    (ltx.OP_RMSNORM, 32772, 0, 0, ltx.F32, "rmsnorm_long_kernel", None, None),
+    # (out of place: the split kernels; the describe line names the two-pass
+    # kernel that an in-place call takes)
+    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 5),
+    (ltx.OP_RMSNORM, 65529, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 4),
+    (ltx.OP_RMSNORM, 32772, 0, 0, ltx.F32, "rmsnorm_split_kernels", None, 5),
+    (ltx.OP_ADALN, 262144, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 16),
+    (ltx.OP_ROPE_INTERLEAVED, 1 << 24, 1024, 1 << 14, ltx.BF16, "rmsnorm_split_kernels", None, 1024),
+    (ltx.OP_RMSNORM, 1 << 24, 0, 0, ltx.F32, "rmsnorm_split_kernels", None, 2048),
+    (ltx.OP_RMSNORM, (1 << 24) - 1, 0, 0, ltx.F32, "rmsnorm_long_kernel", None, None),  # 2049 chunks
     # rotate-half: power-of-two half heads, head-packed lanes, pairs in a lane,
     # LDS exchange, two passes
     (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_xor_kernel", 1, 4),
@@ -410,8 +416,23 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
         assert int(f[per_key]) == per
         assert int(f["threads"]) == 64 * wpr * int(f["rows_per_block"])
         assert (f.get("grid") == "resident") == (name == "rmsnorm_general_kernel"), f
+    elif name == "rmsnorm_split_kernels":
+        E = 4 if dtype == ltx.F32 else 8
+        touched = hidden // E if hidden % E == 0 else (hidden + 2 * E - 2) // E
+        assert int(f["chunks_per_row"]) == per == -(-touched // 2048)
+        assert f["launches"] == "3" and f["vectors_per_chunk"] == "2048" and f["threads"] == "256"
+        assert f["in_place"] == "rmsnorm_long_kernel"
     else:
         assert f["passes"] == "2" and f["threads"] == "1024"
+
+
+def test_split_kernels_limit_the_grid():
+    """The split launches one workgroup per chunk of every row: a call whose
+    rows times chunks would pass 2^31 - 1 workgroups takes the two-pass
+    kernel instead."""
+    rows_ok = (1 << 31) // 5 - 1
+    assert _describe(ltx.OP_RMSNORM, 65544, rows=rows_ok)[0] == "rmsnorm_split_kernels"
+    assert _describe(ltx.OP_RMSNORM, 65544, rows=rows_ok + 1)[0] == "rmsnorm_long_kernel"
 
 
 def test_kernel_choice_lds_and_limits():
@@ -443,7 +464,7 @@ def test_kernel_choice_covers_the_benchmark_workloads():
               "ropei_2x4096x2048_h32d64": "rmsnorm_rope_interleaved_kernel(shared)",
               "adaln_2x4096x2048": "rmsnorm_adaln_kernel", "rms_4x4096x3076": "rmsnorm_general_kernel",
               "rope_2x4096x1152_h16d72": "rmsnorm_rope_packed_kernel(odd)",
-              "rms_1x256x262144": "rmsnorm_long_kernel"}
+              "rms_1x256x262144": "rmsnorm_split_kernels"}
     for name, kernel in expect.items():
         cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[name]
         op = (ltx.OP_ADALN if cfg.adaln else ltx.OP_ROPE_INTERLEAVED if cfg.interleaved
@@ -479,6 +500,11 @@ def test_kernel_choice_always_covers_the_row():
         touched = H // E if whole else (H + 2 * E - 2) // E
         if name == "rmsnorm_long_kernel":
             assert f["threads"] == "1024"
+            assert op == ltx.OP_ROPE or -(-touched // 2048) > 2048 or rows * -(-touched // 2048) >= 2 ** 31, desc
+            continue
+        if name == "rmsnorm_split_kernels":
+            assert op != ltx.OP_ROPE and int(f["chunks_per_row"]) == -(-touched // 2048) <= 2048, desc
+            assert touched > 64 * 16 * 5, desc  # past the general kernel's budget
             continue
         if name == "rmsnorm_short_kernel":
             lanes, per, n = int(f["lanes_per_row"]), int(f["vectors_per_lane"]), H // E
@@ -546,4 +572,5 @@ def test_kernel_choice_always_covers_the_row():
     assert {"rmsnorm_kernel", "rmsnorm_adaln_kernel", "rmsnorm_rope_xor_kernel",
             "rmsnorm_rope_packed_kernel", "rmsnorm_rope_packed_kernel(odd)", "rmsnorm_rope_pair_kernel",
             "rmsnorm_rope_interleaved_kernel", "rmsnorm_rope_interleaved_kernel(shared)",
-            "rmsnorm_general_kernel", "rmsnorm_long_kernel", "rmsnorm_short_kernel"} <= seen, seen
+            "rmsnorm_general_kernel", "rmsnorm_long_kernel", "rmsnorm_split_kernels",
+            "rmsnorm_short_kernel"} <= seen, seen

@@ -174,6 +174,42 @@ def test_paths_invariants(op, hidden, d):
     assert np.array_equal(b[pad: pad + rows * hidden].reshape(rows, hidden), ref)
 
 
+# Long rows out of place take the split kernels: chunks of 2048 vectors over
+# many workgroups, the partial sums staged in the row's own output.  In place
+# they take the two-pass kernel.  Both add a row's squares in the same order.
+SPLIT = [("bf16", 65544, 300), ("bf16", 1 << 20, 5), ("bf16", 70001, 37), ("f32", 40001, 64),
+         ("f16", 262147, 9), ("bf16", 3 * 65536 + 2, 1)]
+
+
+@pytest.mark.parametrize("dtype,hidden,rows", SPLIT)
+def test_split_rows(dtype, hidden, rows):
+    """Every element against the oracle (RMSNorm and AdaLN), x untouched by
+    the staging, and the in-place result (two-pass kernel) equal bit for bit."""
+    code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+    desc = ltx.ltxnorm_describe_launch(ltx.OP_RMSNORM, rows, hidden, 0, 0, code)
+    assert desc.startswith("rmsnorm_split_kernels"), desc
+    announce(f"split rows {dtype} {rows}x{hidden}")
+    seed = hidden + 7 * rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    got, rep = check_rms(x, w, label=f"split rms {dtype} {rows}x{hidden}")
+    if dtype != "f32":
+        assert rep["max_ulp"] <= 1.0
+    # in place: the two-pass kernel, the same bits
+    xt, wt = dev_bf16(x), dev_bf16(w)
+    yt = ltx.rmsnorm(xt, wt, 1e-6)
+    bits = (lambda a: np.asarray(a).view(np.uint16 if dtype != "f32" else np.uint32))
+    assert np.array_equal(bits(host_bits(xt)), bits(x))  # the staging area lives in the output
+    assert np.array_equal(bits(host_bits(yt)), bits(got))
+    ltx.rmsnorm(xt, wt, 1e-6, out=xt)
+    assert np.array_equal(bits(host_bits(xt)), bits(got))
+    rps = max(1, -(-rows // 3))
+    samples = -(-rows // rps)
+    sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    check_adaln(x, w, sc, sh, rps, label=f"split adaln {dtype} {rows}x{hidden}")
+
+
 def test_adaln_null_modulation_any_hidden():
     """NULL scale and shift give RMSNorm bit for bit on the general and
     two-pass kernels too."""
@@ -344,13 +380,15 @@ def test_max_hidden(op, dtype):
 # ---------------------------------------------------------------------------
 
 def test_graph_capture_replays():
-    """Capture one call of each operation (vector, head-packed, general and
-    two-pass kernels) into a graph; replay it three times with new inputs
-    written eagerly between replays; every replay equals the eager result."""
+    """Capture one call of each operation (vector, head-packed, general,
+    split and two-pass kernels) into a graph; replay it three times with new
+    inputs written eagerly between replays; every replay equals the eager
+    result."""
     announce("graph capture")
     shapes = [("rms", 512, 2048, 0), ("adaln", 512, 2048, 0), ("half", 512, 2048, 64),
               ("il", 512, 2048, 64), ("half", 512, 1152, 72), ("rms", 256, 3076, 0),
-              ("rms", 2, 70001, 0)]
+              ("rms", 2, 70001, 0), ("adaln", 4, 65544, 0), ("il", 3, 255 * 258, 258),
+              ("half", 2, 2 * 40000, 40000)]
     s = torch.cuda.Stream()
     bufs = []
     for op, rows, hidden, d in shapes:
