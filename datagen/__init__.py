@@ -235,6 +235,8 @@ GENERAL_CONFIGS = {
     # AdaLN at hidden 1152 (the PixArt size), rows of 144 vectors that
     # several rows share a wavefront for
     "adaln_8x4096x1152": Config("adaln_8x4096x1152", 16, 8, 4096, 1152, adaln_sigma=0.25),
+    # a few very long rows: 64 rows of 2^20, each cut into 64 chunks
+    "rms_1x64x1048576": Config("rms_1x64x1048576", 17, 1, 64, 1 << 20),
 }
 # The fused operations at the headline's size ([4 x 4096 x 3072]), large
 # enough that the launch floor no longer sets their rate: RoPE with 24 heads

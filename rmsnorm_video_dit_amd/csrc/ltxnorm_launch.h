@@ -52,11 +52,17 @@ constexpr int64_t kMaxExchangeLds = 64 * 1024 - 256;
 constexpr int kLongThreads = 1024;        // two-pass kernel: one row per workgroup
 // Split kernels (rows beyond the register budget, out of place): chunks of
 // kSplitChunkVectors vectors of a row, one 256-thread workgroup each, at most
-// kSplitMaxChunkCount chunks per row (the partials a wavefront reads at once)
-// and at most 2^31 - 1 workgroups per launch; other long rows take the
-// two-pass kernel.
+// kSplitMaxChunkCount chunks per row (the partials a wavefront reads at once).
+// The two-pass kernel gives a row one 1024-thread workgroup, which streams
+// at about 35 GB/s: it keeps HBM busy from about 192 rows on.  Below that,
+// rows of at least kSplitMinChunks chunks take the split, whose three
+// launches cost more than they gain on rows of fewer chunks (bf16, 96 rows
+// of 262144: 44.5 -> 35.6 us; 160 rows: 53.5 -> 50.7 us; 192 rows 53.6 ->
+// 57.2 us; 128 rows of 65544, five chunks: 16.5 -> 23.4 us).
 constexpr int kSplitChunkVectors = 2048;
 constexpr int kSplitMaxChunkCount = 2048;
+constexpr int kSplitMinChunks = 16;
+constexpr int64_t kSplitMaxRows = 191;
 
 // Samples (modulation rows) for `rows` rows of `rows_per_sample` each, the
 // last possibly partial: ceil(rows / rows_per_sample) without overflow for
@@ -227,14 +233,14 @@ inline Choice choose(Op op, const Request& r, int E) {
     const bool gfits = touched <= kMaxGeneralRowVectors;
     const Plan gp = plan_for(touched, 4, 2);
     const Choice general{Kernel::kGeneral, gp, 0, 0};
-    // rows past the budget: in chunks over many workgroups when the call is
-    // out of place (the partial sums are staged in the row's own output) and
-    // the operation is element-wise after the norm; otherwise two passes in
-    // one workgroup per row
+    // rows past the budget: two passes in one workgroup per row, or, for a
+    // few rows of many chunks, in chunks over many workgroups when the call
+    // is out of place (the partial sums are staged in the row's own output)
+    // and the operation is element-wise after the norm
     const bool in_place = r.out != nullptr && r.out == r.x;
     const int64_t chunks = (touched + kSplitChunkVectors - 1) / kSplitChunkVectors;
-    const bool split = !in_place && op != Op::kRopeRotateHalf && chunks <= kSplitMaxChunkCount &&
-                       r.rows <= ((int64_t)1 << 31) / chunks - 1;
+    const bool split = !in_place && op != Op::kRopeRotateHalf && r.rows <= kSplitMaxRows &&
+                       chunks >= kSplitMinChunks && chunks <= kSplitMaxChunkCount;
     const Choice two_pass = split ? Choice{Kernel::kSplit, Plan{4, kSplitChunkVectors / 256, false}, 0, 0, (int)chunks}
                                   : Choice{Kernel::kLong, Plan{kLongThreads / kWave, 0, false}, 0, 0};
     const int64_t nvec = H / E;

@@ -330,15 +330,10 @@ def _describe(op, hidden, heads=0, head_dim=0, dtype=ltx.BF16, rows=16384):
     (ltx.OP_RMSNORM, 3076, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 4, 2),
     (ltx.OP_RMSNORM, 1, 0, 0, ltx.BF16, "rmsnorm_general_kernel", 1, 1),
     (ltx.OP_ADALN, 3070, 0, 0, ltx.F32, "rmsnorm_general_kernel", 7, 2),
-    # (out of place: the split kernels; the describe line names the two-pass
-    # kernel that an in-place call takes)
-    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 5),
-    (ltx.OP_RMSNORM, 65529, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 4),
-    (ltx.OP_RMSNORM, 32772, 0, 0, ltx.F32, "rmsnorm_split_kernels", None, 5),
-    (ltx.OP_ADALN, 262144, 0, 0, ltx.BF16, "rmsnorm_split_kernels", None, 16),
-    (ltx.OP_ROPE_INTERLEAVED, 1 << 24, 1024, 1 << 14, ltx.BF16, "rmsnorm_split_kernels", None, 1024),
-    (ltx.OP_RMSNORM, 1 << 24, 0, 0, ltx.F32, "rmsnorm_split_kernels", None, 2048),
-    (ltx.OP_RMSNORM, (1 << 24) - 1, 0, 0, ltx.F32, "rmsnorm_long_kernel", None, None),  # 2049 chunks
+    # (16384 rows fill the GPU with one workgroup per row: two passes)
+    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
+    (ltx.OP_RMSNORM, 32772, 0, 0, ltx.F32, "rmsnorm_long_kernel", None, None),
+    (ltx.OP_ADALN, 262144, 0, 0, ltx.BF16, "rmsnorm_long_kernel", None, None),
     # rotate-half: power-of-two half heads, head-packed lanes, pairs in a lane,
     # LDS exchange, two passes
     (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, "rmsnorm_rope_xor_kernel", 1, 4),
@@ -426,13 +421,35 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
         assert f["passes"] == "2" and f["threads"] == "1024"
 
 
-def test_split_kernels_limit_the_grid():
-    """The split launches one workgroup per chunk of every row: a call whose
-    rows times chunks would pass 2^31 - 1 workgroups takes the two-pass
-    kernel instead."""
-    rows_ok = (1 << 31) // 5 - 1
-    assert _describe(ltx.OP_RMSNORM, 65544, rows=rows_ok)[0] == "rmsnorm_split_kernels"
-    assert _describe(ltx.OP_RMSNORM, 65544, rows=rows_ok + 1)[0] == "rmsnorm_long_kernel"
+@pytest.mark.parametrize("op,hidden,heads,head_dim,dtype,rows,chunks", [
+    # fewer than 192 rows of at least 16 chunks of 2048 vectors: the split
+    (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 191, 16),
+    (ltx.OP_RMSNORM, 245761, 0, 0, ltx.BF16, 1, 16),      # 30722 vectors touched
+    (ltx.OP_RMSNORM, 1 << 20, 0, 0, ltx.BF16, 64, 64),
+    (ltx.OP_RMSNORM, 131072, 0, 0, ltx.F32, 100, 16),
+    (ltx.OP_ADALN, 262144, 0, 0, ltx.F16, 7, 16),
+    (ltx.OP_ROPE_INTERLEAVED, 1 << 24, 1024, 1 << 14, ltx.BF16, 3, 1024),
+    (ltx.OP_RMSNORM, 1 << 24, 0, 0, ltx.F32, 1, 2048),
+    # otherwise two passes in one workgroup per row
+    (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 192, None),
+    (ltx.OP_RMSNORM, 245752, 0, 0, ltx.BF16, 1, None),     # 30719 vectors: 15 chunks
+    (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, 64, None),
+    (ltx.OP_RMSNORM, (1 << 24) - 1, 0, 0, ltx.F32, 1, None),  # 2049 chunks
+    (ltx.OP_ROPE, 1 << 20, 1024, 1024, ltx.BF16, 1, None),  # rotate-half
+])
+def test_kernel_choice_long_rows(op, hidden, heads, head_dim, dtype, rows, chunks):
+    """Rows past the register budget: chunks over many workgroups for a few
+    rows of many chunks, the two-pass kernel otherwise.  The describe line
+    of the split names the two-pass kernel an in-place call takes."""
+    name, f = _describe(op, hidden, heads, head_dim, dtype, rows=rows)
+    if chunks is None:
+        assert name == "rmsnorm_long_kernel"
+        assert f["passes"] == "2" and f["threads"] == "1024"
+    else:
+        assert name == "rmsnorm_split_kernels"
+        assert int(f["chunks_per_row"]) == chunks
+        assert f["launches"] == "3" and f["vectors_per_chunk"] == "2048" and f["threads"] == "256"
+        assert f["in_place"] == "rmsnorm_long_kernel"
 
 
 def test_kernel_choice_lds_and_limits():
@@ -464,7 +481,7 @@ def test_kernel_choice_covers_the_benchmark_workloads():
               "ropei_2x4096x2048_h32d64": "rmsnorm_rope_interleaved_kernel(shared)",
               "adaln_2x4096x2048": "rmsnorm_adaln_kernel", "rms_4x4096x3076": "rmsnorm_general_kernel",
               "rope_2x4096x1152_h16d72": "rmsnorm_rope_packed_kernel(odd)",
-              "rms_1x256x262144": "rmsnorm_split_kernels"}
+              "rms_1x256x262144": "rmsnorm_long_kernel", "rms_1x64x1048576": "rmsnorm_split_kernels"}
     for name, kernel in expect.items():
         cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[name]
         op = (ltx.OP_ADALN if cfg.adaln else ltx.OP_ROPE_INTERLEAVED if cfg.interleaved
@@ -490,21 +507,23 @@ def test_kernel_choice_always_covers_the_row():
             H = heads * d
         else:
             d = heads = 0
-            H = int(rng.choice([rng.integers(1, 9000), rng.integers(1, 80000), 8 * rng.integers(1, 9000)]))
-        rows = int(rng.integers(1, 5000))
+            H = int(rng.choice([rng.integers(1, 9000), rng.integers(1, 80000), 8 * rng.integers(1, 9000),
+                                rng.integers(1, 1 << 19)]))
+        rows = int(rng.choice([rng.integers(1, 5000), rng.integers(1, 300)]))
         desc = ltx.ltxnorm_describe_launch(op, rows, H, heads, d, dtype)
         name, *fields = desc.split()
         f = dict(x.split("=") for x in fields)
         seen.add(name)
         whole = H % E == 0
         touched = H // E if whole else (H + 2 * E - 2) // E
+        chunks = -(-touched // 2048)
         if name == "rmsnorm_long_kernel":
             assert f["threads"] == "1024"
-            assert op == ltx.OP_ROPE or -(-touched // 2048) > 2048 or rows * -(-touched // 2048) >= 2 ** 31, desc
+            assert op == ltx.OP_ROPE or not 16 <= chunks <= 2048 or rows >= 192, desc
             continue
         if name == "rmsnorm_split_kernels":
-            assert op != ltx.OP_ROPE and int(f["chunks_per_row"]) == -(-touched // 2048) <= 2048, desc
-            assert touched > 64 * 16 * 5, desc  # past the general kernel's budget
+            assert op != ltx.OP_ROPE and int(f["chunks_per_row"]) == chunks and 16 <= chunks <= 2048, desc
+            assert rows < 192, desc
             continue
         if name == "rmsnorm_short_kernel":
             lanes, per, n = int(f["lanes_per_row"]), int(f["vectors_per_lane"]), H // E
