@@ -123,9 +123,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
+def read_traffic_parts(kernel: str, workload: str):
+    """(fetched, written) HBM bytes per launch from the committed counter
+    summary, or None when there is none or the kernel sources changed since
+    it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     cur = source_hash()
@@ -136,8 +137,14 @@ def read_traffic(kernel: str, workload: str):
         if kv.get("kernel") == kernel and kv.get("workload") == workload:
             if kv.get("src_sha") != cur:
                 return None
-            return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+            return float(kv["fetch_bytes"]), float(kv["write_bytes"])
     return None
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (fetched + written), or None as above."""
+    parts = read_traffic_parts(kernel, workload)
+    return None if parts is None else parts[0] + parts[1]
 
 
 def to_device(a, dev):
@@ -618,6 +625,7 @@ def main():
                    "hidden": cfg.hidden, "io_dtype": "bf16", "eps": cfg.eps,
                    "bytes_per_step": cfg.algorithmic_bytes(), "rotating_sets": wl.nsets,
                    "seed": datagen.BASE_SEED, "x_fnv": datagen.fnv1a64(wl.host["x"]),
+                   "w_fnv": datagen.fnv1a64(wl.host["w"]),
                    "device": name},
         "dtype_note": "dtype is the arithmetic type (binary32 accumulation and scaling); the "
                       "tensors are bf16 (config.io_dtype)",
@@ -641,7 +649,10 @@ def main():
         line["copy_ceiling"] = ceil
         line["pct_of_copy_ceiling"] = round(100.0 * value / ceil["value"], 2)
     if traffic is not None:
+        fetched, written = read_traffic_parts("rmsnorm", cfg.name)
         line["roofline"]["traffic_bytes_per_launch"] = int(traffic)
+        line["roofline"]["fetch_bytes_per_launch"] = int(fetched)
+        line["roofline"]["write_bytes_per_launch"] = int(written)
     line["launch"] = ("one HIP graph of the K launches, replayed once per window"
                       if graph else "K launches issued one by one on the stream")
     line["graph_launch" if not graph else "stream_launch"] = other

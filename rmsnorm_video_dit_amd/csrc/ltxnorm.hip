@@ -243,8 +243,8 @@ LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, 
         std::snprintf(buf, len, "%s passes=2 rows_per_block=1 threads=%d lds_bytes=0", name,
                       ltxnorm_detail::kLongThreads);
     } else if (c.kernel == Kernel::kSplit) {
-        std::snprintf(buf, len, "%s launches=3 chunks_per_row=%d vectors_per_chunk=%d threads=256 lds_bytes=0 in_place=rmsnorm_long_kernel",
-                      name, c.chunks, ltxnorm_detail::kSplitChunkVectors);
+        std::snprintf(buf, len, "%s launches=3 chunks_per_row=%d vectors_per_chunk=%d slots_per_row=%d threads=256 lds_bytes=0 in_place=rmsnorm_long_kernel",
+                      name, c.chunks, ltxnorm_detail::kSplitChunkVectors, ltxnorm_detail::split_slots(c.chunks));
     } else {
         const int rpb = ltxnorm_detail::rows_per_block(c.plan.wpr);
         std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld%s",

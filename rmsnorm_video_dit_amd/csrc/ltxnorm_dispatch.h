@@ -226,7 +226,7 @@ ltxnorm_status launch_split(const Choice& c, const KArgs& a, hipStream_t stream)
         const void* fns[3] = {(const void*)&rmsnorm_split_partial_kernel<IO>,
                               (const void*)&rmsnorm_split_apply_kernel<IO, OP, false>,
                               (const void*)&rmsnorm_split_apply_kernel<IO, OP, true>};
-        const int64_t grids[3] = {a.rows * chunks, a.rows * (chunks - 1), a.rows};
+        const int64_t grids[3] = {a.rows * chunks, a.rows * split_slots(chunks), a.rows};
         for (int i = 0; i < 3; ++i) {
             const hipError_t e = hipLaunchKernel(fns[i], dim3((unsigned)grids[i]), dim3(kSplitThreads),
                                                  params, 0, stream);

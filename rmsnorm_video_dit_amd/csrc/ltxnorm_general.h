@@ -763,8 +763,15 @@ rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
         row = b;
         c = 0;
     } else {
-        row = b / (chunks - 1);
-        c = 1 + (int)(b - row * (chunks - 1));
+        // Row-major over the row's chunk slots (split_slots: padded to a
+        // multiple of the 8 XCDs where that keeps each chunk on one XCD at
+        // little cost); padding slots exit.  Ordering the grid chunk-major
+        // instead made concurrent workgroups read rows a power of two apart,
+        // and ran slower (64 rows of 2^20: 79.3 -> 81.9 us).
+        const int slots = split_slots(chunks);
+        row = b / slots;
+        c = 1 + (int)(b - row * slots);
+        if (c >= chunks) return;
     }
     const int64_t whole = a.rows * (int64_t)a.hidden / E;
     const RowSpan<E> r(row, a.hidden);

@@ -63,6 +63,19 @@ constexpr int kSplitChunkVectors = 2048;
 constexpr int kSplitMaxChunkCount = 2048;
 constexpr int kSplitMinChunks = 16;
 constexpr int64_t kSplitMaxRows = 191;
+// Workgroup slots per row in the split's second launch (chunks 1 and up).
+// Workgroups are dealt to the 8 XCDs in turn, so with the slot count a
+// multiple of 8 chunk c of every row runs on the same XCD and that XCD's L2
+// keeps its weight chunk: 64 rows of 2^20 (63 chunks here) fetched the 2 MB
+// weight about 25 times without the padding, and ran 79.3 -> 75.5 us with
+// it.  The padding also leaves one XCD with fewer chunks per row (15 chunks:
+// 2 on seven XCDs, 1 on the eighth, and 160 rows of 262144 ran 50.7 -> 52.3
+// us), so the count is padded only where that costs at most 2 %.
+constexpr __host__ __device__ int split_slots(int chunks) {
+    const int n = chunks - 1;
+    const int padded = (n + 7) & ~7;
+    return padded * 50 <= n * 51 ? padded : n;
+}
 
 // Samples (modulation rows) for `rows` rows of `rows_per_sample` each, the
 // last possibly partial: ceil(rows / rows_per_sample) without overflow for

@@ -82,10 +82,11 @@ def test_long_rows(dtype, hidden, rows):
 
 # (heads, head_dim): head sizes the vector kernels cannot pair, rows that are
 # not whole vectors; LONG_ROPE: long rows (head-packed for 129 x 136, the
-# two-pass kernel for the rest)
+# two-pass kernel for the rest, except interleaved pairs on rows of 16 chunks
+# of 2048 vectors or more: the split kernels, whole and ragged rows)
 ROPE_SHAPES = [(1, 2), (33, 2), (5, 6), (7, 10), (4, 24), (16, 72), (32, 40), (3, 130),
                (2, 136), (24, 88), (13, 14), (1, 1000), (9, 18), (20, 52)]
-LONG_ROPE = [(129, 136), (2, 40000), (1, 70002), (255, 258), (64, 1026)]
+LONG_ROPE = [(129, 136), (2, 40000), (1, 70002), (255, 258), (64, 1026), (1024, 256), (2, 122882)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -119,11 +120,12 @@ def test_long_rope(dtype, heads, head_dim, interleaved):
 
 # one shape per path: general RMSNorm/AdaLN, general rotate-half (LDS),
 # general interleaved, two-pass RMSNorm/AdaLN, two-pass rotate-half and
-# interleaved
+# interleaved, split RMSNorm/AdaLN/interleaved (in place: two-pass)
 PATHS = [
     ("rms", 3076, 0), ("adaln", 3070, 0), ("half", 16 * 72, 72), ("il", 7 * 10, 10),
     ("rms", 70001, 0), ("adaln", 65544, 0), ("half", 129 * 136, 136), ("il", 255 * 258, 258),
     ("half", 2 * 40000, 40000),
+    ("rms", 262147, 0), ("adaln", 262144, 0), ("il", 1024 * 256, 256),
 ]
 
 

@@ -56,6 +56,7 @@ def test_traffic_file_is_bound_to_the_kernel_sources(tmp_path, monkeypatch):
                  f"kernel=other workload=w src_sha=0000 fetch_bytes=1 write_bytes=1\n")
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.read_traffic("rmsnorm", "w") == 15.0
+    assert bench.read_traffic_parts("rmsnorm", "w") == (10.0, 5.0)
     assert bench.read_traffic("other", "w") is None      # stale: sources changed since
     assert bench.read_traffic("missing", "w") is None
 
