@@ -541,10 +541,13 @@ __device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEp
     u32x4 v[U], wl[U], wh[U];
     load_span<IO, U>(a, r, whole, q0, stride, t, v);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * stride + t;
-        wl[u] = whole_weight_chunk<IO>(a.w, q - 1, H);
-        wh[u] = whole_weight_chunk<IO>(a.w, q, H);
+    for (int u = 0; u < U; ++u) wh[u] = whole_weight_chunk<IO>(a.w, q0 + u * stride + t, H);
+    // A row that starts on a vector boundary (every row, when hidden is a
+    // whole number of vectors) takes its weight windows whole: chunk q - 1
+    // is loaded, and read, only for shifted windows (a uniform branch).
+    if (r.fw != 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wl[u] = whole_weight_chunk<IO>(a.w, q0 + u * stride + t - 1, H);
     }
     if (a.w != nullptr && wfull * E != H && q0 + stride * (U - 1) + stride > wfull) {
         // windows reaching the weight's partial last chunk
@@ -562,7 +565,7 @@ __device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEp
             const int j0 = q * E - r.first;
             float f[E], g[E];
             IO::widen(v[u], f);
-            IO::widen(weight_window<IO>(wl[u], wh[u], r.fw), g);
+            IO::widen(r.fw == 0 ? wh[u] : weight_window<IO>(wl[u], wh[u], r.fw), g);
 #pragma unroll
             for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
             if constexpr (OP == GOp::kAda) {
