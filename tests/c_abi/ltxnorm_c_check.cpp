@@ -354,6 +354,11 @@ int main() {
     check_rope(st, false, 333, 1, 128, 9);   // one head per row: the partner in the lane's other slot
     check_adaln(st, 10, 1024, 5);
     check_adaln(st, 301, 1152, 100);    // 32-lane segments, 5 vectors per lane
+    // rows past the register budget: 17 chunks of 2048 vectors, out of place
+    // in chunks over many workgroups, in place two passes (the same bits)
+    check_rmsnorm(st, 5, 262147, 7);
+    check_adaln(st, 3, 262144, 2);
+    check_rope(st, true, 3, 1024, 256, 5);
     check_f32(st, 9, 1000);
     check_f16(st, 37, 3072);            // three wavefronts per row
     check_f16(st, 1001, 320);           // 16-lane segments
