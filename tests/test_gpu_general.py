@@ -214,6 +214,66 @@ def test_split_rows(dtype, hidden, rows):
     check_adaln(x, w, sc, sh, rps, label=f"split adaln {dtype} {rows}x{hidden}")
 
 
+def _random_long_cases():
+    """Seeded shapes past the register budget: row counts on both sides of the
+    split's bound, widths of 5 to 40 chunks, whole and ragged rows, every
+    operation and dtype (a list built once, so pytest ids stay stable)."""
+    rng = np.random.default_rng(20261203)
+    cases = []
+    for i in range(12):
+        dtype = ["bf16", "f16", "f32"][i % 3]
+        E = 4 if dtype == "f32" else 8
+        op = ["rms", "adaln", "il", "half"][i % 4]
+        chunks = int(rng.integers(5, 41))
+        hidden = int(chunks * 2048 * E - rng.integers(0, 2048 * E))
+        if op in ("il", "half"):
+            d = 2 * int(rng.integers(8, 200))
+            hidden = max(1, hidden // d) * d
+        rows = int(rng.choice([rng.integers(1, 12), rng.integers(180, 200)]))
+        rows = min(rows, max(1, (24 << 20) // hidden))  # about 24 M elements at most
+        cases.append((op, dtype, rows, hidden, d if op in ("il", "half") else 0))
+    return cases
+
+
+RANDOM_LONG = _random_long_cases()
+
+
+@pytest.mark.parametrize("op,dtype,rows,hidden,d", RANDOM_LONG)
+def test_random_long_rows(op, dtype, rows, hidden, d):
+    """Every element against the oracle, through whichever long-row kernel
+    the library picks; the sample reaches both (asserted in the CPU tests'
+    kernel-choice sweep and here by the case list)."""
+    code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+    opc = {"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "il": ltx.OP_ROPE_INTERLEAVED, "half": ltx.OP_ROPE}[op]
+    desc = ltx.ltxnorm_describe_launch(opc, rows, hidden, hidden // d if d else 0, d, code)
+    assert desc.split()[0] in ("rmsnorm_split_kernels", "rmsnorm_long_kernel"), desc
+    announce(f"random long {op} {dtype} {rows}x{hidden} d={d}: {desc.split()[0]}")
+    seed = hidden + 13 * rows
+    x = datagen.make_x(rows, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    label = f"random long {op} {dtype} {rows}x{hidden} d={d}"
+    if op == "rms":
+        check_rms(x, w, label=label)
+    elif op == "adaln":
+        rps = max(1, -(-rows // 2))
+        samples = -(-rows // rps)
+        sc = datagen.make_x(samples, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+        sh = datagen.make_x(samples, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+        check_adaln(x, w, sc, sh, rps, label=label)
+    else:
+        c, s_ = datagen.rope_tables(7, d)
+        check_rope(x, w, c, s_, hidden // d, d, interleaved=(op == "il"), label=label)
+
+
+def test_random_long_cases_reach_both_kernels():
+    kinds = set()
+    for op, dtype, rows, hidden, d in RANDOM_LONG:
+        code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+        opc = {"rms": ltx.OP_RMSNORM, "adaln": ltx.OP_ADALN, "il": ltx.OP_ROPE_INTERLEAVED, "half": ltx.OP_ROPE}[op]
+        kinds.add(ltx.ltxnorm_describe_launch(opc, rows, hidden, hidden // d if d else 0, d, code).split()[0])
+    assert kinds == {"rmsnorm_split_kernels", "rmsnorm_long_kernel"}, kinds
+
+
 def test_adaln_null_modulation_any_hidden():
     """NULL scale and shift give RMSNorm bit for bit on the general and
     two-pass kernels too."""
