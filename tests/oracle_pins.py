@@ -289,6 +289,26 @@ def pin_rope_row_position(o):
         assert np.array_equal(yr[0], y[r]), r
 
 
+def pin_rope_composition(o):
+    """Rotations compose: turning a normalised row by position p1's table and
+    the result by p2's equals one turn by p1 + p2, since each pair's angle is
+    linear in the position (inv_freq_i * p), in both pairings.  The
+    intermediate row passes through binary32 (the oracle's input type) and
+    the tables are binary32 values, so agreement is to about 1e-6; the single
+    turns differ by far more."""
+    rng = np.random.default_rng(53)
+    heads, d = 3, 16
+    x = rng.standard_normal((2, heads * d)).astype(np.float32)
+    for il in (False, True):
+        for p1, p2 in ((3, 5), (100, 17)):
+            c, s = _tables([p1, p2, p1 + p2], d)
+            y1 = o.rmsnorm_rope(x, None, c[0:1], s[0:1], heads, d, 0.0, interleaved=il)
+            y2 = o.rmsnorm_rope(y1.astype(np.float32), None, c[1:2], s[1:2], heads, d, 0.0, interleaved=il)
+            y12 = o.rmsnorm_rope(x, None, c[2:3], s[2:3], heads, d, 0.0, interleaved=il)
+            assert np.abs(y2 - y12).max() <= 4e-6, (il, p1, p2, np.abs(y2 - y12).max())
+            assert np.abs(y1 - y12).max() > 1e-2, (il, p1, p2)
+
+
 def pin_rope_mag(o):
     """The magnitude sum returned with the rotation is |a c| + |b s| (first
     half) and |b c| + |a s| (second half): it bounds the rotated value and
@@ -708,7 +728,7 @@ PINS = [
     pin_zero_row, pin_scale_invariance, pin_sign_symmetry, pin_textbook_norm,
     pin_none_weight_is_ones, pin_rows_independent, pin_permutation, pin_brute_force_exact,
     pin_rope_position_zero_is_rmsnorm, pin_rope_complex_rotation, pin_rope_pair_norm,
-    pin_rope_constant_row, pin_rope_row_position, pin_rope_mag,
+    pin_rope_constant_row, pin_rope_row_position, pin_rope_mag, pin_rope_composition,
     pin_rope_il_position_zero_is_rmsnorm, pin_rope_il_complex_rotation,
     pin_rope_small_and_odd_halves, pin_rope_il_matches_rotate_half_after_reorder, pin_rope_il_constant_row, pin_rope_il_mag,
     pin_adaln_zero_modulation_is_rmsnorm, pin_adaln_scale_minus_one_gives_shift,
