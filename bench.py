@@ -91,7 +91,7 @@ PROBES = {"rms": (datagen.HEADLINE, "bf16"), "rms_f16": (datagen.HEADLINE, "f16"
           "rope_f16": (datagen.ROPE, "f16"), "rope_f32": (datagen.ROPE, "f32"),
           "adaln_f32": (datagen.ADALN, "f32"),
           "rms_odd": ("rms_4x4096x3076", "bf16"), "rope_d72": ("rope_2x4096x1152_h16d72", "bf16"),
-          "rms_long": ("rms_1x256x262144", "bf16"), "rms_split": ("rms_1x64x1048576", "bf16"),
+          "rms_long": ("rms_1x512x131072", "bf16"), "rms_split": ("rms_1x64x1048576", "bf16"),
           "rms_short": ("rms_2x4096x24_d128", "bf16"),
           "adaln_seg": ("adaln_8x4096x1152", "bf16"),
           "rope_large": ("rope_4x4096x3072_h24d128", "bf16"),
@@ -715,7 +715,7 @@ def main():
         for wname, kernel, path in (
                 ("rms_4x4096x3076", "rmsnorm_odd", "general one-pass"),
                 ("rope_2x4096x1152_h16d72", "rmsnorm_rope_d72", "head-packed vector kernel"),
-                ("rms_1x256x262144", "rmsnorm_long", "two-pass"),
+                ("rms_1x512x131072", "rmsnorm_long", "two-pass"),
                 ("rms_1x64x1048576", "rmsnorm_split", "split rows, chunks over many workgroups"),
                 ("rms_2x4096x24_d128", "rmsnorm_short", "short rows, several per wavefront"),
                 ("adaln_8x4096x1152", "rmsnorm_adaln_seg", "segmented rows, several per wavefront")):

@@ -228,7 +228,9 @@ GENERAL_CONFIGS = {
     "rms_4x4096x3076": Config("rms_4x4096x3076", 9, 4, 4096, 3076),
     "rope_2x4096x1152_h16d72": Config("rope_2x4096x1152_h16d72", 10, 2, 4096, 1152,
                                       heads=16, head_dim=72, theta=10000.0),
-    "rms_1x256x262144": Config("rms_1x256x262144", 11, 1, 256, 262144),
+    # rows past the register budget in whole rounds of the two-pass kernel:
+    # 512 rows of 131072 (8 chunks of 2048 vectors each)
+    "rms_1x512x131072": Config("rms_1x512x131072", 11, 1, 512, 131072),
     # per-head normalisation (query/key norm): rows of one 128-element head,
     # [2 x 4096 x 24 heads] of them
     "rms_2x4096x24_d128": Config("rms_2x4096x24_d128", 12, 2, 4096 * 24, 128),

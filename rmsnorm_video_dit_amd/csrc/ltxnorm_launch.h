@@ -53,16 +53,20 @@ constexpr int kLongThreads = 1024;        // two-pass kernel: one row per workgr
 // Split kernels (rows beyond the register budget, out of place): chunks of
 // kSplitChunkVectors vectors of a row, one 256-thread workgroup each, at most
 // kSplitMaxChunkCount chunks per row (the partials a wavefront reads at once).
-// The two-pass kernel gives a row one 1024-thread workgroup, which streams
-// at about 35 GB/s: it keeps HBM busy from about 192 rows on.  Below that,
-// rows of at least kSplitMinChunks chunks take the split, whose three
-// launches cost more than they gain on rows of fewer chunks (bf16, 96 rows
-// of 262144: 44.5 -> 35.6 us; 160 rows: 53.5 -> 50.7 us; 192 rows 53.6 ->
-// 57.2 us; 128 rows of 65544, five chunks: 16.5 -> 23.4 us).
+// The two-pass kernel gives a row one 1024-thread workgroup, one at a time
+// per CU: rows go in rounds of 256, and a round that is not full still lasts
+// about as long as one workgroup's stream (about 35 GB/s).  Rows of at least
+// kSplitMinChunks chunks take the split below kSplitMaxRows rows (bf16 rows
+// of 262144, us, two passes -> split: 96 rows 44.5 -> 35.6; 160 53.5 ->
+// 50.7; 288 99.2 -> 83.0; 384 118.9 -> 103.0; 512 144.6 -> 130.4; 576
+// 169.9 -> 156.5; 608 173.4 -> 170.2; but 256 rows 69.7 -> 71.9, 640 174.2
+// -> 178.4, 768 210.1 -> 212.1).  With fewer chunks the split's three
+// launches cost more than they gain (128 rows of 65544, five chunks: 16.5 ->
+// 23.4 us; 1200 rows of 131072, eight chunks: 154.7 -> 165.0 us).
 constexpr int kSplitChunkVectors = 2048;
 constexpr int kSplitMaxChunkCount = 2048;
 constexpr int kSplitMinChunks = 16;
-constexpr int64_t kSplitMaxRows = 191;
+constexpr int64_t kSplitMaxRows = 623;
 // Workgroup slots per row in the split's second launch (chunks 1 and up).
 // Workgroups are dealt to the 8 XCDs in turn, so with the slot count a
 // multiple of 8 chunk c of every row runs on the same XCD and that XCD's L2

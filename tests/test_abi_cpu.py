@@ -422,7 +422,7 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
 
 
 @pytest.mark.parametrize("op,hidden,heads,head_dim,dtype,rows,chunks", [
-    # fewer than 192 rows of at least 16 chunks of 2048 vectors: the split
+    # fewer than 624 rows of at least 16 chunks of 2048 vectors: the split
     (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 191, 16),
     (ltx.OP_RMSNORM, 245761, 0, 0, ltx.BF16, 1, 16),      # 30722 vectors touched
     (ltx.OP_RMSNORM, 1 << 20, 0, 0, ltx.BF16, 64, 64),
@@ -431,7 +431,9 @@ def test_kernel_choice(op, hidden, heads, head_dim, dtype, kernel, wpr, per):
     (ltx.OP_ROPE_INTERLEAVED, 1 << 24, 1024, 1 << 14, ltx.BF16, 3, 1024),
     (ltx.OP_RMSNORM, 1 << 24, 0, 0, ltx.F32, 1, 2048),
     # otherwise two passes in one workgroup per row
-    (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 192, None),
+    (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 623, 16),
+    (ltx.OP_RMSNORM, 262144, 0, 0, ltx.BF16, 624, None),
+    (ltx.OP_RMSNORM, 131072, 0, 0, ltx.BF16, 300, None),  # 8 chunks
     (ltx.OP_RMSNORM, 245752, 0, 0, ltx.BF16, 1, None),     # 30719 vectors: 15 chunks
     (ltx.OP_RMSNORM, 65544, 0, 0, ltx.BF16, 64, None),
     (ltx.OP_RMSNORM, (1 << 24) - 1, 0, 0, ltx.F32, 1, None),  # 2049 chunks
@@ -497,7 +499,7 @@ def test_kernel_choice_covers_the_benchmark_workloads():
               "ropei_2x4096x2048_h32d64": "rmsnorm_rope_interleaved_kernel(shared)",
               "adaln_2x4096x2048": "rmsnorm_adaln_kernel", "rms_4x4096x3076": "rmsnorm_general_kernel",
               "rope_2x4096x1152_h16d72": "rmsnorm_rope_packed_kernel(odd)",
-              "rms_1x256x262144": "rmsnorm_long_kernel", "rms_1x64x1048576": "rmsnorm_split_kernels"}
+              "rms_1x512x131072": "rmsnorm_long_kernel", "rms_1x64x1048576": "rmsnorm_split_kernels"}
     for name, kernel in expect.items():
         cfg = {**datagen.CONFIGS, **datagen.GENERAL_CONFIGS}[name]
         op = (ltx.OP_ADALN if cfg.adaln else ltx.OP_ROPE_INTERLEAVED if cfg.interleaved
@@ -535,11 +537,11 @@ def test_kernel_choice_always_covers_the_row():
         chunks = -(-touched // 2048)
         if name == "rmsnorm_long_kernel":
             assert f["threads"] == "1024"
-            assert op == ltx.OP_ROPE or not 16 <= chunks <= 2048 or rows >= 192, desc
+            assert op == ltx.OP_ROPE or not 16 <= chunks <= 2048 or rows >= 624, desc
             continue
         if name == "rmsnorm_split_kernels":
             assert op != ltx.OP_ROPE and int(f["chunks_per_row"]) == chunks and 16 <= chunks <= 2048, desc
-            assert rows < 192, desc
+            assert rows < 624, desc
             continue
         if name == "rmsnorm_short_kernel":
             lanes, per, n = int(f["lanes_per_row"]), int(f["vectors_per_lane"]), H // E

@@ -179,10 +179,11 @@ def test_paths_invariants(op, hidden, d):
 # Long rows out of place take the split kernels: chunks of 2048 vectors over
 # many workgroups, the partial sums staged in the row's own output.  In place
 # they take the two-pass kernel.  Both add a row's squares in the same order.
-# rows of 16 or more chunks of 2048 vectors, fewer than 192 rows: whole and
+# rows of 16 or more chunks of 2048 vectors, fewer than 624 rows: whole and
 # ragged rows, a last chunk of one vector, the most rows, 2048 chunks
 SPLIT = [("bf16", 262144, 37), ("bf16", 1 << 20, 5), ("bf16", 245769, 13), ("f32", 122881, 64),
-         ("f16", 262147, 9), ("bf16", 16 * 16384 + 8, 1), ("bf16", 262144, 191), ("f32", 1 << 24, 1)]
+         ("f16", 262147, 9), ("bf16", 16 * 16384 + 8, 1), ("bf16", 262144, 191), ("f16", 245769, 300),
+         ("f32", 1 << 24, 1)]
 
 
 @pytest.mark.parametrize("dtype,hidden,rows", SPLIT)
