@@ -64,11 +64,12 @@ extern "C" {
 /* Largest supported hidden size, every dtype.  Rows of up to 65536 bf16/fp16
  * or 32768 fp32 elements are held in registers and read from HBM once;
  * longer rows are read twice (once for the sum of squares, once to
- * normalise).  Out of place, such rows are cut into chunks over many
- * workgroups in three launches, and between the first and the last of them
- * the start of each row's output holds binary32 partial sums: a reader of
- * out sees the results only after the call's work on the stream is done, as
- * for every call. */
+ * normalise).  Out of place, a call of a few hundred such rows of many
+ * chunks may cut them into chunks over many workgroups in three launches
+ * (ltxnorm_describe_launch names the choice), and between the first and the
+ * last of them the start of each row's output holds binary32 partial sums: a
+ * reader of out sees the results only after the call's work on the stream is
+ * done, as for every call. */
 #define LTXNORM_MAX_HIDDEN (1 << 24)
 
 typedef enum ltxnorm_dtype {
