@@ -520,11 +520,13 @@ __device__ __forceinline__ void load_span(const KArgs& a, const RowSpan<IO::kEpv
 }
 
 // Normalise U vectors of row `row` (as load_span places them), apply the
-// AdaLN modulation or the interleaved rotation, and store them: every
-// operation but rotate-half, whose pairs are half a head apart.
+// AdaLN modulation or the interleaved rotation, and store them, except the
+// row-relative vectors [skip_lo, skip_hi): every operation but rotate-half,
+// whose pairs are half a head apart.
 template <typename IO, GOp OP, int U>
 __device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEpv>& r, int64_t row,
-                                           int64_t whole, int q0, int stride, int t, float rstd) {
+                                           int64_t whole, int q0, int stride, int t, float rstd,
+                                           int skip_lo = 0, int skip_hi = 0) {
     static_assert(OP != GOp::kRopeHalf, "rotate-half pairs are not element-wise");
     constexpr int E = IO::kEpv;
     const int H = a.hidden;
@@ -561,7 +563,7 @@ __device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEp
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int q = q0 + u * stride + t;
-        if (q < r.nch) {
+        if (q < r.nch && (q < skip_lo || q >= skip_hi)) {
             const int j0 = q * E - r.first;
             float f[E], g[E];
             IO::widen(v[u], f);
@@ -713,14 +715,17 @@ rmsnorm_long_kernel(const KArgs a) {
 // kept 64 of 256 CUs busy).  Three launches, no scratch memory and no wait
 // between workgroups:
 //  1. rmsnorm_split_partial_kernel: each chunk's sum of squares (a fixed
-//     tree) goes to the row's staging area, binary32 words at the start of
-//     the row's first whole output vector; it lies in chunk 0 of the output.
-//  2. rmsnorm_split_apply_kernel<..., false>: every chunk but chunk 0 adds
-//     the row's partials in a fixed order (every workgroup of the row gets
-//     the same bits), normalises its chunk and stores it.
-//  3. rmsnorm_split_apply_kernel<..., true>: chunk 0 of every row does the
-//     same, after all of its wavefronts have read the partials it then
-//     overwrites.
+//     tree) goes to the row's staging area, binary32 words from the row's
+//     first whole output vector on (one vector per four chunks, inside
+//     chunk 0 of the output).
+//  2. rmsnorm_split_apply_kernel<..., false>: every chunk adds the row's
+//     partials in a fixed order (every workgroup of the row gets the same
+//     bits), normalises its chunk and stores it; chunk 0 leaves the staging
+//     vectors alone.
+//  3. rmsnorm_split_apply_kernel<..., true>: one workgroup per row does the
+//     same for the staging vectors, after all of its wavefronts have read
+//     the partials they then overwrite.  (Chunk 0 whole in this launch, one
+//     workgroup per row, took 8.3 of 75 us at 64 rows of 2^20.)
 // x is read twice, as in the two-pass kernel.  In place (out == x) the
 // staging area would overwrite x, so those calls take the two-pass kernel.
 // ---------------------------------------------------------------------------
@@ -754,7 +759,7 @@ rmsnorm_split_partial_kernel(const KArgs a, int chunks) {
     }
 }
 
-template <typename IO, GOp OP, bool CHUNK0>
+template <typename IO, GOp OP, bool STAGE>
 __global__ void __launch_bounds__(kSplitThreads)
 rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
     constexpr int E = IO::kEpv;
@@ -762,7 +767,7 @@ rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
     const int64_t b = blockIdx.x;
     int64_t row;
     int c;
-    if constexpr (CHUNK0) {
+    if constexpr (STAGE) {
         row = b;
         c = 0;
     } else {
@@ -773,7 +778,7 @@ rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
         // and ran slower (64 rows of 2^20: 79.3 -> 81.9 us).
         const int slots = split_slots(chunks);
         row = b / slots;
-        c = 1 + (int)(b - row * slots);
+        c = (int)(b - row * slots);
         if (c >= chunks) return;
     }
     const int64_t whole = a.rows * (int64_t)a.hidden / E;
@@ -793,11 +798,23 @@ rmsnorm_split_apply_kernel(const KArgs a, int chunks) {
 #pragma unroll
     for (int j = 0; j < kSplitMaxChunks / kWave; ++j) t += p[j];
     const float rstd = rstd_of(wave_sum(t), a.hidden_f, a.eps);
-    if constexpr (CHUNK0) __syncthreads();  // every wavefront has read the partials
+    // the staging vectors, row-relative
+    const int s0 = r.first != 0 ? 1 : 0;
+    const int s1 = s0 + (chunks + 3) / 4;
+    if constexpr (STAGE) {
+        __syncthreads();  // every wavefront has read the partials
+        RowSpan<E> rs = r;
+        rs.nch = s1 < r.nch ? s1 : r.nch;
+        for (int q0 = s0; q0 < s1; q0 += kSplitThreads * U)
+            apply_span<IO, OP, U>(a, rs, row, whole, q0, kSplitThreads, (int)threadIdx.x, rstd);
+    } else {
+        const int skip_lo = c == 0 ? s0 : 0;
+        const int skip_hi = c == 0 ? s1 : 0;
 #pragma unroll
-    for (int u0 = 0; u0 < kSplitVpt; u0 += U)
-        apply_span<IO, OP, U>(a, r, row, whole, c * kSplitChunk + u0 * kSplitThreads, kSplitThreads,
-                              (int)threadIdx.x, rstd);
+        for (int u0 = 0; u0 < kSplitVpt; u0 += U)
+            apply_span<IO, OP, U>(a, r, row, whole, c * kSplitChunk + u0 * kSplitThreads, kSplitThreads,
+                                  (int)threadIdx.x, rstd, skip_lo, skip_hi);
+    }
 }
 
 }  // namespace

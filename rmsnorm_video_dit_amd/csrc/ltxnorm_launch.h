@@ -67,18 +67,18 @@ constexpr int kSplitChunkVectors = 2048;
 constexpr int kSplitMaxChunkCount = 2048;
 constexpr int kSplitMinChunks = 16;
 constexpr int64_t kSplitMaxRows = 623;
-// Workgroup slots per row in the split's second launch (chunks 1 and up).
+// Workgroup slots per row in the split's second launch (every chunk).
 // Workgroups are dealt to the 8 XCDs in turn, so with the slot count a
 // multiple of 8 chunk c of every row runs on the same XCD and that XCD's L2
-// keeps its weight chunk: 64 rows of 2^20 (63 chunks here) fetched the 2 MB
-// weight about 25 times without the padding, and ran 79.3 -> 75.5 us with
-// it.  The padding also leaves one XCD with fewer chunks per row (15 chunks:
-// 2 on seven XCDs, 1 on the eighth, and 160 rows of 262144 ran 50.7 -> 52.3
-// us), so the count is padded only where that costs at most 2 %.
+// keeps its weight chunk: 64 rows of 2^20 fetched the 2 MB weight about 25
+// times when a chunk fell on a different XCD for every row, and ran 79.3 ->
+// 75.5 us with one XCD per chunk.  Padding a count leaves one XCD with fewer
+// chunks per row (15 chunks padded to 16: 2 on seven XCDs, 1 on the eighth;
+// 160 rows of 262144 ran 50.7 -> 52.3 us), so a count is padded only where
+// that costs at most 2 %.
 constexpr __host__ __device__ int split_slots(int chunks) {
-    const int n = chunks - 1;
-    const int padded = (n + 7) & ~7;
-    return padded * 50 <= n * 51 ? padded : n;
+    const int padded = (chunks + 7) & ~7;
+    return padded * 50 <= chunks * 51 ? padded : chunks;
 }
 
 // Samples (modulation rows) for `rows` rows of `rows_per_sample` each, the

@@ -452,20 +452,21 @@ def test_kernel_choice_long_rows(op, hidden, heads, head_dim, dtype, rows, chunk
         assert int(f["chunks_per_row"]) == chunks
         assert f["launches"] == "3" and f["vectors_per_chunk"] == "2048" and f["threads"] == "256"
         assert f["in_place"] == "rmsnorm_long_kernel"
-        # the second launch's slots per row: chunks 1.. padded to a multiple
+        # the second launch's slots per row: every chunk, padded to a multiple
         # of the 8 XCDs where one XCD then runs at most 2 % less work
-        n = chunks - 1
+        n = chunks
         slots = int(f["slots_per_row"])
         assert slots == (n + 7) // 8 * 8 if (n + 7) // 8 * 8 * 50 <= n * 51 else slots == n
 
 
 def test_split_slots_padding():
-    """Chunk slots per row: 15 and 31 chunks stay unpadded (one XCD would run
-    6.7 / 3.2 % less), 63, 127 and 2047 are padded to the next multiple of 8,
-    multiples of 8 need none."""
-    for hidden, dtype, slots in ((262144, ltx.BF16, 15), (524288, ltx.BF16, 31), (1 << 20, ltx.BF16, 64),
-                                 (1 << 21, ltx.BF16, 128), (1 << 24, ltx.F32, 2048), (17 * 16384, ltx.BF16, 16),
-                                 (16 * 16384 + 8, ltx.BF16, 16)):
+    """Chunk slots per row: a count that is a multiple of 8 needs no padding;
+    63 chunks pad to 64 (one XCD 1.6 % short); 17 and 125 chunks stay
+    unpadded (one XCD would run 30 / 2.4 % short)."""
+    for hidden, dtype, slots in ((262144, ltx.BF16, 16), (524288, ltx.BF16, 32), (1 << 20, ltx.BF16, 64),
+                                 (63 * 16384, ltx.BF16, 64), (1 << 21, ltx.BF16, 128), (1 << 24, ltx.F32, 2048),
+                                 (17 * 16384, ltx.BF16, 17), (16 * 16384 + 8, ltx.BF16, 17),
+                                 (125 * 16384, ltx.BF16, 125)):
         name, f = _describe(ltx.OP_RMSNORM, hidden, dtype=dtype, rows=4)
         assert name == "rmsnorm_split_kernels" and int(f["slots_per_row"]) == slots, (hidden, f)
 
