@@ -30,6 +30,10 @@
 //    to normalise and store.  Rotate-half pairs are handled as units of one
 //    window of the first half and its partner window in the second half, each
 //    read and written by one thread, so that in-place calls stay correct.
+//  * rmsnorm_split_partial_kernel, rmsnorm_split_apply_kernel: the same rows
+//    out of place, cut into chunks over many workgroups in three launches
+//    (section below); they add a row's squares in the two-pass kernel's
+//    order, so both give the same bits.
 #pragma once
 
 #include "ltxnorm_device.h"
