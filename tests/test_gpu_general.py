@@ -17,7 +17,7 @@ import torch
 import datagen
 import rmsnorm_video_dit_amd as ltx
 from parity import compare
-from test_gpu_parity import (DEV, ORC, announce, check_adaln, check_rms, check_rope, dev_bf16,
+from test_gpu_parity import (DEV, ORC, announce, kind, check_adaln, check_rms, check_rope, dev_bf16,
                              dev_f32, host_bits, run_adaln, run_rms, run_rope)
 
 pytestmark = pytest.mark.gpu
@@ -666,6 +666,55 @@ def test_resident_grid_threads():
         ref32, ref = ORC.round(y, "bf16")
         rep = compare(outs[0], ref, mag, ref32)
         assert rep["pass"], (heads, d, rep)
+
+
+def test_split_streams_concurrent():
+    """Four host threads, each on its own stream, run the split kernels at
+    once on their own rows: each call stages its partial sums in its own
+    output, so concurrent calls do not interfere.  Repeats are bit-identical
+    and every result matches the oracle."""
+    import threading
+    shapes = [("bf16", 262144, 8), ("bf16", 262151, 5), ("f16", 300000, 6), ("f32", 131075, 7)]
+    announce(f"split, {len(shapes)} threads on their own streams")
+    inputs = []
+    for dtype, hidden, rows in shapes:
+        code = {"bf16": ltx.BF16, "f16": ltx.F16, "f32": ltx.F32}[dtype]
+        desc = ltx.ltxnorm_describe_launch(ltx.OP_RMSNORM, rows, hidden, 0, 0, code)
+        assert desc.startswith("rmsnorm_split_kernels"), desc
+        x = datagen.make_x(rows, hidden, seed=hidden + rows, stream=1, dtype=dtype)
+        w = datagen.make_w(hidden, seed=hidden + rows, stream=2, dtype=dtype)
+        inputs.append((x, w))
+    results = [None] * len(shapes)
+    errors = []
+    barrier = threading.Barrier(len(shapes))
+
+    def work(i):
+        try:
+            x, w = inputs[i]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                xt, wt = dev_bf16(x), dev_bf16(w)
+                stream.synchronize()
+                barrier.wait()
+                outs = [ltx.rmsnorm(xt, wt, 1e-6) for _ in range(3)]
+                stream.synchronize()
+            results[i] = [host_bits(o) for o in outs]
+        except Exception as e:  # reported below, in the test's thread
+            errors.append((i, repr(e)))
+            barrier.abort()
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert all(not t.is_alive() for t in threads)
+    for (x, w), outs in zip(inputs, results):
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+        ref32, ref = ORC.round(ORC.rmsnorm(x, w, 1e-6), kind(x))
+        rep = compare(outs[0], ref, None, ref32)
+        assert rep["pass"], rep
 
 
 # ---------------------------------------------------------------------------
