@@ -232,8 +232,16 @@ typedef enum ltxnorm_op {
  *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
  * The general kernel's line ends in "grid=resident": its grid is capped at
  * the number of workgroups the device holds at once, each workgroup looping
- * over rows; every other kernel takes one workgroup per group of rows.  heads and head_dim are
- * read for the RoPE operations only.  LTXNORM_OP_ADALN describes a call
+ * over rows; every other kernel takes one workgroup per group of rows.
+ * Rows past the register budget take two passes in one workgroup per row,
+ *     "rmsnorm_long_kernel passes=2 rows_per_block=1 threads=1024 lds_bytes=0"
+ * or, for a few hundred rows of many chunks, the split kernels:
+ *     "rmsnorm_split_kernels launches=3 chunks_per_row=64
+ *      vectors_per_chunk=2048 slots_per_row=64 threads=256 lds_bytes=0
+ *      in_place=rmsnorm_long_kernel"
+ * where in_place names the kernel a call with out == x takes instead (the
+ * split stages partial sums in out, which must not be x).  heads and
+ * head_dim are read for the RoPE operations only.  LTXNORM_OP_ADALN describes a call
  * with modulation rows (one with neither runs LTXNORM_OP_RMSNORM's kernel).
  *
  * The row split fixes the order in which a row's squares are added, so two
