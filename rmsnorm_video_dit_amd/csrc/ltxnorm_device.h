@@ -307,6 +307,19 @@ struct KArgs {
     float eps;
 };
 
+// Wave priority around a row's loads: a wavefront raises its priority while
+// it issues the loads of its row and drops back as soon as they are in
+// flight, so that on a CU where some wavefronts reduce or store and others
+// start a row, the new row's requests reach memory first.  The kernels use it
+// where it measured faster at about 100-200 MB per launch: RMSNorm and AdaLN
+// rows of several wavefronts (bf16 [16384 x 3072] +0.3 %, fp32 +1.0 %, fp32
+// hidden 4096 +3.8 %; AdaLN hidden 3072 and 4096 +1.3 and +2.1 %) and the
+// general kernel (hidden 1028, 2052, 3076 +3.1, +1.9, +0.5 %).  With one
+// wavefront per row it gained at 8192 rows and lost at 16384, and it slowed
+// the rotate-half RoPE and short-row kernels, so those do not use it.
+__device__ __forceinline__ void priority_for_loads() { __builtin_amdgcn_s_setprio(3); }
+__device__ __forceinline__ void priority_after_loads() { __builtin_amdgcn_s_setprio(0); }
+
 // Common prologue of every kernel: which row slot and lane this thread is.
 template <int WPR>
 struct Lane {

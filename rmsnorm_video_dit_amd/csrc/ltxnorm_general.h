@@ -325,6 +325,7 @@ rmsnorm_general_kernel(const KArgs a) {
     // grid-stride step (gridDim.x * RPB rows) a multiple of 8 whenever a
     // workgroup loops, so every row this slot visits has its first row's
     // offset and the same window (from chunks q - 1 and q).
+    priority_for_loads();
     u32x4 wwin[VPL];
     {
         const int64_t row0 = (int64_t)blockIdx.x * RPB + ln.slot;
@@ -349,6 +350,7 @@ rmsnorm_general_kernel(const KArgs a) {
         const int nch = active ? (first + H + E - 1) / E : 0;  // vectors the row touches
 
         u32x4 xv[VPL];
+        priority_for_loads();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int q = k * L + ln.t;
@@ -362,6 +364,7 @@ rmsnorm_general_kernel(const KArgs a) {
                 if (q < nch && g0 + q >= whole) xv[k] = load_elems<IO>(a.x, (g0 + q) * E, s, s + H);
             }
         }
+        priority_after_loads();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int j0 = (k * L + ln.t) * E - first;

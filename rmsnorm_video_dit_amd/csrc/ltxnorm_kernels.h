@@ -20,6 +20,7 @@ rmsnorm_kernel(const KArgs a) {
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
+    if constexpr (WPR > 1) priority_for_loads();
     u32x4 wv[VPL];
     load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
@@ -33,7 +34,9 @@ rmsnorm_kernel(const KArgs a) {
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
         u32x4 xv[VPL];
+        if constexpr (WPR > 1) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
+        if constexpr (WPR > 1) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
 
@@ -671,6 +674,7 @@ rmsnorm_adaln_kernel(const KArgs a) {
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
+    if constexpr (WPR > 1) priority_for_loads();
     u32x4 wv[VPL];
     load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
@@ -699,11 +703,13 @@ rmsnorm_adaln_kernel(const KArgs a) {
             hv = (a.shift != nullptr && in) ? hr[v] : splat(IO::kNegZero);
         };
         u32x4 xv[VPL], svv[VPL], hvv[VPL];
+        if constexpr (WPR > 1) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         if constexpr (kEarly) {
 #pragma unroll
             for (int k = 0; k < VPL; ++k) mod_rows(k, svv[k], hvv[k]);
         }
+        if constexpr (WPR > 1) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
 
