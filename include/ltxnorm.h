@@ -225,14 +225,20 @@ typedef enum ltxnorm_op {
  * shapes would use.  It is written as one NUL-terminated line of text into
  * buf, truncated to len bytes, for example
  *     "rmsnorm_kernel wavefronts_per_row=3 vectors_per_lane=2 rows_per_block=2
- *      threads=384 lds_bytes=0"
- * (the kernel names are those a profiler shows).  Rows of up to 160
- * vectors may share wavefronts instead, in segments of a few lanes:
+ *      threads=384 lds_bytes=0 load_priority=always"
+ * (the kernel names are those a profiler shows).  load_priority says when
+ * the kernel's wavefronts raise their priority while a row's loads issue:
+ * "always", "never", or "one_wave": only when the launch's whole grid is
+ * resident on the device at once (decided at launch from the device's
+ * occupancy for that instance).  It changes timing only, never a result
+ * bit.  Rows of up to 160 vectors may share wavefronts instead, in
+ * segments of a few lanes:
  *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2
  *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
- * The general kernel's line ends in "grid=resident": its grid is capped at
- * the number of workgroups the device holds at once, each workgroup looping
- * over rows; every other kernel takes one workgroup per group of rows.
+ * The general kernel's line ends in "load_priority=always grid=resident":
+ * its grid is capped at the number of workgroups the device holds at once,
+ * each workgroup looping over rows; every other kernel takes one workgroup
+ * per group of rows.
  * Rows past the register budget take two passes in one workgroup per row,
  *     "rmsnorm_long_kernel passes=2 rows_per_block=1 threads=1024 lds_bytes=0"
  * or, for a few hundred rows of many chunks, the split kernels:

@@ -247,10 +247,16 @@ LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, 
                       name, c.chunks, ltxnorm_detail::kSplitChunkVectors, ltxnorm_detail::split_slots(c.chunks));
     } else {
         const int rpb = ltxnorm_detail::rows_per_block(c.plan.wpr);
-        std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld%s",
+        // wave priority for the loads: always, when the grid is resident at
+        // once (one-wavefront instances), or never (the dispatch's rule)
+        const bool always = c.kernel == Kernel::kGeneral ||
+                            ((c.kernel == Kernel::kRmsNorm || c.kernel == Kernel::kAdaLN) && c.plan.wpr > 1);
+        const bool one_wave = c.plan.wpr == 1 && c.kernel != Kernel::kGeneral && c.kernel != Kernel::kRopePair;
+        std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld load_priority=%s%s",
                       name, c.plan.wpr, c.kernel == Kernel::kRopePair ? "pairs_per_lane" : "vectors_per_lane",
                       c.plan.per, rpb, ltxnorm_detail::kWave * c.plan.wpr * rpb,
-                      (long long)(c.lds_per_row * rpb), c.kernel == Kernel::kGeneral ? " grid=resident" : "");
+                      (long long)(c.lds_per_row * rpb), always ? "always" : (one_wave ? "one_wave" : "never"),
+                      c.kernel == Kernel::kGeneral ? " grid=resident" : "");
     }
     return LTXNORM_OK;
 }

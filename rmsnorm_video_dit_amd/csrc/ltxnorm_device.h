@@ -310,13 +310,20 @@ struct KArgs {
 // Wave priority around a row's loads: a wavefront raises its priority while
 // it issues the loads of its row and drops back as soon as they are in
 // flight, so that on a CU where some wavefronts reduce or store and others
-// start a row, the new row's requests reach memory first.  The kernels use it
-// where it measured faster at about 100-200 MB per launch: RMSNorm and AdaLN
-// rows of several wavefronts (bf16 [16384 x 3072] +0.3 %, fp32 +1.0 %, fp32
-// hidden 4096 +3.8 %; AdaLN hidden 3072 and 4096 +1.3 and +2.1 %) and the
-// general kernel (hidden 1028, 2052, 3076 +3.1, +1.9, +0.5 %).  With one
-// wavefront per row it gained at 8192 rows and lost at 16384, and it slowed
-// the rotate-half RoPE and short-row kernels, so those do not use it.
+// start a row, the new row's requests reach memory first.  Where it is used,
+// measured at about 100-200 MB per launch unless stated:
+//  * RMSNorm and AdaLN rows of several wavefronts, always (bf16
+//    [16384 x 3072] +0.3 %, fp32 +1.0 %, fp32 hidden 4096 +3.8 %; AdaLN
+//    hidden 3072 and 4096 +1.3 and +2.1 %), and the general kernel (hidden
+//    1028, 2052, 3076 +3.1, +1.9, +0.5 %);
+//  * one-wavefront rows of RMSNorm, AdaLN and the RoPE kernels (template flag
+//    PRIO) when the whole grid is resident at once: every row's loads then
+//    issue before the stores start, instead of reads and writes interleaving
+//    (bf16 [8192 x 2048] RMSNorm 13.07 -> 11.33 us, interleaved RoPE 13.30 ->
+//    11.56 us; [4096 x 2048] rotate-half RoPE 8.03 -> 7.23 us, AdaLN 8.40 ->
+//    7.84 us; [4096 x 2048] RMSNorm 7.89 -> 6.63 us).  On grids of several
+//    waves of workgroups the same instances ran 2-9 % slower, and the
+//    short-row kernel was slower either way, so those launches do not use it.
 __device__ __forceinline__ void priority_for_loads() { __builtin_amdgcn_s_setprio(3); }
 __device__ __forceinline__ void priority_after_loads() { __builtin_amdgcn_s_setprio(0); }
 

@@ -18,8 +18,8 @@ namespace {
 // Workgroups of `fn` (at this size and dynamic LDS) that the stream's device
 // holds at once: workgroups per CU times the CU count, or 0 where HIP cannot
 // say.  The figure depends only on the device and the kernel instance, so it
-// is kept in a small table guarded by a mutex (entries are never removed;
-// once the table is full, later instances are queried on every launch).
+// is kept in a table guarded by a mutex (entries are never removed; once the
+// table is full, later instances are queried on every launch).
 inline int64_t resident_workgroups(const void* fn, int threads, size_t lds_bytes,
                                    hipStream_t stream) {
     struct Entry {
@@ -29,7 +29,7 @@ inline int64_t resident_workgroups(const void* fn, int threads, size_t lds_bytes
         int64_t n;
     };
     static std::mutex mu;
-    static Entry table[128];
+    static Entry table[512];
     static int used = 0;
     int dev = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return 0;
@@ -75,53 +75,72 @@ inline ltxnorm_status launch(const void* fn, int threads, int rpb, const KArgs& 
     return e == hipSuccess ? LTXNORM_OK : LTXNORM_ERR_HIP;
 }
 
-// One launcher per kernel family: fn<WPR, PER, FULL>() picks the instance;
-// kResident asks for the grid capped at the resident capacity.
+// One launcher per kernel family: fn<WPR, PER, FULL, PRIO>() picks the
+// instance; kResident asks for the grid capped at the resident capacity;
+// kOneWavePrio says that the family has one-wavefront instances that raise
+// the wave priority for their loads (PRIO), taken when the whole grid is
+// resident at once.
 template <typename IO>
 struct RmsL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
-    static const void* fn() { return (const void*)&rmsnorm_kernel<IO, PER, WPR, FULL>; }
+    static constexpr bool kOneWavePrio = true;
+    template <int WPR, int PER, bool FULL, bool PRIO>
+    static const void* fn() { return (const void*)&rmsnorm_kernel<IO, PER, WPR, FULL, PRIO>; }
 };
 template <typename IO>
 struct RopeXorL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
-    static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL>; }
+    static constexpr bool kOneWavePrio = true;
+    template <int WPR, int PER, bool FULL, bool PRIO>
+    static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO>; }
 };
 template <typename IO>
 struct RopePairL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
+    static constexpr bool kOneWavePrio = false;
+    template <int WPR, int PER, bool FULL, bool PRIO>
     static const void* fn() { return (const void*)&rmsnorm_rope_pair_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO, bool SHARED>
 struct RopeIlL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
+    static constexpr bool kOneWavePrio = true;
+    template <int WPR, int PER, bool FULL, bool PRIO>
     static const void* fn() {
-        return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED>;
+        return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED, PRIO>;
     }
 };
 template <typename IO>
 struct AdaL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
-    static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL>; }
+    static constexpr bool kOneWavePrio = true;
+    template <int WPR, int PER, bool FULL, bool PRIO>
+    static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL, PRIO>; }
 };
 template <typename IO, bool ODD>
 struct RopePackedL {
     static constexpr bool kResident = false;
-    template <int WPR, int PER, bool FULL>
-    static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD>; }
+    static constexpr bool kOneWavePrio = true;
+    template <int WPR, int PER, bool FULL, bool PRIO>
+    static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>; }
 };
 // The general kernel masks every row itself: FULL does not select anything.
 template <typename IO, GOp OP>
 struct GeneralL {
     static constexpr bool kResident = true;
-    template <int WPR, int PER, bool FULL>
+    static constexpr bool kOneWavePrio = false;
+    template <int WPR, int PER, bool FULL, bool PRIO>
     static const void* fn() { return (const void*)&rmsnorm_general_kernel<IO, OP, PER, WPR>; }
 };
+
+// Whether the grid of `rows` rows (rpb per workgroup) is resident at once
+// for instance fn, at this size and dynamic LDS.
+inline bool fits_one_wave(const void* fn, int threads, int rpb, int64_t rows, size_t lds_bytes,
+                          hipStream_t stream) {
+    const int64_t need = (rows + rpb - 1) / rpb;
+    const int64_t cap = resident_workgroups(fn, threads, lds_bytes, stream);
+    return cap > 0 && need <= cap;
+}
 
 template <typename LN, int WPR, int LO, int HI>
 ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStream_t s) {
@@ -129,9 +148,16 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
         return LTXNORM_ERR_UNSUPPORTED;
     } else {
         if (p.per == LO) {
-            const void* fn = p.full ? LN::template fn<WPR, LO, true>() : LN::template fn<WPR, LO, false>();
-            return launch(fn, Layout<WPR>::kThreads, Layout<WPR>::kRowsPerBlock, a,
-                          lds_per_row * Layout<WPR>::kRowsPerBlock, s, LN::kResident);
+            constexpr int kT = Layout<WPR>::kThreads, kRpb = Layout<WPR>::kRowsPerBlock;
+            const size_t lds = lds_per_row * kRpb;
+            const void* fn = p.full ? LN::template fn<WPR, LO, true, false>()
+                                    : LN::template fn<WPR, LO, false, false>();
+            if constexpr (WPR == 1 && LN::kOneWavePrio) {
+                const void* fp = p.full ? LN::template fn<WPR, LO, true, true>()
+                                        : LN::template fn<WPR, LO, false, true>();
+                if (fits_one_wave(fp, kT, kRpb, a.rows, lds, s)) fn = fp;
+            }
+            return launch(fn, kT, kRpb, a, lds, s, LN::kResident);
         }
         return by_per<LN, WPR, LO + 1, HI>(p, a, lds_per_row, s);
     }

@@ -11,16 +11,20 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // RMSNorm: VPL vectors per lane, WPR wavefronts per row.  FULL means every
-// lane's every slot is inside the row (no masking).
+// lane's every slot is inside the row (no masking).  Rows of several
+// wavefronts raise the wave priority while their loads issue; PRIO does the
+// same for one-wavefront rows (the launch asks for it when the whole grid is
+// resident at once).
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_kernel(const KArgs a) {
+    constexpr bool kPrio = WPR > 1 || PRIO;
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
-    if constexpr (WPR > 1) priority_for_loads();
+    if constexpr (kPrio) priority_for_loads();
     u32x4 wv[VPL];
     load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
@@ -34,9 +38,9 @@ rmsnorm_kernel(const KArgs a) {
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
         u32x4 xv[VPL];
-        if constexpr (WPR > 1) priority_for_loads();
+        if constexpr (kPrio) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
-        if constexpr (WPR > 1) priority_after_loads();
+        if constexpr (kPrio) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
 
@@ -249,9 +253,10 @@ rmsnorm_short_kernel(const KArgs a) {
 // the VALU work per vector, which matters because with one row per wavefront
 // the whole grid is resident and compute is not hidden behind later loads).  A lane's half
 // (bit P of t) and its table slice (floats kEpv * (t mod P) .. + kEpv) do not
-// depend on the slot, so each lane reads one table slice per row.
+// depend on the slot, so each lane reads one table slice per row.  PRIO
+// raises the wave priority while a row's loads issue.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_xor_kernel(const KArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
@@ -267,6 +272,7 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
         const float sgn = (ln.t & P) ? 1.0f : -1.0f;  // second half adds, first subtracts
         const int toff = (ln.t & (P - 1)) * E;
 
+        if constexpr (PRIO) priority_for_loads();
         u32x4 wv[VPL];
         load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
@@ -281,7 +287,9 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
             u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
             u32x4 xv[VPL];
+            if constexpr (PRIO) priority_for_loads();
             load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
+            if constexpr (PRIO) priority_after_loads();
             // The table slice is an L2 hit.  With several wavefronts per row
             // it is fetched together with x, off the critical path behind the
             // row's barrier (H = 3072, d = 128: 69.6 -> 74.1 % of peak;
@@ -338,9 +346,10 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 //    fixed register.
 // The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot;
 // the wavefront reads the position's table rows once and the lanes take
-// their slices through LDS (TableLds).
+// their slices through LDS (TableLds).  PRIO raises the wave priority while
+// a row's loads issue.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool ODD>
+template <typename IO, int VPL, int WPR, bool ODD, bool PRIO>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_packed_kernel(const KArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
@@ -378,6 +387,7 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
     }
     auto vec_of = [&](int k) { return (k * WPR + ln.wave_in_row) * lw + l; };
 
+    if constexpr (PRIO) priority_for_loads();
     u32x4 wv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
@@ -397,6 +407,7 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
         u32x4 xv[VPL];
+        if constexpr (PRIO) priority_for_loads();
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vec_of(k);
@@ -410,6 +421,7 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
         // (a.half / G = vph <= 32 chunks per table)
         TableLds<G, Layout<WPR>::kThreads / kWave, kWave / 2> tabs(ln.slot * WPR + ln.wave_in_row);
         tabs.fetch(a.cos_tab + pos * a.half, a.sin_tab + pos * a.half, l, a.half / G);
+        if constexpr (PRIO) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
         tabs.share(l, a.half / G);
@@ -553,9 +565,10 @@ rmsnorm_rope_pair_kernel(const KArgs a) {
 // must be a multiple of kEpv (vectors never straddle heads).  SHARED:
 // head_dim / kEpv divides the lanes per row (every power-of-two head_dim up
 // to 64 kEpv), so all slots of a lane share one table offset and the row
-// needs a single table slice per lane.
+// needs a single table slice per lane.  PRIO raises the wave priority while
+// a row's loads issue.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool SHARED>
+template <typename IO, int VPL, int WPR, bool FULL, bool SHARED, bool PRIO>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_interleaved_kernel(const KArgs a) {
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
@@ -565,6 +578,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
     const Lane<WPR> ln;
     const int vph = a.vec_per_head;
 
+    if constexpr (PRIO) priority_for_loads();
     u32x4 wv[VPL];
     int toff[VPL];
     load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
@@ -582,6 +596,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
 
         u32x4 xv[VPL];
+        if constexpr (PRIO) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         const float* crow = a.cos_tab + pos * a.half;
         const float* srow = a.sin_tab + pos * a.half;
@@ -619,6 +634,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         if constexpr (WPR > 1) {
             if (!gathered) load_tables();
         }
+        if constexpr (PRIO) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
         if constexpr (kGather) {
@@ -665,16 +681,17 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
 // modulation rows are shared by every row of a sample and come from L2.  A
 // null scale reads as +0 (factor exactly 1) and a null shift as -0
 // (x + -0 == x for every x, signed zeros included), so with both null the
-// result equals plain RMSNorm bit for bit.
+// result equals plain RMSNorm bit for bit.  Wave priority as for RMSNorm.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_adaln_kernel(const KArgs a) {
+    constexpr bool kPrio = WPR > 1 || PRIO;  // as for RMSNorm
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
-    if constexpr (WPR > 1) priority_for_loads();
+    if constexpr (kPrio) priority_for_loads();
     u32x4 wv[VPL];
     load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
 
@@ -703,13 +720,13 @@ rmsnorm_adaln_kernel(const KArgs a) {
             hv = (a.shift != nullptr && in) ? hr[v] : splat(IO::kNegZero);
         };
         u32x4 xv[VPL], svv[VPL], hvv[VPL];
-        if constexpr (WPR > 1) priority_for_loads();
+        if constexpr (kPrio) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         if constexpr (kEarly) {
 #pragma unroll
             for (int k = 0; k < VPL; ++k) mod_rows(k, svv[k], hvv[k]);
         }
-        if constexpr (WPR > 1) priority_after_loads();
+        if constexpr (kPrio) priority_after_loads();
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
 

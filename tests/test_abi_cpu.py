@@ -612,3 +612,28 @@ def test_kernel_choice_always_covers_the_row():
             "rmsnorm_rope_interleaved_kernel", "rmsnorm_rope_interleaved_kernel(shared)",
             "rmsnorm_general_kernel", "rmsnorm_long_kernel", "rmsnorm_split_kernels",
             "rmsnorm_short_kernel"} <= seen, seen
+
+
+@pytest.mark.parametrize("op,rows,hidden,heads,head_dim,dtype,want", [
+    # rows of several wavefronts: always (RMSNorm, AdaLN); never (RoPE)
+    (ltx.OP_RMSNORM, 16384, 3072, 0, 0, ltx.BF16, "always"),
+    (ltx.OP_ADALN, 16384, 3072, 0, 0, ltx.BF16, "always"),
+    (ltx.OP_ROPE, 16384, 3072, 24, 128, ltx.BF16, "never"),
+    (ltx.OP_ROPE_INTERLEAVED, 16384, 3072, 24, 128, ltx.BF16, "never"),
+    # one-wavefront rows: when the grid is resident at once
+    (ltx.OP_RMSNORM, 8192, 2048, 0, 0, ltx.BF16, "one_wave"),
+    (ltx.OP_ADALN, 8192, 2048, 0, 0, ltx.F16, "one_wave"),
+    (ltx.OP_ROPE, 8192, 2048, 32, 64, ltx.BF16, "one_wave"),
+    (ltx.OP_ROPE_INTERLEAVED, 8192, 2048, 32, 64, ltx.BF16, "one_wave"),
+    (ltx.OP_ROPE, 8192, 1152, 16, 72, ltx.BF16, "one_wave"),
+    # the general kernel always; the pair-in-lane RoPE never
+    (ltx.OP_RMSNORM, 16384, 3076, 0, 0, ltx.BF16, "always"),
+    (ltx.OP_ROPE, 8192, 2560, 8, 320, ltx.BF16, "never"),
+])
+def test_describe_load_priority(op, rows, hidden, heads, head_dim, dtype, want):
+    """The launch line states when the kernel raises wave priority for its
+    loads; the segmented-row, two-pass and split kernels carry no such field."""
+    name, f = _describe(op, hidden, heads, head_dim, dtype, rows=rows)
+    assert f["load_priority"] == want, (name, f)
+    for args in [(ltx.OP_RMSNORM, 8192, 128), (ltx.OP_RMSNORM, 4, 1 << 20), (ltx.OP_RMSNORM, 512, 131072)]:
+        assert "load_priority" not in ltx.ltxnorm_describe_launch(*args), args

@@ -774,3 +774,63 @@ def test_short_rows_invariants():
     xt = dev_bf16(x)
     ltx.rmsnorm_rope(xt, dev_bf16(w), dev_f32(c), dev_f32(s), 1, 128, 1e-6, out=xt)
     assert np.array_equal(host_bits(xt), ref)
+
+
+# One-wavefront rows: a launch whose whole grid is resident at once takes the
+# instance that raises the wave priority for its loads (load_priority=one_wave
+# in the describe line); a larger launch of the same shape takes the plain
+# instance.  Priority changes timing only: the first rows of a large call and
+# the same rows called alone must agree bit for bit, and both with the oracle.
+ONE_WAVE = [
+    ("bf16", "rms", 2048, 0), ("f16", "rms", 1024, 0), ("f32", "rms", 1024, 0),
+    ("bf16", "adaln", 2048, 0), ("f32", "adaln", 512, 0),
+    ("bf16", "half", 2048, 64),       # power-of-two half heads (lane exchange)
+    ("bf16", "il", 2048, 64),         # interleaved, one table slice per row
+    ("bf16", "il", 1152, 72),         # interleaved, a table slice per slot
+    ("bf16", "half", 1152, 72),       # heads packed into wavefronts, odd groups
+    ("bf16", "half", 1280, 80),       # heads packed into wavefronts, whole vectors
+]
+
+
+@pytest.mark.parametrize("dtype,op,hidden,d", ONE_WAVE)
+def test_one_wave_priority_instances_agree(dtype, op, hidden, d):
+    small, big = 1024, 16384   # 256 workgroups of 4 rows; 4096 (more than any device holds at once)
+    heads = hidden // d if d else 0
+    desc = ltx.ltxnorm_describe_launch(_OPS[op], big, hidden, heads, d, _DT[dtype])
+    announce(f"one-wave priority {dtype} {op} hidden={hidden} d={d} -> {desc}")
+    assert " wavefronts_per_row=1 " in desc and "load_priority=one_wave" in desc, desc
+    seed = 7 * hidden + d
+    x = datagen.make_x(big, hidden, seed=seed, stream=1, dtype=dtype)
+    w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
+    rps = 512
+    sc = datagen.make_x(big // rps, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(big // rps, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    c, s_ = datagen.rope_tables(3000, d) if d else (None, None)
+
+    def call(rows):
+        xt, wt = dev_bf16(x[:rows]), dev_bf16(w)
+        if op == "rms":
+            y = ltx.rmsnorm(xt, wt, 1e-6)
+        elif op == "adaln":
+            n = -(-rows // rps)
+            y = ltx.rmsnorm_adaln(xt, wt, dev_bf16(sc[:n]), dev_bf16(sh[:n]), 1e-6, rows_per_sample=rps)
+        else:
+            y = ltx.rmsnorm_rope(xt, wt, dev_f32(c), dev_f32(s_), heads, d, 1e-6, interleaved=(op == "il"))
+        b = host_bits(y)
+        return b.view(np.uint32) if b.dtype == np.float32 else b.view(np.uint16)
+
+    alone = call(small)
+    assert np.array_equal(alone, call(big)[:small])
+    xs = x[:small]
+    if op == "rms":
+        ref32, ref = ORC.round(ORC.rmsnorm(xs, w, 1e-6), kind(xs))
+        mag = None
+    elif op == "adaln":
+        y, mag = ORC.rmsnorm_adaln(xs, w, sc[:small // rps], sh[:small // rps], rps, 1e-6, with_mag=True)
+        ref32, ref = ORC.round(y, kind(xs))
+    else:
+        y, mag = ORC.rmsnorm_rope(xs, w, c, s_, heads, d, 1e-6, with_mag=True, interleaved=(op == "il"))
+        ref32, ref = ORC.round(y, kind(xs))
+    got = {"f32": alone.view(np.float32), "f16": alone.view(np.float16)}.get(dtype, alone)
+    rep = compare(got, ref, mag, ref32)
+    assert rep["pass"], rep
