@@ -324,6 +324,8 @@ struct KArgs {
 //    7.84 us; [4096 x 2048] RMSNorm 7.89 -> 6.63 us).  On grids of several
 //    waves of workgroups the same instances ran 2-9 % slower, and the
 //    short-row kernel was slower either way, so those launches do not use it.
+//    Rotate-half RoPE also has one-wavefront priority instances with the
+//    weight in LDS (flag WL), which fit 8192 rows of hidden 2048 at once.
 __device__ __forceinline__ void priority_for_loads() { __builtin_amdgcn_s_setprio(3); }
 __device__ __forceinline__ void priority_after_loads() { __builtin_amdgcn_s_setprio(0); }
 

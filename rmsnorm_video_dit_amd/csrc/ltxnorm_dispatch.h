@@ -75,37 +75,42 @@ inline ltxnorm_status launch(const void* fn, int threads, int rpb, const KArgs& 
     return e == hipSuccess ? LTXNORM_OK : LTXNORM_ERR_HIP;
 }
 
-// One launcher per kernel family: fn<WPR, PER, FULL, PRIO>() picks the
+// One launcher per kernel family: fn<WPR, PER, FULL, PRIO, WL>() picks the
 // instance; kResident asks for the grid capped at the resident capacity;
 // kOneWavePrio says that the family has one-wavefront instances that raise
 // the wave priority for their loads (PRIO), taken when the whole grid is
-// resident at once.
+// resident at once; kOneWaveLds that it also has such instances with the
+// weight in LDS (WL), which fit more rows at once.
 template <typename IO>
 struct RmsL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_kernel<IO, PER, WPR, FULL, PRIO>; }
 };
 template <typename IO>
 struct RopeXorL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    template <int WPR, int PER, bool FULL, bool PRIO>
-    static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO>; }
+    static constexpr bool kOneWaveLds = true;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
+    static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO, WL>; }
 };
 template <typename IO>
 struct RopePairL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = false;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_rope_pair_kernel<IO, PER, WPR, FULL>; }
 };
 template <typename IO, bool SHARED>
 struct RopeIlL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() {
         return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED, PRIO>;
     }
@@ -114,14 +119,16 @@ template <typename IO>
 struct AdaL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL, PRIO>; }
 };
 template <typename IO, bool ODD>
 struct RopePackedL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>; }
 };
 // The general kernel masks every row itself: FULL does not select anything.
@@ -129,7 +136,8 @@ template <typename IO, GOp OP>
 struct GeneralL {
     static constexpr bool kResident = true;
     static constexpr bool kOneWavePrio = false;
-    template <int WPR, int PER, bool FULL, bool PRIO>
+    static constexpr bool kOneWaveLds = false;
+    template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_general_kernel<IO, OP, PER, WPR>; }
 };
 
@@ -155,7 +163,13 @@ ltxnorm_status by_per(const Plan& p, const KArgs& a, size_t lds_per_row, hipStre
             if constexpr (WPR == 1 && LN::kOneWavePrio) {
                 const void* fp = p.full ? LN::template fn<WPR, LO, true, true>()
                                         : LN::template fn<WPR, LO, false, true>();
-                if (fits_one_wave(fp, kT, kRpb, a.rows, lds, s)) fn = fp;
+                if (fits_one_wave(fp, kT, kRpb, a.rows, lds, s)) {
+                    fn = fp;
+                } else if constexpr (LN::kOneWaveLds) {
+                    const void* fl = p.full ? LN::template fn<WPR, LO, true, true, true>()
+                                            : LN::template fn<WPR, LO, false, true, true>();
+                    if (fits_one_wave(fl, kT, kRpb, a.rows, lds, s)) fn = fl;
+                }
             }
             return launch(fn, kT, kRpb, a, lds, s, LN::kResident);
         }

@@ -254,15 +254,24 @@ rmsnorm_short_kernel(const KArgs a) {
 // the whole grid is resident and compute is not hidden behind later loads).  A lane's half
 // (bit P of t) and its table slice (floats kEpv * (t mod P) .. + kEpv) do not
 // depend on the slot, so each lane reads one table slice per row.  PRIO
-// raises the wave priority while a row's loads issue.
+// raises the wave priority while a row's loads issue.  WL (one-wavefront
+// rows with PRIO only) keeps the weight in LDS, once per workgroup, instead
+// of in every wavefront's registers: 4 vectors per lane then take 60 VGPRs
+// instead of 75, 8 wavefronts per SIMD instead of 6, so that a launch of
+// 8192 rows is resident at once and can take the priority (bf16
+// [8192 x 2048] 13.36 -> 12.38 us; where the register-weight instance
+// already fits, LDS weight measured 1-3 % slower, so the launch prefers it).
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_xor_kernel(const KArgs a) {
+    static_assert(!WL || (PRIO && WPR == 1), "LDS weight: one-wavefront priority instances only");
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
+    // one array for every copy of the row loop below (one per P)
+    __shared__ u32x4 wlds[WL ? VPL * kWave : 1];
     // one copy of the row loop per partner distance P (a scalar branch at
     // entry): inside it every exchange is straight-line DPP or lane-swap
     // code, and each copy is register-allocated on its own (one loop with a
@@ -273,8 +282,16 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
         const int toff = (ln.t & (P - 1)) * E;
 
         if constexpr (PRIO) priority_for_loads();
-        u32x4 wv[VPL];
-        load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+        u32x4 wv[WL ? 1 : VPL];
+        if constexpr (WL) {
+            // every slot of the row's lanes, ones past the row
+            for (int v = threadIdx.x; v < VPL * kWave; v += Layout<WPR>::kThreads)
+                wlds[v] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v]
+                                                         : splat(IO::kOne);
+            __syncthreads();
+        } else {
+            load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+        }
 
         int parity = 0;
         for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
@@ -315,10 +332,17 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
                 const int v = k * L + ln.t;
                 const bool in = (FULL || v < a.nvec) && (WPR == 1 || active);
                 keep_packed(xv[k]);
-                keep_packed(wv[k]);
                 float own[E], g[E], o[E];
-                IO::widen(xv[k], own);
-                IO::widen(wv[k], g);
+                if constexpr (WL) {
+                    u32x4 wk = wlds[v];
+                    keep_packed(wk);
+                    IO::widen(xv[k], own);
+                    IO::widen(wk, g);
+                } else {
+                    keep_packed(wv[k]);
+                    IO::widen(xv[k], own);
+                    IO::widen(wv[k], g);
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
                 // the partner lane's normalised values, exact binary32 bits

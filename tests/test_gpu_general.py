@@ -781,23 +781,28 @@ def test_short_rows_invariants():
 # in the describe line); a larger launch of the same shape takes the plain
 # instance.  Priority changes timing only: the first rows of a large call and
 # the same rows called alone must agree bit for bit, and both with the oracle.
+# (dtype, op, hidden, head_dim, rows called alone)
 ONE_WAVE = [
-    ("bf16", "rms", 2048, 0), ("f16", "rms", 1024, 0), ("f32", "rms", 1024, 0),
-    ("bf16", "adaln", 2048, 0), ("f32", "adaln", 512, 0),
-    ("bf16", "half", 2048, 64),       # power-of-two half heads (lane exchange)
-    ("bf16", "il", 2048, 64),         # interleaved, one table slice per row
-    ("bf16", "il", 1152, 72),         # interleaved, a table slice per slot
-    ("bf16", "half", 1152, 72),       # heads packed into wavefronts, odd groups
-    ("bf16", "half", 1280, 80),       # heads packed into wavefronts, whole vectors
+    ("bf16", "rms", 2048, 0, 1024), ("f16", "rms", 1024, 0, 1024), ("f32", "rms", 1024, 0, 1024),
+    ("bf16", "adaln", 2048, 0, 1024), ("f32", "adaln", 512, 0, 1024),
+    ("bf16", "half", 2048, 64, 1024),   # power-of-two half heads (lane exchange)
+    ("bf16", "il", 2048, 64, 1024),     # interleaved, one table slice per row
+    ("bf16", "il", 1152, 72, 1024),     # interleaved, a table slice per slot
+    ("bf16", "half", 1152, 72, 1024),   # heads packed into wavefronts, odd groups
+    ("bf16", "half", 1280, 80, 1024),   # heads packed into wavefronts, whole vectors
+    # lane exchange at more rows than the register-weight instance holds at
+    # once: the instance with the weight in LDS (4, 3 and 4 masked vectors
+    # per lane)
+    ("bf16", "half", 2048, 64, 8192), ("f16", "half", 1536, 64, 8192), ("bf16", "half", 2032, 16, 7000),
 ]
 
 
-@pytest.mark.parametrize("dtype,op,hidden,d", ONE_WAVE)
-def test_one_wave_priority_instances_agree(dtype, op, hidden, d):
-    small, big = 1024, 16384   # 256 workgroups of 4 rows; 4096 (more than any device holds at once)
+@pytest.mark.parametrize("dtype,op,hidden,d,small", ONE_WAVE)
+def test_one_wave_priority_instances_agree(dtype, op, hidden, d, small):
+    big = 16384   # 4096 workgroups of 4 rows: more than any device holds at once
     heads = hidden // d if d else 0
     desc = ltx.ltxnorm_describe_launch(_OPS[op], big, hidden, heads, d, _DT[dtype])
-    announce(f"one-wave priority {dtype} {op} hidden={hidden} d={d} -> {desc}")
+    announce(f"one-wave priority {dtype} {op} hidden={hidden} d={d} rows={small} -> {desc}")
     assert " wavefronts_per_row=1 " in desc and "load_priority=one_wave" in desc, desc
     seed = 7 * hidden + d
     x = datagen.make_x(big, hidden, seed=seed, stream=1, dtype=dtype)
@@ -826,7 +831,7 @@ def test_one_wave_priority_instances_agree(dtype, op, hidden, d):
         ref32, ref = ORC.round(ORC.rmsnorm(xs, w, 1e-6), kind(xs))
         mag = None
     elif op == "adaln":
-        y, mag = ORC.rmsnorm_adaln(xs, w, sc[:small // rps], sh[:small // rps], rps, 1e-6, with_mag=True)
+        y, mag = ORC.rmsnorm_adaln(xs, w, sc[:-(-small // rps)], sh[:-(-small // rps)], rps, 1e-6, with_mag=True)
         ref32, ref = ORC.round(y, kind(xs))
     else:
         y, mag = ORC.rmsnorm_rope(xs, w, c, s_, heads, d, 1e-6, with_mag=True, interleaved=(op == "il"))
