@@ -230,8 +230,9 @@ typedef enum ltxnorm_op {
  * the kernel's wavefronts raise their priority while a row's loads issue:
  * "always", "never", or "one_wave": only when the launch's whole grid is
  * resident on the device at once (decided at launch from the device's
- * occupancy for that instance; rotate-half RoPE then may hold its weight
- * in 4 KB of LDS per workgroup instead of registers, so that more rows fit).
+ * occupancy for that instance; rotate-half RoPE then may hold its weight,
+ * and AdaLN does hold it, in 4 KB of LDS per workgroup instead of
+ * registers, so that more rows fit).
  * It changes timing only, never a result bit.  Rows of up to 160 vectors may share wavefronts instead, in
  * segments of a few lanes:
  *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2

@@ -325,7 +325,8 @@ struct KArgs {
 //    waves of workgroups the same instances ran 2-9 % slower, and the
 //    short-row kernel was slower either way, so those launches do not use it.
 //    Rotate-half RoPE also has one-wavefront priority instances with the
-//    weight in LDS (flag WL), which fit 8192 rows of hidden 2048 at once.
+//    weight in LDS (flag WL), and AdaLN's priority instances keep theirs
+//    there: both fit 8192 rows of hidden 2048 at once.
 __device__ __forceinline__ void priority_for_loads() { __builtin_amdgcn_s_setprio(3); }
 __device__ __forceinline__ void priority_after_loads() { __builtin_amdgcn_s_setprio(0); }
 

@@ -794,6 +794,9 @@ ONE_WAVE = [
     # once: the instance with the weight in LDS (4, 3 and 4 masked vectors
     # per lane)
     ("bf16", "half", 2048, 64, 8192), ("f16", "half", 1536, 64, 8192), ("bf16", "half", 2032, 16, 7000),
+    # AdaLN's priority instance (weight in LDS, modulation after the
+    # reduction) at the most rows it holds at once, whole and masked
+    ("bf16", "adaln", 2048, 0, 8192), ("f32", "adaln", 1024, 0, 8192), ("f16", "adaln", 2040, 0, 6000),
 ]
 
 
