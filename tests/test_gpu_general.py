@@ -446,14 +446,16 @@ def test_max_hidden(op, dtype):
 
 def test_graph_capture_replays():
     """Capture one call of each operation (vector, head-packed, general,
-    split and two-pass kernels) into a graph; replay it three times with new
-    inputs written eagerly between replays; every replay equals the eager
-    result."""
+    split and two-pass kernels; one-wavefront rows through the wave-priority
+    instances, the one with the weight in LDS, and the plain instance of a
+    launch too large to be resident at once) into a graph; replay it three
+    times with new inputs written eagerly between replays; every replay
+    equals the eager result."""
     announce("graph capture")
     shapes = [("rms", 512, 2048, 0), ("adaln", 512, 2048, 0), ("half", 512, 2048, 64),
               ("il", 512, 2048, 64), ("half", 512, 1152, 72), ("rms", 256, 3076, 0),
               ("rms", 2, 70001, 0), ("adaln", 4, 65544, 0), ("il", 3, 255 * 258, 258),
-              ("half", 2, 2 * 40000, 40000)]
+              ("half", 2, 2 * 40000, 40000), ("half", 8192, 2048, 64), ("rms", 16384, 1024, 0)]
     s = torch.cuda.Stream()
     bufs = []
     for op, rows, hidden, d in shapes:
