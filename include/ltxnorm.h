@@ -226,14 +226,16 @@ typedef enum ltxnorm_op {
  * buf, truncated to len bytes, for example
  *     "rmsnorm_kernel wavefronts_per_row=3 vectors_per_lane=2 rows_per_block=2
  *      threads=384 lds_bytes=0 load_priority=always"
- * (the kernel names are those a profiler shows).  load_priority says when
- * the kernel's wavefronts raise their priority while a row's loads issue:
- * "always", "never", or "one_wave": only when the launch's whole grid is
- * resident on the device at once (decided at launch from the device's
- * occupancy for that instance; rotate-half RoPE then may hold its weight,
- * and AdaLN does hold it, in 4 KB of LDS per workgroup instead of
- * registers, so that more rows fit).
- * It changes timing only, never a result bit.  Rows of up to 160 vectors may share wavefronts instead, in
+ * (the kernel names are those a profiler shows; lds_bytes is the dynamic
+ * LDS the launch requests per workgroup, not the kernels' fixed LDS for
+ * cross-wavefront sums, table rows or a staged weight).  load_priority
+ * says when the kernel's wavefronts raise their priority while a row's
+ * loads issue: "always", "never", or "one_wave": only when the launch's
+ * whole grid is resident on the device at once (decided at launch from the
+ * device's occupancy for that instance; rotate-half RoPE then may hold its
+ * weight, and AdaLN does hold it, in 4 KB of LDS per workgroup instead of
+ * registers, so that more rows fit).  It changes timing only, never a
+ * result bit.  Rows of up to 160 vectors may share wavefronts instead, in
  * segments of a few lanes:
  *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2
  *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
