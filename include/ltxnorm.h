@@ -235,8 +235,12 @@ typedef enum ltxnorm_op {
  * device's occupancy for that instance; rotate-half RoPE then may hold its
  * weight, and AdaLN does hold it, in 4 KB of LDS per workgroup instead of
  * registers, so that more rows fit).  It changes timing only, never a
- * result bit.  Rows of up to 160 vectors may share wavefronts instead, in
- * segments of a few lanes:
+ * result bit.  An RMSNorm line of 3 or 4 wavefronts x 2 vectors ends in
+ * "one_wave_vectors_per_lane=6" (or 8): when the whole grid then fits on the
+ * device at once, one wavefront takes each row with that many vectors per
+ * lane instead, adding the squares in the same order, so the result bits
+ * do not depend on which of the two a call takes.  Rows of up to 160
+ * vectors may share wavefronts instead, in segments of a few lanes:
  *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2
  *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
  * The general kernel's line ends in "load_priority=always grid=resident":

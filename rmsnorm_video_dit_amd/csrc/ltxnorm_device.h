@@ -439,6 +439,32 @@ __device__ __forceinline__ float sum_squares(const u32x4* xv) {
     return part;
 }
 
+// Row total of a row held by one wavefront (VPL vectors per lane, vector
+// k * 64 + lane in slot k) in the order in which VW wavefronts of VPL / VW
+// vectors per lane would add it: lane l of virtual wavefront j would hold
+// vectors (k * VW + j) * 64 + l, k = 0 .. VPL / VW - 1, which are this
+// lane's slots k * VW + j.  Each virtual wavefront's partial is the same
+// fma chain, reduced by the same wave_sum, and the totals are added in
+// row_sum's order, so the result has the bits of the VW-wavefront split.
+template <typename IO, int VPL, int VW>
+__device__ __forceinline__ float split_order_row_sum(const u32x4* xv) {
+    static_assert(VPL % VW == 0, "whole vectors per virtual wavefront");
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPL / VW; ++k) {
+            float f[IO::kEpv];
+            IO::widen(xv[k * VW + j], f);
+#pragma unroll
+            for (int e = 0; e < IO::kEpv; ++e) part = fmaf(f[e], f[e], part);
+        }
+        s += wave_sum(part);
+    }
+    return s;
+}
+
 // Weight slice (ones for a null weight).
 template <typename IO, int VPL, int L, bool FULL>
 __device__ __forceinline__ void load_weight(u32x4* wv, const void* w, int t, int nvec) {

@@ -195,6 +195,26 @@ ltxnorm_status by_per_also(const Plan& p, const KArgs& a, size_t lds_per_row, hi
 // adds four wavefronts with SPREAD..PER4 (plan_wide_xor); ALSO4 adds
 // ALSO4 items per lane at 4..15 wavefronts (plan_wide_xor past 768
 // vectors).  lds_per_row: dynamic LDS bytes per row slot of the block.
+// RMSNorm rows of 3 or 4 wavefronts x 2 vectors per lane: the one-wavefront
+// instance of 6 or 8 vectors per lane that adds the squares in the same
+// order (split_order_row_sum), raises the wave priority for its loads and
+// keeps the weight in LDS, when its whole grid is resident at once;
+// nullptr otherwise.  bf16 [8192 x 3072] 18.2 -> 17.3 us, [6144 x 3072]
+// 14.5 -> 12.5 us, [4096 x 4096] 13.4 -> 11.3 us, [8192 x 2560] 15.6 ->
+// 14.7 us; launches of more rows keep the split.
+template <typename IO>
+const void* rms_one_wave_split(const Plan& p, const KArgs& a, hipStream_t s) {
+    if (p.per != 2 || (p.wpr != 3 && p.wpr != 4)) return nullptr;
+    const void* fp;
+    if (p.wpr == 3)
+        fp = p.full ? (const void*)&rmsnorm_kernel<IO, 6, 1, true, true, 3>
+                    : (const void*)&rmsnorm_kernel<IO, 6, 1, false, true, 3>;
+    else
+        fp = p.full ? (const void*)&rmsnorm_kernel<IO, 8, 1, true, true, 4>
+                    : (const void*)&rmsnorm_kernel<IO, 8, 1, false, true, 4>;
+    return fits_one_wave(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a.rows, 0, s) ? fp : nullptr;
+}
+
 template <typename LN, int ONE, int SPREAD, int MAXP, bool WIDE = false, int PER4 = SPREAD, int ALSO4 = 0>
 ltxnorm_status by_plan(const Plan& p, const KArgs& a, hipStream_t s, size_t lds_per_row = 0) {
     switch (p.wpr) {
@@ -297,7 +317,10 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
             samples * r.hidden, (float)r.hidden, r.eps};
     switch (c.kernel) {
         case Kernel::kNone: return LTXNORM_OK;
-        case Kernel::kRmsNorm: return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
+        case Kernel::kRmsNorm:
+            if (const void* fp = rms_one_wave_split<IO>(c.plan, a, stream))
+                return launch(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a, 0, stream);
+            return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
         case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3, 4>(c.plan, a, stream);
         case Kernel::kRopePacked:

@@ -14,19 +14,33 @@ namespace {
 // lane's every slot is inside the row (no masking).  Rows of several
 // wavefronts raise the wave priority while their loads issue; PRIO does the
 // same for one-wavefront rows (the launch asks for it when the whole grid is
-// resident at once).
+// resident at once).  VW > 1 (one-wavefront priority instances of 6 or 8
+// vectors per lane) adds the squares in the order of VW wavefronts of
+// VPL / VW vectors, the split such rows take otherwise, so the bits do not
+// depend on which of the two a launch takes; these instances keep the
+// weight in LDS, once per workgroup.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, int VW = 1>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_kernel(const KArgs a) {
+    static_assert(VW == 1 || (WPR == 1 && PRIO), "split-order sums: one-wavefront priority instances");
     constexpr bool kPrio = WPR > 1 || PRIO;
+    constexpr bool kWl = VW > 1;  // weight in LDS
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
     const Lane<WPR> ln;
     if constexpr (kPrio) priority_for_loads();
-    u32x4 wv[VPL];
-    load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+    __shared__ u32x4 wlds[kWl ? VPL * kWave : 1];
+    u32x4 wv[kWl ? 1 : VPL];
+    if constexpr (kWl) {
+        // every slot of the row's lanes, ones past the row
+        for (int v = threadIdx.x; v < VPL * kWave; v += Layout<WPR>::kThreads)
+            wlds[v] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+        __syncthreads();
+    } else {
+        load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+    }
 
     int parity = 0;
     for (int64_t base = (int64_t)blockIdx.x * RPB; base < a.rows;
@@ -41,8 +55,14 @@ rmsnorm_kernel(const KArgs a) {
         if constexpr (kPrio) priority_for_loads();
         load_row<VPL, L, FULL, WPR>(xv, xr, ln.t, a.nvec, active);
         if constexpr (kPrio) priority_after_loads();
-        const float part = sum_squares<IO, VPL>(xv);
-        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        float sum_sq;
+        if constexpr (VW > 1) {
+            sum_sq = split_order_row_sum<IO, VPL, VW>(xv);
+        } else {
+            const float part = sum_squares<IO, VPL>(xv);
+            sum_sq = row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity);
+        }
+        const float rstd = rstd_of(sum_sq, a.hidden_f, a.eps);
 
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -51,8 +71,14 @@ rmsnorm_kernel(const KArgs a) {
             float f[E], g[E];
             keep_packed(xv[k]);
             IO::widen(xv[k], f);
-            keep_packed(wv[k]);
-            IO::widen(wv[k], g);
+            if constexpr (kWl) {
+                u32x4 wk = wlds[v];
+                keep_packed(wk);
+                IO::widen(wk, g);
+            } else {
+                keep_packed(wv[k]);
+                IO::widen(wv[k], g);
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) f[e] = (f[e] * rstd) * g[e];
             if (in) store_stream(yr + v, IO::narrow(f));

@@ -637,3 +637,21 @@ def test_describe_load_priority(op, rows, hidden, heads, head_dim, dtype, want):
     assert f["load_priority"] == want, (name, f)
     for args in [(ltx.OP_RMSNORM, 8192, 128), (ltx.OP_RMSNORM, 4, 1 << 20), (ltx.OP_RMSNORM, 512, 131072)]:
         assert "load_priority" not in ltx.ltxnorm_describe_launch(*args), args
+
+
+@pytest.mark.parametrize("dtype,hidden,want", [
+    (ltx.BF16, 3072, 6), (ltx.BF16, 2312, 6), (ltx.BF16, 4096, 8), (ltx.F16, 3584, 8), (ltx.F32, 2048, 8),
+    (ltx.F32, 1028, 6), (ltx.BF16, 2048, None), (ltx.BF16, 5120, None), (ltx.BF16, 3076, None),
+])
+def test_describe_one_wave_regroup(dtype, hidden, want):
+    """RMSNorm rows of 3 or 4 wavefronts x 2 vectors name the one-wavefront
+    form they take when the whole grid is resident at once; other splits,
+    the general kernel and the other operations do not."""
+    name, f = _describe(ltx.OP_RMSNORM, hidden, dtype=dtype, rows=8192)
+    if want is None:
+        assert "one_wave_vectors_per_lane" not in f, (name, f)
+    else:
+        assert name == "rmsnorm_kernel" and f["vectors_per_lane"] == "2", (name, f)
+        assert int(f["one_wave_vectors_per_lane"]) == want == 2 * int(f["wavefronts_per_row"]), (name, f)
+    for op, h, hd, d in [(ltx.OP_ADALN, 3072, 0, 0), (ltx.OP_ROPE, 3072, 24, 128), (ltx.OP_ROPE_INTERLEAVED, 3072, 24, 128)]:
+        assert "one_wave_vectors_per_lane" not in ltx.ltxnorm_describe_launch(op, 8192, h, hd, d), op

@@ -781,8 +781,10 @@ def test_short_rows_invariants():
 # One-wavefront rows: a launch whose whole grid is resident at once takes the
 # instance that raises the wave priority for its loads (load_priority=one_wave
 # in the describe line); a larger launch of the same shape takes the plain
-# instance.  Priority changes timing only: the first rows of a large call and
-# the same rows called alone must agree bit for bit, and both with the oracle.
+# instance.  RMSNorm rows of 3 or 4 wavefronts likewise take one wavefront of
+# 6 or 8 vectors per lane (one_wave_vectors_per_lane), adding in the split's
+# order.  Neither changes a bit: the first rows of a large call and the same
+# rows called alone must agree bit for bit, and both with the oracle.
 # (dtype, op, hidden, head_dim, rows called alone)
 ONE_WAVE = [
     ("bf16", "rms", 2048, 0, 1024), ("f16", "rms", 1024, 0, 1024), ("f32", "rms", 1024, 0, 1024),
@@ -799,6 +801,11 @@ ONE_WAVE = [
     # AdaLN's priority instance (weight in LDS, modulation after the
     # reduction) at the most rows it holds at once, whole and masked
     ("bf16", "adaln", 2048, 0, 8192), ("f32", "adaln", 1024, 0, 8192), ("f16", "adaln", 2040, 0, 6000),
+    # RMSNorm rows of 3 or 4 wavefronts x 2 vectors: alone, one wavefront of
+    # 6 or 8 vectors per lane adding in the same order (whole and masked
+    # rows); inside the large call, the split itself
+    ("bf16", "rms", 3072, 0, 8192), ("bf16", "rms", 2560, 0, 8192), ("bf16", "rms", 4096, 0, 4096),
+    ("f16", "rms", 3584, 0, 6000), ("f32", "rms", 2048, 0, 8192), ("f32", "rms", 1028, 0, 8192),
 ]
 
 
@@ -808,7 +815,8 @@ def test_one_wave_priority_instances_agree(dtype, op, hidden, d, small):
     heads = hidden // d if d else 0
     desc = ltx.ltxnorm_describe_launch(_OPS[op], big, hidden, heads, d, _DT[dtype])
     announce(f"one-wave priority {dtype} {op} hidden={hidden} d={d} rows={small} -> {desc}")
-    assert " wavefronts_per_row=1 " in desc and "load_priority=one_wave" in desc, desc
+    assert ((" wavefronts_per_row=1 " in desc and "load_priority=one_wave" in desc)
+            or " one_wave_vectors_per_lane=" in desc), desc
     seed = 7 * hidden + d
     x = datagen.make_x(big, hidden, seed=seed, stream=1, dtype=dtype)
     w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
