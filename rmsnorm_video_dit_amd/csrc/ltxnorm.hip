@@ -252,14 +252,14 @@ LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, 
         const bool always = c.kernel == Kernel::kGeneral ||
                             ((c.kernel == Kernel::kRmsNorm || c.kernel == Kernel::kAdaLN) && c.plan.wpr > 1);
         const bool one_wave = c.plan.wpr == 1 && c.kernel != Kernel::kGeneral && c.kernel != Kernel::kRopePair;
-        // RMSNorm rows of 3 or 4 wavefronts x 2 vectors: one wavefront of
-        // 6 or 8 vectors per lane when the whole grid is resident at once
-        const bool regroup = c.kernel == Kernel::kRmsNorm && c.plan.per == 2 && (c.plan.wpr == 3 || c.plan.wpr == 4);
+        // rows of a few wavefronts: one wavefront of that many vectors per
+        // lane when the whole grid is resident at once
+        const int regroup = ltxnorm_detail::regroup_vectors(c.kernel, c.plan, rope ? (int)(head_dim / epv) : 0);
         char tail[64] = "";
         if (c.kernel == Kernel::kGeneral)
             std::snprintf(tail, sizeof(tail), " grid=resident");
         else if (regroup)
-            std::snprintf(tail, sizeof(tail), " one_wave_vectors_per_lane=%d", 2 * c.plan.wpr);
+            std::snprintf(tail, sizeof(tail), " one_wave_vectors_per_lane=%d", regroup);
         std::snprintf(buf, len, "%s wavefronts_per_row=%d %s=%d rows_per_block=%d threads=%d lds_bytes=%lld load_priority=%s%s",
                       name, c.plan.wpr, c.kernel == Kernel::kRopePair ? "pairs_per_lane" : "vectors_per_lane",
                       c.plan.per, rpb, ltxnorm_detail::kWave * c.plan.wpr * rpb,

@@ -330,6 +330,20 @@ struct KArgs {
 __device__ __forceinline__ void priority_for_loads() { __builtin_amdgcn_s_setprio(3); }
 __device__ __forceinline__ void priority_after_loads() { __builtin_amdgcn_s_setprio(0); }
 
+// One rotation term a * c + b * s in a fixed form: a * c rounded, then
+// fused with b * s (b is the partner value, which may still be on its way
+// from another lane).  Written out so that the compiler's contraction of
+// the plain expression, which may fuse either product and chooses per
+// instruction, cannot make two instances or two paths of the same row round
+// differently (a - b form passes -b).
+__device__ __forceinline__ float rot(float a, float c, float b, float s) { return fmaf(b, s, a * c); }
+
+// AdaLN modulation t * (1 + scale) + shift, fused in one fixed form for
+// the same reason.  A null scale (+0) and shift (-0) give t bit for bit.
+__device__ __forceinline__ float modulate(float t, float scale, float shift) {
+    return fmaf(t, 1.0f + scale, shift);
+}
+
 // Common prologue of every kernel: which row slot and lane this thread is.
 template <int WPR>
 struct Lane {

@@ -88,6 +88,9 @@ struct RmsL {
     static constexpr bool kOneWaveLds = false;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_kernel<IO, PER, WPR, FULL, PRIO>; }
+    // one wavefront of VPL vectors per lane adding in the order of VW
+    template <int VPL, bool FULL, int VW>
+    static const void* regroup() { return (const void*)&rmsnorm_kernel<IO, VPL, 1, FULL, true, VW>; }
 };
 template <typename IO>
 struct RopeXorL {
@@ -96,6 +99,8 @@ struct RopeXorL {
     static constexpr bool kOneWaveLds = true;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO, WL>; }
+    template <int VPL, bool FULL, int VW>
+    static const void* regroup() { return (const void*)&rmsnorm_rope_xor_kernel<IO, VPL, 1, FULL, true, true, VW>; }
 };
 template <typename IO>
 struct RopePairL {
@@ -114,6 +119,11 @@ struct RopeIlL {
     static const void* fn() {
         return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED, PRIO>;
     }
+    template <int VPL, bool FULL, int VW>
+    static const void* regroup() {
+        if constexpr (SHARED) return (const void*)&rmsnorm_rope_interleaved_kernel<IO, VPL, 1, FULL, true, true, VW>;
+        return nullptr;
+    }
 };
 template <typename IO>
 struct AdaL {
@@ -122,6 +132,8 @@ struct AdaL {
     static constexpr bool kOneWaveLds = false;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() { return (const void*)&rmsnorm_adaln_kernel<IO, PER, WPR, FULL, PRIO>; }
+    template <int VPL, bool FULL, int VW>
+    static const void* regroup() { return (const void*)&rmsnorm_adaln_kernel<IO, VPL, 1, FULL, true, VW>; }
 };
 template <typename IO, bool ODD>
 struct RopePackedL {
@@ -195,23 +207,26 @@ ltxnorm_status by_per_also(const Plan& p, const KArgs& a, size_t lds_per_row, hi
 // adds four wavefronts with SPREAD..PER4 (plan_wide_xor); ALSO4 adds
 // ALSO4 items per lane at 4..15 wavefronts (plan_wide_xor past 768
 // vectors).  lds_per_row: dynamic LDS bytes per row slot of the block.
-// RMSNorm rows of 3 or 4 wavefronts x 2 vectors per lane: the one-wavefront
-// instance of 6 or 8 vectors per lane that adds the squares in the same
-// order (split_order_row_sum), raises the wave priority for its loads and
-// keeps the weight in LDS, when its whole grid is resident at once;
-// nullptr otherwise.  bf16 [8192 x 3072] 18.2 -> 17.3 us, [6144 x 3072]
-// 14.5 -> 12.5 us, [4096 x 4096] 13.4 -> 11.3 us, [8192 x 2560] 15.6 ->
-// 14.7 us; launches of more rows keep the split.
-template <typename IO>
-const void* rms_one_wave_split(const Plan& p, const KArgs& a, hipStream_t s) {
-    if (p.per != 2 || (p.wpr != 3 && p.wpr != 4)) return nullptr;
-    const void* fp;
-    if (p.wpr == 3)
-        fp = p.full ? (const void*)&rmsnorm_kernel<IO, 6, 1, true, true, 3>
-                    : (const void*)&rmsnorm_kernel<IO, 6, 1, false, true, 3>;
-    else
-        fp = p.full ? (const void*)&rmsnorm_kernel<IO, 8, 1, true, true, 4>
-                    : (const void*)&rmsnorm_kernel<IO, 8, 1, false, true, 4>;
+// Rows of W wavefronts x P vectors per lane (the splits regroup_vectors
+// names for the kernel): the one-wavefront instance of W * P vectors per
+// lane that adds the squares in the W-wavefront order (split_order_row_sum),
+// raises the wave priority for its loads and keeps the weight in LDS, when
+// its whole grid is resident at once; nullptr otherwise.  RMSNorm bf16
+// [8192 x 3072] 18.2 -> 17.3 us, [6144 x 3072] 14.5 -> 12.5 us,
+// [4096 x 4096] 13.4 -> 11.3 us; launches of more rows keep the split.
+template <typename LN, int W, int P>
+const void* regroup_instance(bool full) {
+    return full ? LN::template regroup<W * P, true, W>() : LN::template regroup<W * P, false, W>();
+}
+template <typename LN, int W2P3, int W2P4, int W3P2, int W4P2>
+const void* one_wave_regroup(int vectors, const Plan& p, const KArgs& a, hipStream_t s) {
+    if (vectors == 0) return nullptr;
+    const void* fp = nullptr;
+    if constexpr (W2P3) if (p.wpr == 2 && p.per == 3) fp = regroup_instance<LN, 2, 3>(p.full);
+    if constexpr (W2P4) if (p.wpr == 2 && p.per == 4) fp = regroup_instance<LN, 2, 4>(p.full);
+    if constexpr (W3P2) if (p.wpr == 3 && p.per == 2) fp = regroup_instance<LN, 3, 2>(p.full);
+    if constexpr (W4P2) if (p.wpr == 4 && p.per == 2) fp = regroup_instance<LN, 4, 2>(p.full);
+    if (fp == nullptr) return nullptr;
     return fits_one_wave(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a.rows, 0, s) ? fp : nullptr;
 }
 
@@ -310,6 +325,7 @@ template <typename IO>
 ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
     constexpr int E = IO::kEpv;
     const Choice c = choose(op, r, E);
+    const int regroup = regroup_vectors(c.kernel, c.plan, r.head_dim / E);
     const int64_t samples = sample_count(r.rows, r.rows_per_sample);
     KArgs a{r.out, r.x, r.w, r.cos_tab, r.sin_tab, r.scale, r.shift, r.rows, r.seq_len,
             r.rows_per_sample, (int32_t)(r.hidden / E), (int32_t)(r.hidden / (2 * E)),
@@ -318,11 +334,17 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
     switch (c.kernel) {
         case Kernel::kNone: return LTXNORM_OK;
         case Kernel::kRmsNorm:
-            if (const void* fp = rms_one_wave_split<IO>(c.plan, a, stream))
+            if (const void* fp = one_wave_regroup<RmsL<IO>, 0, 0, 1, 1>(regroup, c.plan, a, stream))
                 return launch(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a, 0, stream);
             return by_plan<RmsL<IO>, 4, 2, kMaxVecPerLane>(c.plan, a, stream);
-        case Kernel::kAdaLN: return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
-        case Kernel::kRopeXor: return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3, 4>(c.plan, a, stream);
+        case Kernel::kAdaLN:
+            if (const void* fp = one_wave_regroup<AdaL<IO>, 1, 1, 0, 0>(regroup, c.plan, a, stream))
+                return launch(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a, 0, stream);
+            return by_plan<AdaL<IO>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
+        case Kernel::kRopeXor:
+            if (const void* fp = one_wave_regroup<RopeXorL<IO>, 1, 1, 0, 0>(regroup, c.plan, a, stream))
+                return launch(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a, 0, stream);
+            return by_plan<RopeXorL<IO>, 4, 2, kMaxVecPerLane, true, 3, 4>(c.plan, a, stream);
         case Kernel::kRopePacked:
             return by_plan<RopePackedL<IO, false>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopePackedOdd:
@@ -333,6 +355,8 @@ ltxnorm_status launch_op(Op op, const Request& r, hipStream_t stream) {
         case Kernel::kRopeInterleaved:
             return by_plan<RopeIlL<IO, false>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kRopeInterleavedShared:
+            if (const void* fp = one_wave_regroup<RopeIlL<IO, true>, 1, 0, 1, 1>(regroup, c.plan, a, stream))
+                return launch(fp, Layout<1>::kThreads, Layout<1>::kRowsPerBlock, a, 0, stream);
             return by_plan<RopeIlL<IO, true>, 4, 2, kMaxVecPerLane, true>(c.plan, a, stream);
         case Kernel::kShort:
             switch (op) {

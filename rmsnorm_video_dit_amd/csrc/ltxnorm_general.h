@@ -287,8 +287,8 @@ __device__ __forceinline__ void rope_interleaved_vec(const KArgs& a, const float
     }
 #pragma unroll
     for (int p = 0; p < E / 2; ++p) {
-        o[2 * p] = f[2 * p] * c[p] - f[2 * p + 1] * sn[p];
-        o[2 * p + 1] = f[2 * p + 1] * c[p] + f[2 * p] * sn[p];
+        o[2 * p] = rot(f[2 * p], c[p], -f[2 * p + 1], sn[p]);
+        o[2 * p + 1] = rot(f[2 * p + 1], c[p], f[2 * p], sn[p]);
     }
 }
 
@@ -428,7 +428,7 @@ rmsnorm_general_kernel(const KArgs a) {
                         // indices clamped into the row: every LDS read is in range
                         const int jj = valid ? j : 0;
                         const int pj = valid ? (hd < half ? j + half : j - half) : 0;
-                        o[e] = yrow[jj] * c[e] + yrow[pj] * sn[e];
+                        o[e] = rot(yrow[jj], c[e], yrow[pj], sn[e]);
                         if (++hd == d) hd = 0;
                     }
                     store_row_vec<IO>(a.out, g0, q, j0, H, IO::narrow(o));
@@ -461,7 +461,7 @@ rmsnorm_general_kernel(const KArgs a) {
                         IO::widen(sv, sc);
                         IO::widen(hv, sh);
 #pragma unroll
-                        for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+                        for (int e = 0; e < E; ++e) f[e] = modulate(f[e], sc[e], sh[e]);
                     }
                     if constexpr (OP == GOp::kRopeIl) {
                         float o[E];
@@ -586,7 +586,7 @@ __device__ __forceinline__ void apply_span(const KArgs& a, const RowSpan<IO::kEp
                 IO::widen(sv, sc);
                 IO::widen(hv, sh);
 #pragma unroll
-                for (int e = 0; e < E; ++e) f[e] = f[e] * (1.0f + sc[e]) + sh[e];
+                for (int e = 0; e < E; ++e) f[e] = modulate(f[e], sc[e], sh[e]);
             }
             if constexpr (OP == GOp::kRopeIl) {
                 float o[E];
@@ -699,8 +699,8 @@ rmsnorm_long_kernel(const KArgs a) {
                     const float yb = (xb[e] * rstd) * gb[e];
                     const float c = e < cnt ? crow[i0 + e] : 0.0f;
                     const float sn = e < cnt ? srow[i0 + e] : 0.0f;
-                    o1[e] = ya * c - yb * sn;
-                    o2[e] = yb * c + ya * sn;
+                    o1[e] = rot(ya, c, -yb, sn);
+                    o2[e] = rot(yb, c, ya, sn);
                 }
                 if (cnt == E && ((ea | eb) & (E - 1)) == 0) {
                     store_stream(static_cast<u32x4*>(a.out) + ea / E, IO::narrow(o1));

@@ -218,8 +218,8 @@ rmsnorm_short_kernel(const KArgs a) {
                 float o0[E], o1[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    o0[e] = f0[e] * c[0][e] + f1[e] * (sn[0][e] * -1.0f);
-                    o1[e] = f1[e] * c[0][e] + f0[e] * (sn[0][e] * 1.0f);
+                    o0[e] = rot(f0[e], c[0][e], f1[e], sn[0][e] * -1.0f);
+                    o1[e] = rot(f1[e], c[0][e], f0[e], sn[0][e] * 1.0f);
                 }
                 if (rin && l < a.nvec) store_stream(yr + l, IO::narrow(o0));
                 if (rin && S + l < a.nvec) store_stream(yr + S + l, IO::narrow(o1));
@@ -243,20 +243,20 @@ rmsnorm_short_kernel(const KArgs a) {
                 IO::widen(sv[k], sc);
                 IO::widen(hv[k], sh);
 #pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = f[e] * (1.0f + sc[e]) + sh[e];
+                for (int e = 0; e < E; ++e) o[e] = modulate(f[e], sc[e], sh[e]);
             } else if constexpr (OP == GOp::kRopeHalf) {
                 // the partner lane's normalised values; -sin in the first half
                 // (P <= S / 2 <= 16 here)
                 with_pow2(a.vec_per_half, [&](auto pc) {
                     constexpr int PC = decltype(pc)::value < 16 ? decltype(pc)::value : 16;
 #pragma unroll
-                    for (int e = 0; e < E; ++e) o[e] = f[e] * c[0][e] + xor_lane<PC>(f[e]) * (sn[0][e] * sgn);
+                    for (int e = 0; e < E; ++e) o[e] = rot(f[e], c[0][e], xor_lane<PC>(f[e]), sn[0][e] * sgn);
                 });
             } else if constexpr (OP == GOp::kRopeIl) {
 #pragma unroll
                 for (int j = 0; j < E / 2; ++j) {
-                    o[2 * j] = f[2 * j] * c[k][j] - f[2 * j + 1] * sn[k][j];
-                    o[2 * j + 1] = f[2 * j + 1] * c[k][j] + f[2 * j] * sn[k][j];
+                    o[2 * j] = rot(f[2 * j], c[k][j], -f[2 * j + 1], sn[k][j]);
+                    o[2 * j + 1] = rot(f[2 * j + 1], c[k][j], f[2 * j], sn[k][j]);
                 }
             } else {
 #pragma unroll
@@ -288,10 +288,11 @@ rmsnorm_short_kernel(const KArgs a) {
 // [8192 x 2048] 13.36 -> 12.38 us; where the register-weight instance
 // already fits, LDS weight measured 1-3 % slower, so the launch prefers it).
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL, int VW = 1>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_xor_kernel(const KArgs a) {
     static_assert(!WL || (PRIO && WPR == 1), "LDS weight: one-wavefront priority instances only");
+    static_assert(VW == 1 || WL, "split-order sums: LDS-weight instances");
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
@@ -344,8 +345,14 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
                 load_floats<E>(a.cos_tab + pos * a.half + toff, c);
                 load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
             }
-            const float part = sum_squares<IO, VPL>(xv);
-            const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+            float sum_sq;
+            if constexpr (VW > 1) {
+                sum_sq = split_order_row_sum<IO, VPL, VW>(xv);
+            } else {
+                const float part = sum_squares<IO, VPL>(xv);
+                sum_sq = row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity);
+            }
+            const float rstd = rstd_of(sum_sq, a.hidden_f, a.eps);
             if constexpr (WPR == 1) {
                 load_floats<E>(a.cos_tab + pos * a.half + toff, c);
                 load_floats<E>(a.sin_tab + pos * a.half + toff, ss);
@@ -373,7 +380,7 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
                 for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
                 // the partner lane's normalised values, exact binary32 bits
 #pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + xor_lane<P>(own[e]) * ss[e];
+                for (int e = 0; e < E; ++e) o[e] = rot(own[e], c[e], xor_lane<P>(own[e]), ss[e]);
                 if (in) store_stream(yr + v, IO::narrow(o));
             }
         }
@@ -503,7 +510,7 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
                 par[e + G] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, own[from1])));
             }
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = own[e] * c[e] + par[e] * ss[e];
+            for (int e = 0; e < E; ++e) o[e] = rot(own[e], c[e], par[e], ss[e]);
             if (in) store_stream(yr + v, IO::narrow(o));
         }
     }
@@ -596,8 +603,8 @@ rmsnorm_rope_pair_kernel(const KArgs a) {
             float o1[E], o2[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                o1[e] = ya[e] * c[e] - yb[e] * s[e];
-                o2[e] = yb[e] * c[e] + ya[e] * s[e];
+                o1[e] = rot(ya[e], c[e], -yb[e], s[e]);
+                o2[e] = rot(yb[e], c[e], ya[e], s[e]);
             }
             if (in) {
                 store_stream(yr + va[k], IO::narrow(o1));
@@ -618,9 +625,11 @@ rmsnorm_rope_pair_kernel(const KArgs a) {
 // needs a single table slice per lane.  PRIO raises the wave priority while
 // a row's loads issue.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool SHARED, bool PRIO>
+template <typename IO, int VPL, int WPR, bool FULL, bool SHARED, bool PRIO, int VW = 1>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_interleaved_kernel(const KArgs a) {
+    static_assert(VW == 1 || (SHARED && PRIO && WPR == 1), "split-order sums: shared-slice priority instances");
+    constexpr bool kWl = VW > 1;  // weight in LDS
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
@@ -629,9 +638,16 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
     const int vph = a.vec_per_head;
 
     if constexpr (PRIO) priority_for_loads();
-    u32x4 wv[VPL];
+    __shared__ u32x4 wlds[kWl ? VPL * kWave : 1];
+    u32x4 wv[kWl ? 1 : VPL];
     int toff[VPL];
-    load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+    if constexpr (kWl) {
+        for (int v = threadIdx.x; v < VPL * kWave; v += Layout<WPR>::kThreads)
+            wlds[v] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+        __syncthreads();
+    } else {
+        load_weight<IO, VPL, L, FULL>(wv, a.w, ln.t, a.nvec);
+    }
 #pragma unroll
     for (int k = 0; k < VPL; ++k) toff[k] = ((k * L + ln.t) % vph) * NP;
 
@@ -685,8 +701,14 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
             if (!gathered) load_tables();
         }
         if constexpr (PRIO) priority_after_loads();
-        const float part = sum_squares<IO, VPL>(xv);
-        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        float sum_sq;
+        if constexpr (VW > 1) {
+            sum_sq = split_order_row_sum<IO, VPL, VW>(xv);
+        } else {
+            const float part = sum_squares<IO, VPL>(xv);
+            sum_sq = row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity);
+        }
+        const float rstd = rstd_of(sum_sq, a.hidden_f, a.eps);
         if constexpr (kGather) {
             if (gathered) tabs.share(ln.lane, vph);
         }
@@ -708,16 +730,23 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
             const float* ck = c[kAll ? k : 0];
             const float* sk = sn[kAll ? k : 0];
             keep_packed(xv[k]);
-            keep_packed(wv[k]);
             float y[E], g[E], o[E];
-            IO::widen(xv[k], y);
-            IO::widen(wv[k], g);
+            if constexpr (kWl) {
+                u32x4 wk = wlds[v];
+                keep_packed(wk);
+                IO::widen(xv[k], y);
+                IO::widen(wk, g);
+            } else {
+                keep_packed(wv[k]);
+                IO::widen(xv[k], y);
+                IO::widen(wv[k], g);
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) y[e] = (y[e] * rstd) * g[e];
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                o[2 * j] = y[2 * j] * ck[j] - y[2 * j + 1] * sk[j];
-                o[2 * j + 1] = y[2 * j + 1] * ck[j] + y[2 * j] * sk[j];
+                o[2 * j] = rot(y[2 * j], ck[j], -y[2 * j + 1], sk[j]);
+                o[2 * j + 1] = rot(y[2 * j + 1], ck[j], y[2 * j], sk[j]);
             }
             if (in) store_stream(yr + v, IO::narrow(o));
         }
@@ -739,9 +768,10 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
 // 12.73 us; 4096 rows 7.91 -> 7.63, 6144 rows 11.52 -> 9.84, fp32 [8192 x
 // 1024] 13.86 -> 12.42 us).
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool PRIO>
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, int VW = 1>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_adaln_kernel(const KArgs a) {
+    static_assert(VW == 1 || (WPR == 1 && PRIO), "split-order sums: one-wavefront priority instances");
     constexpr bool kPrio = WPR > 1 || PRIO;  // as for RMSNorm
     constexpr bool kWl = PRIO && WPR == 1;   // weight in LDS
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
@@ -793,8 +823,14 @@ rmsnorm_adaln_kernel(const KArgs a) {
             for (int k = 0; k < VPL; ++k) mod_rows(k, svv[k], hvv[k]);
         }
         if constexpr (kPrio) priority_after_loads();
-        const float part = sum_squares<IO, VPL>(xv);
-        const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
+        float sum_sq;
+        if constexpr (VW > 1) {
+            sum_sq = split_order_row_sum<IO, VPL, VW>(xv);
+        } else {
+            const float part = sum_squares<IO, VPL>(xv);
+            sum_sq = row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity);
+        }
+        const float rstd = rstd_of(sum_sq, a.hidden_f, a.eps);
 
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -822,7 +858,7 @@ rmsnorm_adaln_kernel(const KArgs a) {
             IO::widen(sv, sc);
             IO::widen(hv, sh);
 #pragma unroll
-            for (int e = 0; e < E; ++e) f[e] = ((f[e] * rstd) * g[e]) * (1.0f + sc[e]) + sh[e];
+            for (int e = 0; e < E; ++e) f[e] = modulate((f[e] * rstd) * g[e], sc[e], sh[e]);
             if (in) store_stream(yr + v, IO::narrow(f));
         }
     }

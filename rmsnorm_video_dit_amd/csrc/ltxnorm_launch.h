@@ -329,6 +329,30 @@ inline Choice choose(Op op, const Request& r, int E) {
     return Choice{Kernel::kNone, Plan{0, 0, false}, 0, 0};
 }
 
+// Rows of W wavefronts x P vectors per lane that a launch may regroup into
+// one wavefront of W * P vectors per lane when that grid is resident at
+// once (adding the squares in the W-wavefront order, so the bits do not
+// change): the vectors per lane of that form, or 0.  Per kernel, the splits
+// its plans produce that have such instances: RMSNorm 3 x 2 and 4 x 2,
+// AdaLN and rotate-half RoPE 2 x 3 and 2 x 4, interleaved RoPE with one
+// table slice per row 2 x 3, 3 x 2 and 4 x 2 when a head's vectors
+// (vec_per_head) divide one wavefront's lanes, so the slice stays shared.
+inline int regroup_vectors(Kernel k, const Plan& p, int vec_per_head) {
+    const int W = p.wpr, P = p.per;
+    bool ok = false;
+    switch (k) {
+        case Kernel::kRmsNorm: ok = P == 2 && (W == 3 || W == 4); break;
+        case Kernel::kAdaLN:
+        case Kernel::kRopeXor: ok = W == 2 && (P == 3 || P == 4); break;
+        case Kernel::kRopeInterleavedShared:
+            ok = ((W == 2 && P == 3) || (P == 2 && (W == 3 || W == 4))) && vec_per_head > 0 &&
+                 kWave % vec_per_head == 0;
+            break;
+        default: break;
+    }
+    return ok ? W * P : 0;
+}
+
 inline const char* kernel_name(Kernel k) {
     switch (k) {
         case Kernel::kNone: return "none";

@@ -653,5 +653,25 @@ def test_describe_one_wave_regroup(dtype, hidden, want):
     else:
         assert name == "rmsnorm_kernel" and f["vectors_per_lane"] == "2", (name, f)
         assert int(f["one_wave_vectors_per_lane"]) == want == 2 * int(f["wavefronts_per_row"]), (name, f)
-    for op, h, hd, d in [(ltx.OP_ADALN, 3072, 0, 0), (ltx.OP_ROPE, 3072, 24, 128), (ltx.OP_ROPE_INTERLEAVED, 3072, 24, 128)]:
-        assert "one_wave_vectors_per_lane" not in ltx.ltxnorm_describe_launch(op, 8192, h, hd, d), op
+
+
+@pytest.mark.parametrize("op,hidden,heads,head_dim,dtype,want", [
+    (ltx.OP_ADALN, 3072, 0, 0, ltx.BF16, 6), (ltx.OP_ADALN, 4096, 0, 0, ltx.BF16, 8),
+    (ltx.OP_ADALN, 2048, 0, 0, ltx.F32, 8), (ltx.OP_ADALN, 5120, 0, 0, ltx.BF16, None),
+    (ltx.OP_ROPE, 3072, 24, 128, ltx.BF16, 6), (ltx.OP_ROPE, 4096, 32, 128, ltx.BF16, 8),
+    (ltx.OP_ROPE, 5120, 40, 128, ltx.BF16, None), (ltx.OP_ROPE, 2048, 32, 64, ltx.BF16, None),
+    (ltx.OP_ROPE_INTERLEAVED, 3072, 24, 128, ltx.BF16, 6), (ltx.OP_ROPE_INTERLEAVED, 2560, 20, 128, ltx.BF16, 6),
+    (ltx.OP_ROPE_INTERLEAVED, 4096, 32, 128, ltx.BF16, 8),
+    # a head of 48 vectors is shared by 3 wavefronts' lanes, not by one's
+    (ltx.OP_ROPE_INTERLEAVED, 3072, 8, 384, ltx.BF16, None),
+])
+def test_describe_one_wave_regroup_fused(op, hidden, heads, head_dim, dtype, want):
+    """AdaLN and the fused RoPE kernels name their one-wavefront form for
+    the splits that have one (2 wavefronts x 3 or 4 vectors; interleaved
+    also 3 or 4 x 2, where a head's vectors divide one wavefront's lanes)."""
+    name, f = _describe(op, hidden, heads, head_dim, dtype, rows=8192)
+    got = f.get("one_wave_vectors_per_lane")
+    if want is None:
+        assert got is None, (name, f)
+    else:
+        assert int(got) == want == int(f["wavefronts_per_row"]) * int(f["vectors_per_lane"]), (name, f)

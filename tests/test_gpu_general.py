@@ -806,6 +806,12 @@ ONE_WAVE = [
     # rows); inside the large call, the split itself
     ("bf16", "rms", 3072, 0, 8192), ("bf16", "rms", 2560, 0, 8192), ("bf16", "rms", 4096, 0, 4096),
     ("f16", "rms", 3584, 0, 6000), ("f32", "rms", 2048, 0, 8192), ("f32", "rms", 1028, 0, 8192),
+    # AdaLN and rotate-half RoPE rows of 2 wavefronts x 3 or 4 vectors, and
+    # interleaved RoPE rows of 2 x 3, 3 x 2 or 4 x 2, regrouped the same way
+    ("bf16", "adaln", 3072, 0, 4096), ("bf16", "adaln", 2304, 0, 8000), ("f32", "adaln", 2048, 0, 6000),
+    ("f16", "adaln", 4096, 0, 3000),
+    ("bf16", "half", 3072, 128, 4096), ("bf16", "half", 4096, 128, 3000), ("f32", "half", 2048, 64, 6000),
+    ("bf16", "il", 3072, 128, 8192), ("bf16", "il", 2560, 128, 6000), ("f16", "il", 4096, 128, 4096),
 ]
 
 
