@@ -98,3 +98,55 @@ def test_random_sweep_reaches_every_kernel_family():
     assert {"rmsnorm_kernel", "rmsnorm_adaln_kernel", "rmsnorm_general_kernel", "rmsnorm_long_kernel",
             "rmsnorm_split_kernels", "rmsnorm_rope_interleaved_kernel", "rmsnorm_rope_pair_kernel",
             "rmsnorm_short_kernel"} <= seen, seen
+
+
+def _mid_cases(seed=20261205, n=40):
+    """Launches of 500 to 9000 rows of hidden about 1500 to 5200: whole grids
+    that a device may hold at once, where the library takes its one-wavefront
+    priority and regrouped forms, next to the same shapes' plain splits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = str(rng.choice(["bf16", "f16", "f32"]))
+        E = 4 if dtype == "f32" else 8
+        op = str(rng.choice(["rms", "adaln", "half", "il"]))
+        H = int(E * rng.integers(1500 // E, 5200 // E))
+        d = heads = 0
+        if op in ("half", "il"):
+            d = int(rng.choice([32, 64, 128])) if rng.random() < 0.7 else int(2 * rng.integers(1, 200))
+            heads = max(1, H // d)
+            H = heads * d
+        rows = int(min(rng.integers(500, 9000), 40_000_000 // H))
+        out.append(dict(dtype=dtype, op=op, H=H, d=d, heads=heads, rows=rows, seed=int(rng.integers(1 << 30)),
+                        null_w=bool(rng.random() < 0.1), eps=float(rng.choice([1e-6, 1e-5])),
+                        inplace=bool(rng.random() < 0.2), seq=int(rng.integers(1, rows + 6)),
+                        rps=int(rng.integers(1, rows + 1)), null_mod=int(rng.integers(0, 8))))
+    return out
+
+
+MID_CASES = _mid_cases()
+
+
+@pytest.mark.parametrize("i", range(len(MID_CASES)))
+def test_random_mid_sweep(i):
+    c = MID_CASES[i]
+    desc = ltx.ltxnorm_describe_launch(OPC[c["op"]], c["rows"], c["H"], c["heads"], c["d"], CODE[c["dtype"]])
+    announce(f"random mid sweep {i}: {c} -> {desc}")
+    rep = _run(c)
+    assert rep["pass"], (c, desc, rep)
+
+
+def test_random_mid_sweep_reaches_the_one_wave_forms():
+    """The mid-size cases, as the library describes them (no GPU work):
+    one-wavefront rows that may take the priority instances, and rows of a
+    few wavefronts that may regroup, in RMSNorm, AdaLN and both RoPEs."""
+    seen = set()
+    for c in MID_CASES:
+        d = ltx.ltxnorm_describe_launch(OPC[c["op"]], c["rows"], c["H"], c["heads"], c["d"], CODE[c["dtype"]])
+        name = d.split()[0].split("(")[0]
+        if "one_wave_vectors_per_lane=" in d:
+            seen.add(name + " regroup")
+        elif "load_priority=one_wave" in d:
+            seen.add(name + " one-wave")
+    assert {"rmsnorm_kernel regroup", "rmsnorm_adaln_kernel regroup", "rmsnorm_rope_xor_kernel regroup",
+            "rmsnorm_rope_interleaved_kernel regroup", "rmsnorm_kernel one-wave"} <= seen, seen
