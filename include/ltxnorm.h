@@ -232,9 +232,10 @@ typedef enum ltxnorm_op {
  * says when the kernel's wavefronts raise their priority while a row's
  * loads issue: "always", "never", or "one_wave": only when the launch's
  * whole grid is resident on the device at once (decided at launch from the
- * device's occupancy for that instance; rotate-half RoPE then may hold its
- * weight, and AdaLN does hold it, in 4 KB of LDS per workgroup instead of
- * registers, so that more rows fit).  It changes timing only, never a
+ * device's occupancy for that instance; rotate-half and head-packed RoPE
+ * then may hold their weight, and AdaLN does hold it, in 4 KB of LDS per
+ * workgroup instead of registers, so that more rows fit; a head-packed
+ * launch of that form shows as rmsnorm_rope_packed_wl_kernel).  It changes timing only, never a
  * result bit.  An RMSNorm line of 3 or 4 wavefronts x 2 vectors ends in
  * "one_wave_vectors_per_lane=6" (or 8): when the whole grid then fits on the
  * device at once, one wavefront takes each row with that many vectors per

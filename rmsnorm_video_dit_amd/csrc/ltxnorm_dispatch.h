@@ -139,9 +139,12 @@ template <typename IO, bool ODD>
 struct RopePackedL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    static constexpr bool kOneWaveLds = false;
+    static constexpr bool kOneWaveLds = true;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
-    static const void* fn() { return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>; }
+    static const void* fn() {
+        if constexpr (WL) return (const void*)&rmsnorm_rope_packed_wl_kernel<IO, PER, ODD>;
+        return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>;
+    }
 };
 // The general kernel masks every row itself: FULL does not select anything.
 template <typename IO, GOp OP>

@@ -404,11 +404,17 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
 // The lane's table slice (kEpv cos and kEpv sin) does not depend on the slot;
 // the wavefront reads the position's table rows once and the lanes take
 // their slices through LDS (TableLds).  PRIO raises the wave priority while
-// a row's loads issue.
+// a row's loads issue.  WL (one-wavefront rows with PRIO only) keeps the
+// weight in LDS, takes the lane's table slices from LDS per vector instead
+// of holding them, and asks for 8 wavefronts per SIMD up to 3 vectors per
+// lane (64 VGPRs instead of 76 at d = 72, no spill), so that 8192 rows of
+// hidden 1152 are resident at once: 9.84 -> 8.53 us at [8192 x 1152],
+// d = 72; where the register-weight instance already fits (4096 and 6144
+// rows) this form measured 5 % slower, so the launch prefers that one.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool ODD, bool PRIO>
-__global__ void __launch_bounds__(Layout<WPR>::kThreads)
-rmsnorm_rope_packed_kernel(const KArgs a) {
+template <typename IO, int VPL, int WPR, bool ODD, bool PRIO, bool WL>
+__device__ __forceinline__ void rope_packed_rows(const KArgs& a) {
+    static_assert(!WL || (PRIO && WPR == 1), "LDS weight: one-wavefront priority instances only");
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int E = IO::kEpv;
     constexpr int G = E / 2;  // elements per group (ODD)
@@ -445,12 +451,20 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
     auto vec_of = [&](int k) { return (k * WPR + ln.wave_in_row) * lw + l; };
 
     if constexpr (PRIO) priority_for_loads();
-    u32x4 wv[VPL];
+    __shared__ u32x4 wlds[WL ? VPL * kWave : 1];
+    u32x4 wv[WL ? 1 : VPL];
+    if constexpr (WL) {
+        // every slot of the wavefront's lanes, ones past the row
+        for (int v = threadIdx.x; v < VPL * kWave; v += Layout<WPR>::kThreads)
+            wlds[v] = (a.w != nullptr && v < a.nvec) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+        __syncthreads();
+    } else {
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int v = vec_of(k);
-        const bool in = l < lw && v < a.nvec;
-        wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+        for (int k = 0; k < VPL; ++k) {
+            const int v = vec_of(k);
+            const bool in = l < lw && v < a.nvec;
+            wv[k] = (a.w != nullptr && in) ? reinterpret_cast<const u32x4*>(a.w)[v] : splat(IO::kOne);
+        }
     }
 
     int parity = 0;
@@ -482,22 +496,40 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
         const float part = sum_squares<IO, VPL>(xv);
         const float rstd = rstd_of(row_sum<WPR>(part, ln.slot, ln.wave_in_row, parity), a.hidden_f, a.eps);
         tabs.share(l, a.half / G);
-        tabs.take(col0, c, ss);
-        tabs.take(col1, c + G, ss + G);
+        if constexpr (!WL) {
+            tabs.take(col0, c, ss);
+            tabs.take(col1, c + G, ss + G);
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-            ss[e] *= sg0;
-            ss[e + G] *= sg1;
+            for (int e = 0; e < G; ++e) {
+                ss[e] *= sg0;
+                ss[e + G] *= sg1;
+            }
         }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int v = vec_of(k);
             const bool in = l < lw && v < a.nvec && (WPR == 1 || active);
+            if constexpr (WL) {  // per vector: fewer registers held
+                tabs.take(col0, c, ss);
+                tabs.take(col1, c + G, ss + G);
+#pragma unroll
+                for (int e = 0; e < G; ++e) {
+                    ss[e] *= sg0;
+                    ss[e + G] *= sg1;
+                }
+            }
             keep_packed(xv[k]);
-            keep_packed(wv[k]);
             float own[E], g[E], par[E], o[E];
-            IO::widen(xv[k], own);
-            IO::widen(wv[k], g);
+            if constexpr (WL) {
+                u32x4 wk = wlds[v];
+                keep_packed(wk);
+                IO::widen(xv[k], own);
+                IO::widen(wk, g);
+            } else {
+                keep_packed(wv[k]);
+                IO::widen(xv[k], own);
+                IO::widen(wv[k], g);
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) own[e] = (own[e] * rstd) * g[e];
             // group 0 takes the partner lane's second group (ODD) or first
@@ -514,6 +546,19 @@ rmsnorm_rope_packed_kernel(const KArgs a) {
             if (in) store_stream(yr + v, IO::narrow(o));
         }
     }
+}
+
+template <typename IO, int VPL, int WPR, bool ODD, bool PRIO>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_packed_kernel(const KArgs a) {
+    rope_packed_rows<IO, VPL, WPR, ODD, PRIO, false>(a);
+}
+
+// The WL form (its own kernel, so that only it carries the occupancy request).
+template <typename IO, int VPL, bool ODD>
+__global__ void __launch_bounds__(Layout<1>::kThreads) __attribute__((amdgpu_waves_per_eu(VPL <= 3 ? 8 : 1, 8)))
+rmsnorm_rope_packed_wl_kernel(const KArgs a) {
+    rope_packed_rows<IO, VPL, 1, ODD, true, true>(a);
 }
 
 // ---------------------------------------------------------------------------

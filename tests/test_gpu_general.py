@@ -812,6 +812,9 @@ ONE_WAVE = [
     ("f16", "adaln", 4096, 0, 3000),
     ("bf16", "half", 3072, 128, 4096), ("bf16", "half", 4096, 128, 3000), ("f32", "half", 2048, 64, 6000),
     ("bf16", "il", 3072, 128, 8192), ("bf16", "il", 2560, 128, 6000), ("f16", "il", 4096, 128, 4096),
+    # head-packed rotate-half at more rows than its register-weight priority
+    # instance holds: the form with the weight in LDS (odd and even groups)
+    ("bf16", "half", 1152, 72, 8192), ("f16", "half", 1280, 80, 8192), ("bf16", "half", 1080, 24, 7500),
 ]
 
 
