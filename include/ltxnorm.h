@@ -243,7 +243,8 @@ typedef enum ltxnorm_op {
  * do not depend on which of the two a call takes.  Rows of up to 160
  * vectors may share wavefronts instead, in segments of a few lanes:
  *     "rmsnorm_short_kernel lanes_per_row=8 vectors_per_lane=2
- *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0"
+ *      rows_per_wavefront=8 rows_per_block=32 threads=256 lds_bytes=0
+ *      load_priority=one_wave"
  * The general kernel's line ends in "load_priority=always grid=resident":
  * its grid is capped at the number of workgroups the device holds at once,
  * each workgroup looping over rows; every other kernel takes one workgroup

@@ -236,7 +236,7 @@ LTXNORM_API ltxnorm_status ltxnorm_describe_launch(ltxnorm_op op, int64_t rows, 
         std::snprintf(buf, len, "none");
     } else if (c.kernel == Kernel::kShort) {
         const int per_wave = ltxnorm_detail::kWave / c.lanes_per_row;
-        std::snprintf(buf, len, "%s lanes_per_row=%d vectors_per_lane=%d rows_per_wavefront=%d rows_per_block=%d threads=%d lds_bytes=0",
+        std::snprintf(buf, len, "%s lanes_per_row=%d vectors_per_lane=%d rows_per_wavefront=%d rows_per_block=%d threads=%d lds_bytes=0 load_priority=one_wave",
                       name, c.lanes_per_row, c.plan.per, per_wave, ltxnorm_detail::kShortWavesPerBlock * per_wave,
                       ltxnorm_detail::kWave * ltxnorm_detail::kShortWavesPerBlock);
     } else if (c.kernel == Kernel::kLong) {

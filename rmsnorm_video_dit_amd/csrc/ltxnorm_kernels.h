@@ -123,7 +123,7 @@ __device__ __forceinline__ float segment_sum(float v) {
 
 
 
-template <typename IO, GOp OP, int S, int V>
+template <typename IO, GOp OP, int S, int V, bool PRIO>
 __global__ void __launch_bounds__(kWave * kShortWavesPerBlock)
 rmsnorm_short_kernel(const KArgs a) {
     constexpr int E = IO::kEpv;
@@ -133,6 +133,7 @@ rmsnorm_short_kernel(const KArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int l = lane % S;                // first vector of the lane within the row
     const int seg = lane / S;              // row within the wavefront
+    if constexpr (PRIO) priority_for_loads();
     u32x4 wv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
@@ -163,6 +164,7 @@ rmsnorm_short_kernel(const KArgs a) {
         const bool rin = row < a.rows;
         const u32x4* xr = reinterpret_cast<const u32x4*>(a.x) + row * a.nvec;
         u32x4* yr = reinterpret_cast<u32x4*>(a.out) + row * a.nvec;
+        if constexpr (PRIO) priority_for_loads();
         u32x4 xv[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -195,6 +197,7 @@ rmsnorm_short_kernel(const KArgs a) {
             }
         }
 
+        if constexpr (PRIO) priority_after_loads();
         const float part = sum_squares<IO, V>(xv);
         const float rstd = rstd_of(segment_sum<S>(part), a.hidden_f, a.eps);
         if constexpr (OP == GOp::kRopeHalf && V == 2) {

@@ -632,10 +632,13 @@ def test_kernel_choice_always_covers_the_row():
 ])
 def test_describe_load_priority(op, rows, hidden, heads, head_dim, dtype, want):
     """The launch line states when the kernel raises wave priority for its
-    loads; the segmented-row, two-pass and split kernels carry no such field."""
+    loads; the segmented-row kernel does when its grid fits at once, and the
+    two-pass and split kernels carry no such field."""
     name, f = _describe(op, hidden, heads, head_dim, dtype, rows=rows)
     assert f["load_priority"] == want, (name, f)
-    for args in [(ltx.OP_RMSNORM, 8192, 128), (ltx.OP_RMSNORM, 4, 1 << 20), (ltx.OP_RMSNORM, 512, 131072)]:
+    name, f = _describe(ltx.OP_RMSNORM, 128, rows=8192)
+    assert name == "rmsnorm_short_kernel" and f["load_priority"] == "one_wave", (name, f)
+    for args in [(ltx.OP_RMSNORM, 4, 1 << 20), (ltx.OP_RMSNORM, 512, 131072)]:
         assert "load_priority" not in ltx.ltxnorm_describe_launch(*args), args
 
 

@@ -815,23 +815,29 @@ ONE_WAVE = [
     # head-packed rotate-half at more rows than its register-weight priority
     # instance holds: the form with the weight in LDS (odd and even groups)
     ("bf16", "half", 1152, 72, 8192), ("f16", "half", 1280, 80, 8192), ("bf16", "half", 1080, 24, 7500),
+    # segmented rows (8-32 per workgroup): the large call needs more rows to
+    # exceed one wave
+    ("bf16", "rms", 576, 0, 16384, 131072), ("bf16", "adaln", 1152, 0, 8192, 65536),
+    ("f16", "rms", 256, 0, 32768, 262144), ("bf16", "il", 576, 64, 16384, 131072),
 ]
+ONE_WAVE = [c if len(c) == 6 else c + (16384,) for c in ONE_WAVE]
 
 
-@pytest.mark.parametrize("dtype,op,hidden,d,small", ONE_WAVE)
-def test_one_wave_priority_instances_agree(dtype, op, hidden, d, small):
-    big = 16384   # 4096 workgroups of 4 rows: more than any device holds at once
+@pytest.mark.parametrize("dtype,op,hidden,d,small,big", ONE_WAVE)
+def test_one_wave_priority_instances_agree(dtype, op, hidden, d, small, big):
+    # big: more workgroups (4096 of 4 one-wavefront rows, or of 8-32
+    # segmented rows) than any device holds at once
     heads = hidden // d if d else 0
     desc = ltx.ltxnorm_describe_launch(_OPS[op], big, hidden, heads, d, _DT[dtype])
     announce(f"one-wave priority {dtype} {op} hidden={hidden} d={d} rows={small} -> {desc}")
-    assert ((" wavefronts_per_row=1 " in desc and "load_priority=one_wave" in desc)
+    assert ("load_priority=one_wave" in desc and (" wavefronts_per_row=1 " in desc or " lanes_per_row=" in desc)
             or " one_wave_vectors_per_lane=" in desc), desc
     seed = 7 * hidden + d
     x = datagen.make_x(big, hidden, seed=seed, stream=1, dtype=dtype)
     w = datagen.make_w(hidden, seed=seed, stream=2, dtype=dtype)
     rps = 512
-    sc = datagen.make_x(big // rps, hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
-    sh = datagen.make_x(big // rps, hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
+    sc = datagen.make_x(-(-big // rps), hidden, seed=seed, stream=4, sigma=0.25, dtype=dtype)
+    sh = datagen.make_x(-(-big // rps), hidden, seed=seed, stream=5, sigma=0.25, dtype=dtype)
     c, s_ = datagen.rope_tables(3000, d) if d else (None, None)
 
     def call(rows):
