@@ -114,10 +114,10 @@ template <typename IO, bool SHARED>
 struct RopeIlL {
     static constexpr bool kResident = false;
     static constexpr bool kOneWavePrio = true;
-    static constexpr bool kOneWaveLds = false;
+    static constexpr bool kOneWaveLds = !SHARED;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() {
-        return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED, PRIO>;
+        return (const void*)&rmsnorm_rope_interleaved_kernel<IO, PER, WPR, FULL, SHARED, PRIO, 1, WL>;
     }
     template <int VPL, bool FULL, int VW>
     static const void* regroup() {

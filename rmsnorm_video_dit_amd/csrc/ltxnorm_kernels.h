@@ -671,13 +671,18 @@ rmsnorm_rope_pair_kernel(const KArgs a) {
 // head_dim / kEpv divides the lanes per row (every power-of-two head_dim up
 // to 64 kEpv), so all slots of a lane share one table offset and the row
 // needs a single table slice per lane.  PRIO raises the wave priority while
-// a row's loads issue.
+// a row's loads issue.  WL (per-slot one-wavefront priority instances) keeps
+// the weight in LDS and takes each slot's table slice in turn instead of
+// holding them all: 54-62 VGPRs at 3 vectors per lane instead of 78-88, so
+// 8192 rows of hidden 1152 fit at once (d = 72: 9.69 -> 8.92 us; d = 24:
+// 9.65 -> 8.87 us); the launch prefers the register form where it fits.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool SHARED, bool PRIO, int VW = 1>
+template <typename IO, int VPL, int WPR, bool FULL, bool SHARED, bool PRIO, int VW = 1, bool WL = false>
 __global__ void __launch_bounds__(Layout<WPR>::kThreads)
 rmsnorm_rope_interleaved_kernel(const KArgs a) {
     static_assert(VW == 1 || (SHARED && PRIO && WPR == 1), "split-order sums: shared-slice priority instances");
-    constexpr bool kWl = VW > 1;  // weight in LDS
+    static_assert(!WL || (!SHARED && PRIO && WPR == 1), "LDS weight: per-slot one-wavefront priority instances");
+    constexpr bool kWl = VW > 1 || WL;  // weight in LDS
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
     constexpr int L = Layout<WPR>::kLanesPerRow;
     constexpr int E = IO::kEpv;
@@ -725,7 +730,7 @@ rmsnorm_rope_interleaved_kernel(const KArgs a) {
         // [43690 x 1152], 64.4 -> 67.2 % and 65.1 -> 67.4 %), with x for
         // several wavefronts per row and after the reduction for one; more
         // slots would spill registers, so there slots 1.. load in turn.
-        constexpr bool kAll = !SHARED && VPL <= 4;
+        constexpr bool kAll = !SHARED && VPL <= 4 && !WL;
         constexpr int NT = kAll ? VPL : 1;  // table slices held at once
         float c[NT][NP], sn[NT][NP];
         constexpr bool kGather = !SHARED && WPR == 1;

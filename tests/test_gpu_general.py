@@ -815,6 +815,8 @@ ONE_WAVE = [
     # head-packed rotate-half at more rows than its register-weight priority
     # instance holds: the form with the weight in LDS (odd and even groups)
     ("bf16", "half", 1152, 72, 8192), ("f16", "half", 1280, 80, 8192), ("bf16", "half", 1080, 24, 7500),
+    # interleaved with a table slice per slot, the same way
+    ("bf16", "il", 1152, 72, 8192), ("f16", "il", 1152, 24, 8000),
     # segmented rows (8-32 per workgroup): the large call needs more rows to
     # exceed one wave
     ("bf16", "rms", 576, 0, 16384, 131072), ("bf16", "adaln", 1152, 0, 8192, 65536),
