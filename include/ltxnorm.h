@@ -234,8 +234,9 @@ typedef enum ltxnorm_op {
  * whole grid is resident on the device at once (decided at launch from the
  * device's occupancy for that instance; rotate-half and head-packed RoPE
  * then may hold their weight, and AdaLN does hold it, in 4 KB of LDS per
- * workgroup instead of registers, so that more rows fit; a head-packed
- * launch of that form shows as rmsnorm_rope_packed_wl_kernel).  It changes timing only, never a
+ * workgroup instead of registers, so that more rows fit; such launches of
+ * head-packed and whole-row rotate-half RoPE show as
+ * rmsnorm_rope_packed_wl_kernel and rmsnorm_rope_xor_wl_kernel).  It changes timing only, never a
  * result bit.  An RMSNorm line of 3 or 4 wavefronts x 2 vectors ends in
  * "one_wave_vectors_per_lane=6" (or 8): when the whole grid then fits on the
  * device at once, one wavefront takes each row with that many vectors per

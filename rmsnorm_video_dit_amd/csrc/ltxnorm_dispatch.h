@@ -98,7 +98,10 @@ struct RopeXorL {
     static constexpr bool kOneWavePrio = true;
     static constexpr bool kOneWaveLds = true;
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
-    static const void* fn() { return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO, WL>; }
+    static const void* fn() {
+        if constexpr (WL && FULL) return (const void*)&rmsnorm_rope_xor_wl_kernel<IO, PER>;
+        else return (const void*)&rmsnorm_rope_xor_kernel<IO, PER, WPR, FULL, PRIO, WL>;
+    }
     template <int VPL, bool FULL, int VW>
     static const void* regroup() { return (const void*)&rmsnorm_rope_xor_kernel<IO, VPL, 1, FULL, true, true, VW>; }
 };
@@ -143,7 +146,7 @@ struct RopePackedL {
     template <int WPR, int PER, bool FULL, bool PRIO, bool WL = false>
     static const void* fn() {
         if constexpr (WL) return (const void*)&rmsnorm_rope_packed_wl_kernel<IO, PER, ODD>;
-        return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>;
+        else return (const void*)&rmsnorm_rope_packed_kernel<IO, PER, WPR, ODD, PRIO>;
     }
 };
 // The general kernel masks every row itself: FULL does not select anything.

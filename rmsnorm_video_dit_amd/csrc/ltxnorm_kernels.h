@@ -294,9 +294,8 @@ rmsnorm_short_kernel(const KArgs a) {
 // (TableLds) and take the lane's slice after the reduction, instead of an
 // L2 round trip then: 12.42 -> 11.74 us at [8192 x 2048], d = 64.
 // ---------------------------------------------------------------------------
-template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL, int VW = 1>
-__global__ void __launch_bounds__(Layout<WPR>::kThreads)
-rmsnorm_rope_xor_kernel(const KArgs a) {
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL, int VW>
+__device__ __forceinline__ void rope_xor_rows(const KArgs& a) {
     static_assert(!WL || (PRIO && WPR == 1), "LDS weight: one-wavefront priority instances only");
     static_assert(VW == 1 || WL, "split-order sums: LDS-weight instances");
     constexpr int RPB = Layout<WPR>::kRowsPerBlock;
@@ -397,6 +396,21 @@ rmsnorm_rope_xor_kernel(const KArgs a) {
             }
         }
     });
+}
+
+template <typename IO, int VPL, int WPR, bool FULL, bool PRIO, bool WL, int VW = 1>
+__global__ void __launch_bounds__(Layout<WPR>::kThreads)
+rmsnorm_rope_xor_kernel(const KArgs a) {
+    rope_xor_rows<IO, VPL, WPR, FULL, PRIO, WL, VW>(a);
+}
+
+// The WL form of whole-vector rows, its own kernel so that only it carries
+// the request for 8 wavefronts per SIMD (fp16, 4 vectors per lane: 66 -> 64
+// VGPRs, no spill; masked rows would spill and keep the kernel above).
+template <typename IO, int VPL>
+__global__ void __launch_bounds__(Layout<1>::kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+rmsnorm_rope_xor_wl_kernel(const KArgs a) {
+    rope_xor_rows<IO, VPL, 1, true, true, true, 1>(a);
 }
 
 // ---------------------------------------------------------------------------
